@@ -1,0 +1,461 @@
+"""Pins of the CPU oracle against things other than itself.
+
+The pages print no layer outputs, so the oracle is pinned by closed forms, library
+routines, brute force on tiny inputs, constructed cases whose result follows from the
+definition by hand, and invariants (exactness, per-row independence, permutation).
+Each test names the step it pins. None of these needs a GPU.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from latent_mixture_experts_bf16_amd import synth
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _dims(**kw):
+    base = dict(hidden=512, latent=128, n_experts=16, n_group=4, topk_group=2, top_k=2,
+                expert_inter=256, shared_inter=512)
+    base.update(kw)
+    return synth.LayerDims(**base)
+
+
+# ------------------------------------------------------------------ number formats
+
+def test_bf16_rounding_matches_torch():
+    """rnd() to bf16 equals a library conversion (torch, round to nearest even)."""
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(200000).astype(np.float32) * np.float32(s)
+                        for s in (1e-30, 1e-3, 1.0, 1e3, 1e30)])
+    # exact ties between two bf16 neighbours, both parities, and subnormals
+    ties = ((np.arange(1, 5000, dtype=np.uint32) << 16) | 0x8000).view(np.float32)
+    sub = (np.arange(1, 70000, 7, dtype=np.uint32)).view(np.float32)
+    v = np.concatenate([v, ties, -ties, sub, -sub, np.float32([0.0, -0.0, np.inf, -np.inf])])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f32_to_bf16(v), ref)
+
+
+def test_f16_conversions_match_numpy():
+    """fp16 decode of every pattern and fp32->fp16 rounding equal numpy's (a library
+    routine: IEEE binary16, round to nearest even, subnormals, overflow to inf)."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (h & 0x7C00) != 0x7C00
+    ref = h.view(np.float16).astype(np.float32)
+    got = O.f16_to_f32(h)
+    assert np.array_equal(got[finite].view(np.uint32), ref[finite].view(np.uint32))
+    assert np.isnan(got[~finite & ((h & 0x3FF) != 0)]).all()
+    rng = np.random.default_rng(6)
+    v = np.concatenate([
+        rng.standard_normal(300000).astype(np.float32) * np.float32(s) for s in (1e-7, 1e-5, 1.0, 1e2, 3e4)]
+        + [np.float32([65504, 65519.99, 65520, 65536, 1e6, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                       2.0 ** -14, 0.0, -0.0, np.inf, -np.inf])])
+    # exact midpoints between neighbouring fp16 values
+    a = np.arange(0, 0x7BFF, 3, dtype=np.uint16).view(np.float16).astype(np.float64)
+    b = (np.arange(0, 0x7BFF, 3, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
+    mids = ((a + b) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.f32_to_f16(v), ref)
+
+
+# ------------------------------------------------------------------ P1 dequant closed form
+
+def test_dequant_closed_form_every_code_and_scale():
+    """w = q*scale + bias with bias = -8*scale equals (q - 8)*scale exactly, for all 16
+    codes and every positive finite bf16 scale with 16*scale finite."""
+    scales = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    sval = O.bf16_to_f32(scales).astype(np.float64)
+    ok = sval * 16 <= np.finfo(np.float32).max
+    scales, sval = scales[ok], sval[ok]
+    bias = O.f32_to_bf16((-8.0 * sval).astype(np.float32))
+    L = O.lib()
+    step = 97  # every 97th scale through ctypes keeps the test fast; the rest below
+    for q in range(16):
+        exact = ((q - 8) * sval).astype(np.float32)      # exact in float64, then in fp32
+        for i in range(0, len(scales), step):
+            assert L.oracle_dequant(q, int(scales[i]), int(bias[i])) == exact[i]
+    # all scales, through the matvec path: one-hot inputs pick single weights
+    n = len(scales)
+    Q = np.full((n, 8), 0, np.uint32)
+    x = np.zeros(64, np.float32)
+    for q in (0, 7, 8, 15):
+        Q[:] = np.uint32(q * 0x11111111)
+        x[:] = 0
+        x[3] = 1.0
+        got = O.q4_matvec(Q, scales[:, None], bias[:, None], x)
+        assert np.array_equal(got, ((q - 8) * sval).astype(np.float32))
+
+
+def test_nibble_layout_low_nibble_first():
+    """Code k of a row sits in word k // 8 at bits 4 * (k % 8) (the layout this build
+    fixes): a one-hot input at k returns exactly the dequantised weight at k."""
+    rng = np.random.default_rng(7)
+    K = 256
+    codes = rng.integers(0, 16, size=(3, K))
+    words = np.zeros((3, K // 8), np.uint32)
+    for r in range(3):
+        for k in range(K):
+            words[r, k // 8] |= np.uint32(codes[r, k]) << np.uint32(4 * (k % 8))
+    s = O.f32_to_bf16(rng.uniform(0.005, 0.02, size=(3, K // 64)).astype(np.float32))
+    b = O.f32_to_bf16(-8 * O.bf16_to_f32(s))
+    for k in range(K):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        got = O.q4_matvec(words, s, b, x)
+        want = ((codes[:, k] - 8) * O.bf16_to_f32(s[:, k // 64]).astype(np.float64)).astype(np.float32)
+        assert np.array_equal(got, want), k
+
+
+# ------------------------------------------------------------------ P2 dot products vs fp64
+
+def _gamma(K):
+    u = 2.0 ** -24
+    return K * u / (1 - K * u)
+
+
+@pytest.mark.parametrize("K", [128, 1024, 4096])
+def test_dense_dot_within_fp64_bound(K):
+    """Every fp32 dot product is within gamma_K * sum|x*w| of the exact value (products
+    are exact in fp32, so only the summation rounds); the exact value comes from a
+    float64 library matmul."""
+    rng = np.random.default_rng(K)
+    W = synth.f32_to_bf16_bits((rng.standard_normal((64, K)) * 0.02).astype(np.float32))
+    x = O.bf16_to_f32(synth.f32_to_bf16_bits(rng.standard_normal(K).astype(np.float32)))
+    got = O.dense(W, x).astype(np.float64)
+    Wf = O.bf16_to_f32(W).astype(np.float64)
+    exact = Wf @ x.astype(np.float64)
+    bound = _gamma(K) * (np.abs(Wf) @ np.abs(x.astype(np.float64)))
+    assert (np.abs(got - exact) <= bound).all()
+
+
+def test_dense_and_q4_exact_on_integer_data():
+    """With small-integer data every partial sum is exact, so the oracle must return the
+    integer matmul exactly: a dropped, repeated or misplaced term cannot hide."""
+    rng = np.random.default_rng(13)
+    K, N = 2048, 48
+    Wi = rng.integers(-8, 8, size=(N, K))
+    xi = rng.integers(-16, 16, size=K)
+    W = synth.f32_to_bf16_bits(Wi.astype(np.float32))
+    assert np.array_equal(O.dense(W, xi.astype(np.float32)), (Wi @ xi).astype(np.float32))
+    codes = rng.integers(0, 16, size=(N, K))
+    Q = np.zeros((N, K // 8), np.uint32)
+    for i in range(8):
+        Q |= (codes[:, i::8].astype(np.uint32) << np.uint32(4 * i))
+    S = np.full((N, K // 64), synth.f32_to_bf16_bits(np.float32([0.25]))[0], np.uint16)
+    B = np.full((N, K // 64), synth.f32_to_bf16_bits(np.float32([-2.0]))[0], np.uint16)
+    want = (((codes - 8) @ xi) * 0.25).astype(np.float32)
+    assert np.array_equal(O.q4_matvec(Q, S, B, xi.astype(np.float32)), want)
+
+
+def test_q4_dot_within_fp64_bound():
+    rng = np.random.default_rng(11)
+    N, K = 32, 2048
+    Q = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint32)
+    S = synth.f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(N, K // 64)).astype(np.float32))
+    B = synth.f32_to_bf16_bits((-8 * synth.bf16_bits_to_f32(S)))
+    x = O.bf16_to_f32(synth.f32_to_bf16_bits(np.abs(rng.standard_normal(K)).astype(np.float32)))
+    k = np.arange(K)
+    q = ((Q[:, k // 8] >> (4 * (k % 8)).astype(np.uint32)) & 15).astype(np.float64)
+    Wf = (q - 8) * O.bf16_to_f32(S).astype(np.float64)[:, k // 64]
+    exact = Wf @ x
+    got = O.q4_matvec(Q, S, B, x).astype(np.float64)
+    bound = _gamma(K) * (np.abs(Wf) @ np.abs(x))
+    assert (np.abs(got - exact) <= bound).all()
+
+
+# ------------------------------------------------------------------ gate C64 order
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_gate_c64_constructed_cases():
+    """Hand-derived results of the gate's fixed order (cases in golden/gate_c64_cases.json,
+    each with its derivation) and exact integer sums."""
+    for case in _golden("gate_c64_cases.json")["cases"]:
+        K = case["K"]
+        x = np.zeros(K, np.float32)
+        w = np.ones(K, np.float32)
+        for k, v in case["terms"]:
+            x[k] = v
+        got = O.gate_c64(x, w)[0, 0]
+        assert got == np.float32(case["expect"]), case["why"]
+    rng = np.random.default_rng(3)
+    for K in (512, 4096, 5120):
+        xi = rng.integers(-64, 64, size=(4, K)).astype(np.float32)
+        wi = rng.integers(-64, 64, size=(5, K)).astype(np.float32)
+        exact = xi.astype(np.int64) @ wi.astype(np.int64).T       # |sum| < 2^24: exact in fp32
+        assert np.array_equal(O.gate_c64(xi, wi), exact.astype(np.float32))
+
+
+def test_gate_fp32_router_uses_fused_multiply_add():
+    """fp32 router (fp16 x * fp32 w): each term is one fused multiply-add, so a single
+    nonzero term returns the correctly rounded product (the float64 product rounded)."""
+    rng = np.random.default_rng(9)
+    x = np.zeros((1, 512), np.float32)
+    w = np.zeros((1, 512), np.float32)
+    for _ in range(200):
+        a = np.float32(np.float16(rng.standard_normal()))
+        b = np.float32(rng.standard_normal() * 0.02)
+        x[0, 77], w[0, 77] = a, b
+        assert O.gate_c64(x, w)[0, 0] == np.float32(np.float64(a) * np.float64(b))
+
+
+# ------------------------------------------------------------------ P3 sigmoid
+
+def test_sigmoid_every_bf16_against_library():
+    """sigmoid of all 65,536 bf16 patterns equals scipy's expit (float64), rounded to fp32."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    z = O.bf16_to_f32(h)
+    got = O.sigmoid(z)
+    ref = scipy.special.expit(z.astype(np.float64)).astype(np.float32)
+    fin = np.isfinite(z)
+    assert np.array_equal(got[fin], ref[fin])
+    assert O.sigmoid(np.float32([0.0]))[0] == 0.5
+    assert O.sigmoid(np.float32([np.inf, -np.inf])).tolist() == [1.0, 0.0]
+    assert np.isnan(O.sigmoid(np.float32([np.nan]))[0])
+
+
+def test_sigmoid_fp32_sample_against_library():
+    rng = np.random.default_rng(10)
+    z = (rng.standard_normal(2_000_000) * 4).astype(np.float32)
+    got = O.sigmoid(z)
+    ref = scipy.special.expit(z.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------ P4 route by brute force
+
+def _rank_key(v, i):
+    # larger value first, NaN last (NaNs by id), then lower id
+    return (1, 0.0, i) if np.isnan(v) else (0, -float(v), i)
+
+
+def _brute_route(dims, z, bias):
+    E, G, TG, K = dims.n_experts, dims.n_group, dims.topk_group, dims.top_k
+    per = E // G
+    s = scipy.special.expit(z.astype(np.float64)).astype(np.float32)
+    b = (s + bias).astype(np.float32) if bias is not None else s
+    gam = []
+    for g in range(G):
+        members = list(range(g * per, (g + 1) * per))
+        best2 = None
+        for pair in itertools.combinations(members, min(2, per)):
+            # the pair no other member ranks before
+            if all(all(_rank_key(b[p], p) < _rank_key(b[o], o) for p in pair)
+                   for o in members if o not in pair):
+                best2 = pair
+        vals = sorted(best2, key=lambda e: _rank_key(b[e], e))
+        gam.append(np.float32(b[vals[0]] + b[vals[1]]) if len(vals) == 2 else b[vals[0]])
+    gam = np.array(gam, np.float32)
+    kept = [S for S in itertools.combinations(range(G), TG)
+            if all(_rank_key(gam[a], a) < _rank_key(gam[o], o)
+                   for a in S for o in range(G) if o not in S)]
+    assert len(kept) == 1
+    cand = [e for e in range(E) if e // per in kept[0]]
+    picks = [P for P in itertools.combinations(cand, K)
+             if all(_rank_key(b[a], a) < _rank_key(b[o], o) for a in P for o in cand if o not in P)]
+    assert len(picks) == 1
+    return sorted(picks[0], key=lambda e: _rank_key(b[e], e)), s
+
+
+@pytest.mark.parametrize("E,G,TG,K", [(16, 4, 2, 2), (16, 4, 2, 5), (12, 3, 1, 3), (16, 8, 3, 4),
+                                      (16, 1, 1, 3), (8, 2, 2, 8), (16, 16 // 2, 8, 6)])
+def test_route_matches_brute_force(E, G, TG, K):
+    dims = _dims(n_experts=E, n_group=G, topk_group=TG, top_k=K)
+    rng = np.random.default_rng(E * 100 + G * 10 + K)
+    for trial in range(40):
+        z = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal(E).astype(np.float32)))
+        bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+        if trial % 4 == 1:       # planted equal biased scores: ties go to the lower id
+            z[:] = z[0]
+            bias[:] = bias[0]
+        if trial % 4 == 2:       # planted equal group scores
+            bias = np.tile(bias[: E // G], G)
+            z = np.tile(z[: E // G], G)
+        idx, w, s = O.route(dims, z, bias)
+        want, s_ref = _brute_route(dims, z, bias)
+        assert idx.tolist() == list(want), (trial, idx, want)
+        assert np.array_equal(s, s_ref)
+
+
+def test_route_nan_ranks_lowest():
+    dims = _dims(n_experts=16, n_group=4, topk_group=4, top_k=3)
+    z = np.linspace(-1, 1, 16).astype(np.float32)
+    z[15] = np.nan                   # would be the largest score otherwise
+    idx, w, _ = O.route(dims, z, np.zeros(16, np.float32))
+    assert idx.tolist() == [14, 13, 12]
+    z[:] = np.nan
+    z[5] = 0.0
+    idx, _, _ = O.route(dims, z, None)
+    assert idx.tolist() == [5, 0, 1]  # the number first, then NaNs by id
+
+
+# ------------------------------------------------------------------ P10 weights
+
+@pytest.mark.parametrize("K,rho", [(1, 2.5), (2, 2.5), (8, 1.0), (9, 2.5)])
+def test_route_weights_sum_to_scale(K, rho):
+    dims = _dims(n_experts=16, n_group=4, topk_group=4, top_k=K, routed_scaling=rho)
+    rng = np.random.default_rng(K)
+    for _ in range(50):
+        z = rng.standard_normal(16).astype(np.float32)
+        _, w, _ = O.route(dims, z, (rng.standard_normal(16) * 0.01).astype(np.float32))
+        if K == 1:
+            assert w[0] == np.float32(rho)
+        assert abs(w.astype(np.float64).sum() - rho) <= K * rho * 2.0 ** -23
+
+
+# ------------------------------------------------------------------ combine lane order
+
+def test_combine_constructed_cases():
+    """Hand-derived results of the 8-lane combine order (golden/combine_cases.json)."""
+    for case in _golden("combine_cases.json")["cases"]:
+        k = case["k"]
+        y = np.zeros((k, 1), np.float32)
+        for j, v in case["y"]:
+            y[j, 0] = v
+        w = np.ones(k, np.float32)
+        assert O.combine(y, w)[0] == np.float32(case["expect"]), case["why"]
+
+
+def test_combine_equals_exact_sum_when_exact():
+    rng = np.random.default_rng(12)
+    for k in (1, 2, 8, 9, 17):
+        y = rng.integers(-100, 100, size=(k, 300)).astype(np.float32)
+        w = rng.integers(1, 8, size=k).astype(np.float32)
+        assert np.array_equal(O.combine(y, w), (w.astype(np.int64) @ y.astype(np.int64)).astype(np.float32))
+
+
+# ------------------------------------------------------------------ P5 zero input
+
+@pytest.mark.parametrize("cid", [0, 3])
+def test_zero_input(cid):
+    dims, arrays = next(synth.workload_layers(cid))
+    x = np.zeros_like(arrays["x"][:1])
+    r = O.forward(dims, arrays, x=x, stages=True)
+    assert (r["z"] == 0).all() and (r["s"] == 0.5).all()
+    assert (r["out"] == 0).all() and (r["out_f32"] == 0).all()
+    K, rho = dims.top_k, np.float32(dims.routed_scaling)
+    if dims.has_bias:
+        # all biased scores are 0.5 + c: routing follows the bias alone
+        want, _ = _brute_route(dims, np.zeros(dims.n_experts, np.float32), arrays["corr_bias"])
+        assert r["idx"][0].tolist() == list(want)
+    else:
+        assert r["idx"][0].tolist() == list(range(K))      # all tie: lowest ids
+    wj = np.float32(np.float32(0.5) / np.float32(np.float32(0.5) * K if K <= 2 else _seqsum(K)))
+    assert (r["w"][0] == np.float32(wj * rho)).all()
+
+
+def _seqsum(K):
+    S = np.float32(0.5)
+    for _ in range(K - 1):
+        S = np.float32(S + np.float32(0.5))
+    return S
+
+
+# ------------------------------------------------------------------ P6 textbook single expert
+
+def test_single_expert_identity_latent_is_textbook_mlp():
+    """E = k = 1, no shared expert, identity latent projections: the layer reduces to
+    out = x + rho * D relu(U x)^2 with rounding points; compared with float64 matmuls
+    (rounded at the same points) to within the fp32 summation bound."""
+    H = 512
+    dims = synth.LayerDims(hidden=H, latent=H, n_experts=1, n_group=1, topk_group=1, top_k=1,
+                           expert_inter=256, shared_inter=0)
+    arrays = synth.make_layer(_dims(hidden=H, latent=H, n_experts=1, n_group=1, topk_group=1,
+                                    top_k=1, shared_inter=0), 3, 77)
+    eye = synth.f32_to_bf16_bits(np.eye(H, dtype=np.float32))
+    arrays["fc1_w"], arrays["fc2_w"] = eye, eye
+    r = O.forward(dims, arrays, stages=True)
+    for row in range(3):
+        x = O.bf16_to_f32(arrays["x"][row]).astype(np.float64)
+        assert np.array_equal(r["u"][row], x.astype(np.float32))       # identity fc1 is exact
+        k = np.arange(H)
+        Uq = ((arrays["up_q"][0][:, k // 8] >> (4 * (k % 8)).astype(np.uint32)) & 15).astype(np.float64)
+        U = (Uq - 8) * O.bf16_to_f32(arrays["up_scales"][0]).astype(np.float64)[:, k // 64]
+        h64 = U @ x
+        bound = _gamma(H) * (np.abs(U) @ np.abs(x))
+        a = r["a"][row, 0].astype(np.float64)
+        # a = rnd(relu(rnd(h))^2): h within the bound before rounding
+        h_or = O.bf16_to_f32(O.f32_to_bf16(h64.astype(np.float32)))
+        relu_ok = np.abs(np.sqrt(a) - np.maximum(h_or, 0)) <= np.abs(h_or) * 2 ** -7 + bound + 1e-30
+        assert relu_ok.all()
+        kk = np.arange(256)
+        Dq = ((arrays["down_q"][0][:, kk // 8] >> (4 * (kk % 8)).astype(np.uint32)) & 15).astype(np.float64)
+        Dm = (Dq - 8) * O.bf16_to_f32(arrays["down_scales"][0]).astype(np.float64)[:, kk // 64]
+        y64 = Dm @ a
+        ybound = _gamma(256) * (np.abs(Dm) @ np.abs(a))
+        y = r["y"][row, 0].astype(np.float64)
+        assert (np.abs(y - y64) <= ybound + np.abs(y64) * 2 ** -8).all()
+        # w = rho exactly, so c = rnd(rho * y), m = c, out = rnd(x + c)
+        assert r["w"][row, 0] == np.float32(2.5)
+        c = O.bf16_to_f32(O.f32_to_bf16((np.float32(2.5) * r["y"][row, 0]).astype(np.float32)))
+        assert np.array_equal(r["c"][row], c)
+        assert np.array_equal(r["m"][row], c)
+        assert np.array_equal(r["out_f32"][row], (x.astype(np.float32) + c).astype(np.float32))
+
+
+# ------------------------------------------------------------------ P7 latent identity == non-latent
+
+def test_identity_latent_equals_non_latent_path():
+    H = 512
+    kw = dict(hidden=H, n_experts=16, n_group=4, topk_group=2, top_k=3, expert_inter=128,
+              shared_inter=0)
+    lat = synth.LayerDims(latent=H, **kw)
+    non = synth.LayerDims(latent=0, **kw)
+    arrays = synth.make_layer(non, 4, 21)
+    eye = synth.f32_to_bf16_bits(np.eye(H, dtype=np.float32))
+    a2 = dict(arrays, fc1_w=eye, fc2_w=eye)
+    r1 = O.forward(lat, a2)
+    r2 = O.forward(non, arrays)
+    for k in ("out", "idx", "w"):
+        assert np.array_equal(r1[k], r2[k])
+
+
+# ------------------------------------------------------------------ P8 permutation metamorphic
+
+def test_group_permutation_permutes_routing_only():
+    dims, arrays = next(synth.workload_layers(0))
+    E, G = dims.n_experts, dims.n_group
+    per = E // G
+    gperm = np.array([2, 0, 3, 1])
+    eperm = np.concatenate([np.arange(g * per, (g + 1) * per) for g in gperm])  # new e -> old e
+    inv = np.argsort(eperm)
+    a2 = dict(arrays)
+    for k in ("gate_w", "corr_bias", "up_q", "up_scales", "up_biases", "down_q", "down_scales",
+              "down_biases"):
+        a2[k] = arrays[k][eperm]
+    r1 = O.forward(dims, arrays)
+    r2 = O.forward(dims, a2)
+    assert np.array_equal(r1["out"], r2["out"])
+    assert np.array_equal(inv[r1["idx"]], r2["idx"])
+    assert np.array_equal(r1["w"], r2["w"])
+
+
+# ------------------------------------------------------------------ P9 per-row independence
+
+def test_rows_are_independent():
+    dims, arrays = next(synth.workload_layers(0, rows=9))
+    full = O.forward(dims, arrays)
+    for r in range(9):
+        one = O.forward(dims, arrays, x=arrays["x"][r:r + 1])
+        for k in ("out", "out_f32", "idx", "w"):
+            assert np.array_equal(full[k][r], one[k][0])
+
+
+def test_magnitudes_are_finite_on_every_workload_row0():
+    """The stated distributions give finite outputs (no fp16/bf16 overflow) on row 0 of
+    the tiny and fp16 workloads."""
+    for cid in (0, 3):
+        dims, arrays = next(synth.workload_layers(cid))
+        r = O.forward(dims, arrays, rows=[0])
+        assert np.isfinite(r["out_f32"]).all()
