@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the latent mixture-of-experts decode layer on one MI355X.
+
+A step is one forward of the whole layer (gate gemv, route, fc1_latent_proj, routed 4-bit
+experts, combine, fc2_latent_proj, shared expert, residual) over one batch of rows, with
+inputs already resident in HBM. Consecutive steps rotate through `--instances` distinct
+copies of the layer's weights (independent seeded draws), so that each step streams its
+weights from HBM instead of the 256 MB Infinity Cache: 8 copies of the 107 MB Bolt-like
+layer are 0.86 GB. The steps are replayed from a captured HIP graph.
+
+Prints one JSON line: layer-tokens/s (rows x steps / seconds), the whole layer's achieved
+HBM bandwidth from its algorithmic bytes, the dominant kernel's roofline (algorithmic
+bytes of one launch / its average duration, both measured here with HIP events on the
+launch stream), and the CPU oracle timed on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+GROUP_NAMES = {0: "gate+fc1+shared_up", 1: "route+shared_down", 2: "schedule", 3: "expert_up",
+               4: "expert_down", 5: "combine", 6: "fc2+shared+residual"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2400)
+    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--config", type=int, default=1, help="workload id (0..3 single layer)")
+    ap.add_argument("--instances", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def group_bytes(dims, rows, n_distinct):
+    """Algorithmic bytes each launch group must move for one pass: every weight byte read
+    once (routed experts: only the distinct experts the pass picked), activations in and out."""
+    H, L, E, I, SI, K = dims.hidden, dims.latent, dims.n_experts, dims.expert_inter, dims.shared_inter, dims.top_k
+    D = L or H
+    a = 2  # activation bytes
+    gate_w = E * H * (4 if dims.router_dtype == 3 else 2)
+    expert = D * I // 2 + (D * I // 64) * 4            # codes + bf16 scale and bias per 64
+    g = {}
+    g[0] = gate_w + L * H * 2 + SI * H * 2 + rows * H * a + rows * E * 2 + rows * L * a + rows * SI * a
+    g[1] = (E * 4 if dims.has_bias else 0) + rows * E * 2 + rows * K * 8 + H * SI * 2 + rows * SI * a + rows * H * a
+    g[2] = rows * K * 8
+    g[3] = n_distinct * expert + rows * D * a + rows * K * I * a
+    g[4] = n_distinct * expert + rows * K * I * a + rows * K * D * a
+    g[5] = (rows * K * D * a + rows * K * 4 + rows * D * a) if (rows > 1 or not L) else 0
+    if not L:
+        g[5] += 2 * rows * H * a
+    g[6] = (H * L * 2 + rows * (D if rows > 1 else K * D) * a + 3 * rows * H * a) if L else 0
+    return g
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the layer's sharding "
+              "is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from latent_mixture_experts_bf16_amd import binding as B
+    from latent_mixture_experts_bf16_amd import layer as LY
+    from latent_mixture_experts_bf16_amd import synth
+
+    wl = synth.WORKLOADS[args.config]
+    if len(wl.layers) != 1:
+        print("bench.py times single-layer workloads (configs 0-3)", file=sys.stderr)
+        return 2
+    dims = wl.layers[0]
+    rows = wl.rows
+    inst = args.instances or (8 if args.config == 1 else (4 if args.config in (2, 3) else 2))
+    print(f"[bench] workload {wl.name}: generating {inst} weight instances", file=sys.stderr, flush=True)
+    t0 = time.time()
+    layers, xs, outs, host0 = [], [], [], None
+    for i in range(inst):
+        d, arrays = next(synth.workload_layers(args.config, instance=i))
+        layers.append(LY.DeviceLayer(d, arrays, max_rows=rows))
+        xs.append(LY.to_device(arrays["x"]))
+        outs.append(torch.empty_like(xs[-1]))
+        if i == 0:
+            host0 = arrays
+        del arrays
+    torch.cuda.synchronize()
+    print(f"[bench] generated and uploaded in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    s = torch.cuda.Stream()
+    for lay in layers:
+        B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+    with torch.cuda.stream(s):
+        for lay, x, o in zip(layers, xs, outs):
+            lay.forward(x, o, rows)
+    s.synchronize()
+    for lay in layers:
+        lay.status()
+
+    # distinct experts each instance's pass picks (for its algorithmic bytes)
+    distinct = []
+    for lay in layers:
+        idx, _ = lay.routing(rows)
+        distinct.append(len(np.unique(idx)))
+    gb = [group_bytes(dims, rows, u) for u in distinct]
+    step_bytes = float(np.mean([sum(g.values()) for g in gb]))
+
+    # graphs: one sweep over all instances, and one graph per instance for a remainder
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+        return g
+
+    with torch.cuda.stream(s):
+        sweep = capture(lambda: [lay.forward(x, o, rows) for lay, x, o in zip(layers, xs, outs)])
+        singles = [capture(lambda lay=lay, x=x, o=o: lay.forward(x, o, rows)) for lay, x, o in zip(layers, xs, outs)]
+
+    def run_steps(n):
+        for _ in range(n // inst):
+            sweep.replay()
+        for j in range(n % inst):
+            singles[j].replay()
+
+    with torch.cuda.stream(s):
+        run_steps(args.warmup)
+    s.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        e0.record(s)
+        run_steps(args.steps)
+        e1.record(s)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    for lay in layers:
+        lay.status()
+    ms_step = ms_total / args.steps
+    tok_s = rows * args.steps / (ms_total / 1e3)
+    layer_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # each launch group on its own: replay graphs of that group over all instances
+    group_stats = {}
+    reps = max(20, args.steps // (4 * inst))
+    for gid in range(7):
+        if B.moe_latent_group_items(layers[0].handle, rows, gid) <= 0:
+            continue
+        with torch.cuda.stream(s):
+            gg = capture(lambda gid=gid: [B.moe_latent_launch_group(lay.handle, rows, x.data_ptr(), o.data_ptr(), gid)
+                                          for lay, x, o in zip(layers, xs, outs)])
+            for _ in range(3):
+                gg.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps):
+                gg.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * inst)
+        gbytes = float(np.mean([g[gid] for g in gb]))
+        group_stats[gid] = {"name": GROUP_NAMES[gid], "us": round(us, 3), "bytes": int(gbytes),
+                            "gbps": round(gbytes / (us * 1e-6) / 1e9, 1)}
+        del gg
+    for lay in layers:
+        lay.status()
+    dom = max(group_stats, key=lambda k: group_stats[k]["us"])
+    d = group_stats[dom]
+    print(f"[bench] groups: {json.dumps(group_stats)}", file=sys.stderr, flush=True)
+
+    # parity of instance 0 against the oracle, and the oracle timed on this host
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        out0 = outs[0].cpu().numpy().view(np.uint16)
+        idx0, w0 = layers[0].routing(rows)
+        n, t_start = 0, time.time()
+        ref = None
+        while True:
+            r = O.forward(dims, host0)
+            ref = ref or r
+            n += 1
+            if time.time() - t_start >= args.cpu_seconds:
+                break
+        el = time.time() - t_start
+        got = O.act_to_f32(dims, out0).astype(np.float64)
+        refv = ref["out_f32"].astype(np.float64)
+        rel_rms = float(np.sqrt(((got - refv) ** 2).mean() / (refv ** 2).mean()))
+        rel_max = float(np.abs(got - refv).max() / np.abs(refv).max())
+        parity = {"routing_bitwise": bool(np.array_equal(idx0, ref["idx"]) and
+                                          np.array_equal(w0.view(np.uint32), ref["w"].view(np.uint32))),
+                  "rel_rms": rel_rms, "rel_max": rel_max}
+        cpu = {"value": round(rows * n / el, 3), "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} forwards of instance 0 ({rows} row(s) each), single-threaded plain C, {el:.1f} s"}
+
+    line = {
+        "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of roofline) at 1/16/64 rows",
+        "value": round(tok_s, 1),
+        "unit": "layer-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dims.act_dtype == 1 else "f16",
+        "data": "synthetic (seeded; random-init weights of the workload's shapes)",
+        "config": {"workload": wl.name, "rows": rows, "hidden": dims.hidden, "latent": dims.latent,
+                   "n_experts": dims.n_experts, "top_k": dims.top_k, "expert_inter": dims.expert_inter,
+                   "shared_inter": dims.shared_inter, "weight_instances": inst},
+        "layer_hbm": {"bytes_per_step": int(step_bytes), "achieved_gbps": round(layer_gbps, 1),
+                      "frac": round(layer_gbps / HBM_PEAK_GBPS, 4)},
+        "roofline": {"bound": "hbm", "kernel": f"moe_group_kernel<{dom}> ({d['name']})",
+                     "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]},
+        "groups": {GROUP_NAMES[k]: v for k, v in group_stats.items()},
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    for lay in layers:
+        lay.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,198 @@
+/*
+ * moe_latent.h -- C ABI of one latent mixture-of-experts decode layer on MI355X (gfx950).
+ *
+ * The layer (TensorFold pull request 1038, «What's in it», the latent MoE bullet) runs, per
+ * row of the input, in this order:
+ *   bf16 router gate gemv -> sigmoid, group-limited top-k with a correction bias ->
+ *   fc1_latent_proj (hidden -> latent) -> routed experts (4-bit affine up, relu^2, 4-bit
+ *   down) in the latent -> weighted combine over the picks -> fc2_latent_proj (latent ->
+ *   hidden) -> + shared expert -> + residual.
+ * A non-latent variant (latent = 0: experts act on the hidden vector, no fc1/fc2) with fp16
+ * activations and an fp32 router covers the fp16 family router of TensorFold pull request
+ * 1295 («What this changes», family kernels: fp32 router, sigmoid top-8, per-expert norm
+ * and sum).
+ *
+ * Every pointer handed to this library is a device pointer (hipMalloc'd or from a torch
+ * tensor on the current GPU) unless stated otherwise. All calls are host calls; forward
+ * work is enqueued on the handle's HIP stream and does not synchronise.
+ *
+ * Errors: every int-returning call returns MOE_OK (0) or one of the moe_status codes;
+ * moe_latent_last_error() then returns a message (per calling thread) that names the
+ * refused parameter or tensor.
+ */
+#ifndef MOE_LATENT_H
+#define MOE_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of moe_tensor.dtype and of the activation / router switches */
+enum moe_dtype { MOE_DT_BF16 = 1, MOE_DT_F16 = 2, MOE_DT_F32 = 3, MOE_DT_U32 = 4, MOE_DT_I32 = 5 };
+
+/* expert activation (the only one the layer uses: relu^2 of the up projection) */
+enum moe_activation { MOE_ACT_RELU2 = 1 };
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,      /* NULL handle / pointer, unknown enum value */
+    MOE_ERR_TOPK_GT_EXPERTS = 2,  /* top_k larger than the layer's own expert count */
+    MOE_ERR_GROUPS = 3,           /* n_experts % n_group, topk_group > n_group, too few candidates */
+    MOE_ERR_SHAPE = 4,            /* a size the kernels do not take (see moe_latent_config) */
+    MOE_ERR_MISSING_TENSOR = 5,   /* a tensor the configuration needs has data == NULL */
+    MOE_ERR_DTYPE = 6,            /* e.g. a quantized or non-bf16 latent projection */
+    MOE_ERR_LAYOUT = 7,           /* wrong rank, shape, or strides (transposed / non-contiguous) */
+    MOE_ERR_EXPERTS_OVER_HIDDEN = 8, /* latent layer whose experts are stored over hidden */
+    MOE_ERR_DEVICE = 9,           /* no device, or the current device is not gfx950 */
+    MOE_ERR_ROWS = 10,            /* rows < 1 or rows > max_rows */
+    MOE_ERR_ALIAS = 11,           /* out partially overlaps hidden_in */
+    MOE_ERR_HIP = 12,             /* a HIP runtime call failed (message holds its error) */
+    MOE_ERR_OOM = 13,             /* device allocation failed */
+    MOE_ERR_DEVICE_CHECK = 14     /* a kernel's own consistency check failed (see the message) */
+};
+
+/* A borrowed view of one weight tensor: data is a device pointer, shape/stride in elements,
+ * row-major expected (stride of the last dim 1, each outer stride the product of the inner
+ * extents). Unused trailing entries are ignored. */
+typedef struct {
+    const void *data;
+    int32_t dtype;   /* moe_dtype */
+    int32_t ndim;    /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4];
+} moe_tensor;
+
+/* Layer configuration. Sizes the kernels take: hidden % 512 == 0; latent == 0 or
+ * latent % 128 == 0; expert_inter % 64 == 0; shared_inter == 0 or % 128 == 0; expert input
+ * and inter widths <= 6144; group_size == 64; n_experts <= 1024; n_group <= 256; top_k <= 16;
+ * 1 <= max_rows <= 256. latent == 0 selects the non-latent layer; shared_inter == 0 drops
+ * the shared expert. */
+typedef struct {
+    int32_t hidden;         /* H */
+    int32_t latent;         /* L, or 0 (non-latent) */
+    int32_t n_experts;      /* E */
+    int32_t n_group;        /* G: contiguous groups of E / G experts */
+    int32_t topk_group;     /* groups kept per row */
+    int32_t top_k;          /* k experts picked per row */
+    int32_t expert_inter;   /* I: routed expert intermediate width */
+    int32_t shared_inter;   /* SI: shared expert width, or 0 */
+    int32_t group_size;     /* quantization group along the input dim (64) */
+    int32_t act_dtype;      /* MOE_DT_BF16 or MOE_DT_F16 (F16 only with latent == 0, no shared) */
+    int32_t router_dtype;   /* MOE_DT_BF16 (bf16 gate, bf16 logits) or MOE_DT_F32 */
+    int32_t activation;     /* MOE_ACT_RELU2 */
+    int32_t has_bias;       /* 1: fp32 correction bias added for selection only */
+    int32_t norm_topk;      /* 1: weights = scores / (sum over picks), then * routed_scaling */
+    int32_t max_rows;       /* largest rows a forward may pass; sizes the workspace */
+    float routed_scaling;   /* rho */
+} moe_latent_config;
+
+/* The layer's weights (borrowed: the caller keeps every buffer alive until destroy).
+ *   gate_w      [E][H]     bf16 (router_dtype BF16) or fp32 (F32)
+ *   corr_bias   [E]        fp32 (only read when has_bias)
+ *   fc1_w       [L][H]     bf16 (latent layers only)
+ *   fc2_w       [H][L]     bf16 (latent layers only)
+ *   up_q        [E][I][D/8]   u32: 8 codes per word, code of input k in word k/8 at bits
+ *                             4*(k%8) (lowest nibble = lowest k); D = L, or H if non-latent
+ *   up_scales   [E][I][D/64]  bf16 scale per group of 64 inputs
+ *   up_biases   [E][I][D/64]  bf16 bias per group: weight = code * scale + bias
+ *   down_q      [E][D][I/8]   u32, same packing
+ *   down_scales [E][D][I/64]  bf16
+ *   down_biases [E][D][I/64]  bf16
+ *   shared_up   [SI][H]   bf16 (shared_inter > 0 only)
+ *   shared_down [H][SI]   bf16 (shared_inter > 0 only) */
+typedef struct {
+    moe_tensor gate_w, corr_bias, fc1_w, fc2_w;
+    moe_tensor up_q, up_scales, up_biases, down_q, down_scales, down_biases;
+    moe_tensor shared_up, shared_down;
+} moe_latent_weights;
+
+typedef struct moe_latent moe_latent_t;
+
+/* Create a layer handle (TensorFold pull request 1038, «What's in it»: refusals before
+ * load, per-layer loader; the review thread: release of device resources on every
+ * refusal). Checks, in order, the configuration (top_k against this layer's own expert
+ * count, groups, sizes), then every tensor descriptor (presence, dtype, shape, row-major
+ * strides; a latent projection that is missing, quantized, transposed or not bf16 is
+ * refused by name, and so are experts stored over hidden in a latent layer), then that the
+ * current device is gfx950 -- all before any weight byte is read. Then it allocates the
+ * workspace for max_rows rows on the current device. hip_stream: the hipStream_t forwards
+ * are enqueued on (NULL = the null stream). On failure *out is NULL and nothing stays
+ * allocated. */
+int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
+                      void *hip_stream, moe_latent_t **out);
+
+/* One forward of `rows` independent rows (TensorFold pull request 1038, «What's in it»,
+ * layer order; «Per operator and row invariance»: each row of a multi-row pass equals its
+ * own one-row pass). hidden_in: [rows][H] activations (act_dtype); out: [rows][H] (same
+ * dtype). out == hidden_in (in place) is allowed; any other overlap is refused. Enqueued on
+ * the handle's stream as up to seven launches (no host synchronisation, no allocation, no
+ * memset: it can be captured in a HIP graph); returns launch errors only -- device-side
+ * faults surface at the caller's next synchronisation / moe_latent_status(). The handle is
+ * not reentrant: forwards on one handle must not overlap in time on different streams. */
+int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out);
+
+/* Release the workspace and the handle (NULL-safe). Synchronises the handle's stream. */
+void moe_latent_destroy(moe_latent_t *h);
+
+/* Launch groups of a forward, in order (stages that share a launch do not depend on each
+ * other): 0 gate + fc1 + shared up; 1 route + shared down; 2 schedule (multi-row passes);
+ * 3 routed expert up; 4 routed expert down; 5 combine (multi-row or non-latent passes);
+ * 6 fc2 + shared + residual (forms the combine itself in a one-row pass). */
+
+/* Enqueue only launch group `group` (0..6) of a forward of `rows` rows, for timing one
+ * kernel on its own. Its inputs are what the earlier groups of the same forward wrote, so
+ * call it after a full moe_latent_forward with the same rows, hidden_in and out; it then
+ * rewrites the same values. A group with no work for this pass enqueues nothing. */
+int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
+                            int32_t group);
+
+/* Number of workgroups launch group `group` runs for a pass of `rows` rows (0: nothing to
+ * launch), or -1 for an invalid handle, rows or group. */
+int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
+
+/* Change the stream later forwards are enqueued on (e.g. a graph-capture stream). */
+int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
+
+/* Execution variant. 1 (the default and the only one available): the forward is a chain of
+ * launches on the handle's stream, stages that do not depend on each other sharing one.
+ * 0 (one fused launch per forward, a dependency-ordered work queue) is reserved and refused
+ * with MOE_ERR_INVALID_ARG: that variant is disabled until a failure of it is understood. */
+int moe_latent_set_variant(moe_latent_t *h, int32_t variant);
+
+/* Copy the last forward's routing to device buffers, enqueued on the handle's stream:
+ * idx_dev [rows][top_k] int32 expert ids in pick order, w_dev [rows][top_k] fp32 weights. */
+int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev);
+
+/* Intermediate values of the last forward, for stage-by-stage checks. */
+enum moe_stage {
+    MOE_STAGE_LOGITS = 1,      /* [rows][E] bf16 (router BF16) or fp32 (router F32) */
+    MOE_STAGE_LATENT = 2,      /* [rows][D] act: fc1 output (or hidden_in when non-latent) */
+    MOE_STAGE_EXPERT_ACT = 3,  /* [rows][top_k][I] act: relu^2 of each pick's up projection */
+    MOE_STAGE_EXPERT_OUT = 4,  /* [rows][top_k][D] act: each pick's down projection */
+    MOE_STAGE_COMBINE = 5,     /* [rows][D] act */
+    MOE_STAGE_SHARED_ACT = 6,  /* [rows][SI] act: relu^2 of the shared up projection */
+    MOE_STAGE_SHARED_OUT = 7   /* [rows][H] act: shared expert output */
+};
+
+/* Copy `bytes` bytes of stage `stage` of the last forward to dst_dev (enqueued on the
+ * handle's stream). bytes must not exceed the stage's size for the last forward's rows. */
+int moe_latent_read_stage(moe_latent_t *h, int32_t stage, void *dst_dev, size_t bytes);
+
+/* Synchronise the handle's stream, then report device-side errors of past forwards
+ * (MOE_ERR_DEVICE_CHECK) or MOE_ERR_HIP; clears the device error flag. */
+int moe_latent_status(moe_latent_t *h);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *moe_latent_last_error(void);
+
+/* Number of device allocations the library currently holds (all handles). */
+int32_t moe_latent_live_allocations(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LATENT_H */

@@ -1,0 +1,495 @@
+// moe_latent_api.hip -- host side of the C ABI declared in include/moe_latent.h.
+//
+// Refusal conventions follow TensorFold pull request 1038 («What's in it»: refusals before
+// load -- a layer whose top-k exceeds its own expert count; a latent projection that is
+// missing, quantized, transposed or not bf16; experts stored over hidden; an unsupported
+// chip -- each by name, before any weight is read; review thread: the device resources a
+// failed load created are released). Here: configuration, then tensor descriptors, then the
+// device, then allocation; every failure frees what was allocated and returns a named code.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "moe_latent.h"
+#include "layer_plan.h"
+
+namespace moe {
+template <int G> __global__ void moe_group_kernel(LayerParams p);
+__global__ void moe_clear_kernel(uint32_t *ctr, int n);
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_latent {
+    moe_latent_config cfg;
+    LayerParams base;       // sizes, weights and workspace pointers; per-forward fields set later
+    hipStream_t stream;
+    int device;
+    int last_rows;
+    void *ws;               // one workspace allocation
+    size_t ws_bytes;
+    uint32_t magic;
+};
+
+static const uint32_t kMagic = 0x4D4F454Cu;
+static thread_local std::string g_err;
+static std::atomic<int> g_live_allocs{0};
+static std::atomic<int> g_alloc_calls{0};
+
+static int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+// Device allocation with leak accounting. MOE_LATENT_FAIL_ALLOC_AT=n makes the n-th
+// allocation (counted from 1 over the process) fail, to test the release paths.
+static hipError_t dev_alloc(void **p, size_t bytes) {
+    const int n = ++g_alloc_calls;
+    const char *f = getenv("MOE_LATENT_FAIL_ALLOC_AT");
+    if (f && atoi(f) == n) { *p = nullptr; return hipErrorOutOfMemory; }
+    hipError_t e = hipMalloc(p, bytes);
+    if (e == hipSuccess) ++g_live_allocs;
+    return e;
+}
+
+static void dev_free(void *p) {
+    if (p && hipFree(p) == hipSuccess) --g_live_allocs;
+}
+
+// ------------------------------------------------------------------ validation
+
+static const char *dt_name(int dt) {
+    switch (dt) {
+    case MOE_DT_BF16: return "bf16";
+    case MOE_DT_F16: return "f16";
+    case MOE_DT_F32: return "f32";
+    case MOE_DT_U32: return "u32";
+    case MOE_DT_I32: return "i32";
+    default: return "unknown";
+    }
+}
+
+static int check_config(const moe_latent_config &c) {
+    if (c.hidden <= 0 || c.n_experts <= 0 || c.n_group <= 0 || c.topk_group <= 0 || c.top_k <= 0 ||
+        c.expert_inter <= 0 || c.latent < 0 || c.shared_inter < 0)
+        return fail(MOE_ERR_INVALID_ARG, "config: sizes must be positive (latent, shared_inter >= 0)");
+    if (c.top_k > c.n_experts)
+        return fail(MOE_ERR_TOPK_GT_EXPERTS, "config: top_k %d exceeds this layer's n_experts %d",
+                    c.top_k, c.n_experts);
+    if (c.n_experts > MAX_EXPERTS)
+        return fail(MOE_ERR_SHAPE, "config: n_experts %d > %d", c.n_experts, (int)MAX_EXPERTS);
+    if (c.top_k > MAX_TOPK) return fail(MOE_ERR_SHAPE, "config: top_k %d > %d", c.top_k, (int)MAX_TOPK);
+    if (c.n_group > 256 || c.n_experts % c.n_group)
+        return fail(MOE_ERR_GROUPS, "config: n_experts %d not divisible into n_group %d groups (<= 256)",
+                    c.n_experts, c.n_group);
+    const int per = c.n_experts / c.n_group;
+    if (c.topk_group > c.n_group)
+        return fail(MOE_ERR_GROUPS, "config: topk_group %d > n_group %d", c.topk_group, c.n_group);
+    if (c.n_group > 1 && per < 2)
+        return fail(MOE_ERR_GROUPS, "config: groups of %d expert; a group score needs two", per);
+    if (c.topk_group * per < c.top_k)
+        return fail(MOE_ERR_GROUPS, "config: %d kept groups of %d experts cannot hold top_k %d",
+                    c.topk_group, per, c.top_k);
+    if (c.group_size != 64) return fail(MOE_ERR_SHAPE, "config: group_size %d (only 64)", c.group_size);
+    if (c.hidden % 512) return fail(MOE_ERR_SHAPE, "config: hidden %d not a multiple of 512", c.hidden);
+    if (c.latent % 128) return fail(MOE_ERR_SHAPE, "config: latent %d not a multiple of 128", c.latent);
+    if (c.shared_inter % 128)
+        return fail(MOE_ERR_SHAPE, "config: shared_inter %d not a multiple of 128", c.shared_inter);
+    const int D = c.latent ? c.latent : c.hidden;
+    if (c.expert_inter % 64 || c.expert_inter > 6144 || D > 6144)
+        return fail(MOE_ERR_SHAPE, "config: expert dims (in %d, inter %d) must be multiples of 64, <= 6144",
+                    D, c.expert_inter);
+    if (c.act_dtype != MOE_DT_BF16 && c.act_dtype != MOE_DT_F16)
+        return fail(MOE_ERR_DTYPE, "config: act_dtype %s (bf16 or f16)", dt_name(c.act_dtype));
+    if (c.act_dtype == MOE_DT_F16 && (c.latent || c.shared_inter))
+        return fail(MOE_ERR_DTYPE, "config: f16 activations only for the non-latent layer without a shared expert");
+    if (c.router_dtype != MOE_DT_BF16 && c.router_dtype != MOE_DT_F32)
+        return fail(MOE_ERR_DTYPE, "config: router_dtype %s (bf16 or f32)", dt_name(c.router_dtype));
+    if (c.activation != MOE_ACT_RELU2) return fail(MOE_ERR_INVALID_ARG, "config: activation %d", c.activation);
+    if (c.max_rows < 1 || c.max_rows > MAX_ROWS)
+        return fail(MOE_ERR_ROWS, "config: max_rows %d outside 1..%d", c.max_rows, (int)MAX_ROWS);
+    return MOE_OK;
+}
+
+// shape expected row-major with the given extents
+static int check_tensor(const char *name, const moe_tensor &t, int dtype, int ndim, const int64_t *shape) {
+    if (!t.data) return fail(MOE_ERR_MISSING_TENSOR, "%s: missing (data == NULL)", name);
+    if (t.dtype != dtype) {
+        if (dtype == MOE_DT_BF16 && t.dtype == MOE_DT_U32)
+            return fail(MOE_ERR_DTYPE, "%s: quantized (u32 codes); a bf16 tensor is required", name);
+        return fail(MOE_ERR_DTYPE, "%s: dtype %s, expected %s", name, dt_name(t.dtype), dt_name(dtype));
+    }
+    if (t.ndim != ndim) return fail(MOE_ERR_LAYOUT, "%s: rank %d, expected %d", name, t.ndim, ndim);
+    bool transposed = ndim == 2 && t.shape[0] == shape[1] && t.shape[1] == shape[0] && shape[0] != shape[1];
+    for (int i = 0; i < ndim; ++i)
+        if (t.shape[i] != shape[i]) {
+            if (transposed) return fail(MOE_ERR_LAYOUT, "%s: transposed ([%lld][%lld], expected [%lld][%lld])", name,
+                                        (long long)t.shape[0], (long long)t.shape[1], (long long)shape[0],
+                                        (long long)shape[1]);
+            return fail(MOE_ERR_LAYOUT, "%s: dim %d is %lld, expected %lld", name, i, (long long)t.shape[i],
+                        (long long)shape[i]);
+        }
+    int64_t st = 1;
+    for (int i = ndim - 1; i >= 0; --i) {
+        if (t.stride[i] != st) {
+            if (ndim == 2 && t.stride[0] == 1 && t.stride[1] == shape[0])
+                return fail(MOE_ERR_LAYOUT, "%s: transposed (column-major strides)", name);
+            return fail(MOE_ERR_LAYOUT, "%s: not contiguous row-major (stride[%d] = %lld, expected %lld)", name, i,
+                        (long long)t.stride[i], (long long)st);
+        }
+        st *= shape[i];
+    }
+    return MOE_OK;
+}
+
+static int check_weights(const moe_latent_config &c, const moe_latent_weights &w) {
+    const int64_t H = c.hidden, L = c.latent, E = c.n_experts, I = c.expert_inter, SI = c.shared_inter;
+    const int64_t D = L ? L : H;
+    int rc;
+    {
+        const int64_t s[2] = {E, H};
+        if ((rc = check_tensor("gate_w", w.gate_w, c.router_dtype, 2, s))) return rc;
+    }
+    if (c.has_bias) {
+        const int64_t s[1] = {E};
+        if ((rc = check_tensor("corr_bias", w.corr_bias, MOE_DT_F32, 1, s))) return rc;
+    }
+    if (L) {
+        const int64_t s1[2] = {L, H}, s2[2] = {H, L};
+        if ((rc = check_tensor("fc1_latent_proj", w.fc1_w, MOE_DT_BF16, 2, s1))) return rc;
+        if ((rc = check_tensor("fc2_latent_proj", w.fc2_w, MOE_DT_BF16, 2, s2))) return rc;
+        // experts must live in the latent: refuse expert tensors laid out over hidden
+        if (w.up_q.data && w.up_q.ndim == 3 && w.up_q.shape[2] == H / 8 && H != L)
+            return fail(MOE_ERR_EXPERTS_OVER_HIDDEN, "up_q: experts stored over hidden (%lld inputs), latent is %lld",
+                        (long long)H, (long long)L);
+        if (w.down_q.data && w.down_q.ndim == 3 && w.down_q.shape[1] == H && H != L)
+            return fail(MOE_ERR_EXPERTS_OVER_HIDDEN, "down_q: experts stored over hidden (%lld outputs), latent is %lld",
+                        (long long)H, (long long)L);
+    }
+    {
+        const int64_t q[3] = {E, I, D / 8}, g[3] = {E, I, D / 64};
+        if ((rc = check_tensor("up_q", w.up_q, MOE_DT_U32, 3, q))) return rc;
+        if ((rc = check_tensor("up_scales", w.up_scales, MOE_DT_BF16, 3, g))) return rc;
+        if ((rc = check_tensor("up_biases", w.up_biases, MOE_DT_BF16, 3, g))) return rc;
+    }
+    {
+        const int64_t q[3] = {E, D, I / 8}, g[3] = {E, D, I / 64};
+        if ((rc = check_tensor("down_q", w.down_q, MOE_DT_U32, 3, q))) return rc;
+        if ((rc = check_tensor("down_scales", w.down_scales, MOE_DT_BF16, 3, g))) return rc;
+        if ((rc = check_tensor("down_biases", w.down_biases, MOE_DT_BF16, 3, g))) return rc;
+    }
+    if (SI) {
+        const int64_t s1[2] = {SI, H}, s2[2] = {H, SI};
+        if ((rc = check_tensor("shared_up", w.shared_up, MOE_DT_BF16, 2, s1))) return rc;
+        if ((rc = check_tensor("shared_down", w.shared_down, MOE_DT_BF16, 2, s2))) return rc;
+    }
+    return MOE_OK;
+}
+
+static int check_device(int *dev_out, int *cus) {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n < 1) return fail(MOE_ERR_DEVICE, "no HIP device (%s)", hipGetErrorString(e));
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    hipDeviceProp_t prop;
+    if ((e = hipGetDeviceProperties(&prop, dev)) != hipSuccess)
+        return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MOE_ERR_DEVICE, "device %d is %s; this library is built for gfx950 (MI355X)", dev,
+                    prop.gcnArchName);
+    *dev_out = dev;
+    *cus = prop.multiProcessorCount;
+    return MOE_OK;
+}
+
+// ------------------------------------------------------------------ workspace
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int setup_workspace(moe_latent *h) {
+    const moe_latent_config &c = h->cfg;
+    const size_t R = c.max_rows, E = c.n_experts, K = c.top_k, I = c.expert_inter, H = c.hidden;
+    const size_t D = c.latent ? c.latent : c.hidden, SI = c.shared_inter, L = c.latent;
+    struct Region { size_t bytes; size_t off; } reg[11];
+    const size_t sizes[11] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
+                              R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
+                              R * H * 2, 256};
+    size_t off = 0;
+    for (int i = 0; i < 11; ++i) { reg[i].bytes = sizes[i]; reg[i].off = off; off += align256(sizes[i]); }
+    h->ws_bytes = off;
+    hipError_t e = dev_alloc(&h->ws, off);
+    if (e != hipSuccess) return fail(MOE_ERR_OOM, "workspace of %zu bytes: %s", off, hipGetErrorString(e));
+    char *b = (char *)h->ws;
+    LayerParams &p = h->base;
+    p.logits = b + reg[0].off;
+    p.idx = (int32_t *)(b + reg[1].off);
+    p.wts = (float *)(b + reg[2].off);
+    p.sched = (int32_t *)(b + reg[3].off);
+    p.u = (uint16_t *)(b + reg[4].off);
+    p.shact = (uint16_t *)(b + reg[5].off);
+    p.eact = (uint16_t *)(b + reg[6].off);
+    p.eout = (uint16_t *)(b + reg[7].off);
+    p.comb = (uint16_t *)(b + reg[8].off);
+    p.shout = (uint16_t *)(b + reg[9].off);
+    p.err = (uint32_t *)(b + reg[10].off);
+    return MOE_OK;
+}
+
+static hipError_t clear_flag(moe_latent *h) {
+    hipLaunchKernelGGL(moe_clear_kernel, dim3(1), dim3(64), 0, h->stream, h->base.err, 64);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ API
+
+extern "C" const char *moe_latent_last_error(void) { return g_err.c_str(); }
+
+extern "C" int32_t moe_latent_live_allocations(void) { return g_live_allocs.load(); }
+
+extern "C" void moe_latent_destroy(moe_latent_t *h) {
+    if (!h || h->magic != kMagic) return;
+    (void)hipStreamSynchronize(h->stream);
+    dev_free(h->ws);
+    h->magic = 0;
+    delete h;
+}
+
+extern "C" int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w, void *hip_stream,
+                                 moe_latent_t **out) {
+    g_err.clear();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !w) return fail(MOE_ERR_INVALID_ARG, "cfg or weights is NULL");
+    int rc;
+    if ((rc = check_config(*cfg))) return rc;
+    if ((rc = check_weights(*cfg, *w))) return rc;
+    int dev = 0, cus = 0;
+    if ((rc = check_device(&dev, &cus))) return rc;
+
+    moe_latent *h = new moe_latent();
+    memset(&h->base, 0, sizeof h->base);
+    h->cfg = *cfg;
+    h->stream = (hipStream_t)hip_stream;
+    h->device = dev;
+    h->magic = kMagic;
+    h->last_rows = 0;
+
+    LayerParams &p = h->base;
+    p.H = cfg->hidden;
+    p.L = cfg->latent;
+    p.D = cfg->latent ? cfg->latent : cfg->hidden;
+    p.E = cfg->n_experts;
+    p.G = cfg->n_group;
+    p.TG = cfg->topk_group;
+    p.K = cfg->top_k;
+    p.I = cfg->expert_inter;
+    p.SI = cfg->shared_inter;
+    p.act_f16 = cfg->act_dtype == MOE_DT_F16;
+    p.router_f32 = cfg->router_dtype == MOE_DT_F32;
+    p.has_bias = cfg->has_bias != 0;
+    p.norm_topk = cfg->norm_topk != 0;
+    p.rho = cfg->routed_scaling;
+    p.gate_w16 = p.router_f32 ? nullptr : (const uint16_t *)w->gate_w.data;
+    p.gate_w32 = p.router_f32 ? (const float *)w->gate_w.data : nullptr;
+    p.bias = cfg->has_bias ? (const float *)w->corr_bias.data : nullptr;
+    p.fc1 = (const uint16_t *)w->fc1_w.data;
+    p.fc2 = (const uint16_t *)w->fc2_w.data;
+    p.up_q = (const uint32_t *)w->up_q.data;
+    p.up_s = (const uint16_t *)w->up_scales.data;
+    p.up_b = (const uint16_t *)w->up_biases.data;
+    p.dn_q = (const uint32_t *)w->down_q.data;
+    p.dn_s = (const uint16_t *)w->down_scales.data;
+    p.dn_b = (const uint16_t *)w->down_biases.data;
+    p.su = (const uint16_t *)w->shared_up.data;
+    p.sd = (const uint16_t *)w->shared_down.data;
+
+    if ((rc = setup_workspace(h))) {
+        delete h;
+        return rc;
+    }
+    (void)cus;
+    hipError_t e;
+    if ((e = clear_flag(h)) != hipSuccess || (e = hipStreamSynchronize(h->stream)) != hipSuccess) {
+        dev_free(h->ws);
+        delete h;
+        return fail(MOE_ERR_HIP, "initialising the workspace: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return MOE_OK;
+}
+
+static bool valid(moe_latent_t *h) { return h && h->magic == kMagic; }
+
+extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    h->stream = (hipStream_t)hip_stream;
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_set_variant(moe_latent_t *h, int32_t variant) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (variant == 0)
+        return fail(MOE_ERR_INVALID_ARG, "variant 0 (one fused launch per forward) is disabled: its first "
+                    "GPU run did not complete and the cause is not yet found");
+    if (variant != 1) return fail(MOE_ERR_INVALID_ARG, "variant %d (1: launch groups)", variant);
+    return MOE_OK;
+}
+
+static void plan_items(LayerParams &p, int rows) {
+    int n[NSTAGE];
+    p.rows = rows;
+    p.single_row = rows == 1;
+    const bool inline_combine = p.single_row && p.L > 0;
+    p.umax = p.E < rows * p.K ? p.E : rows * p.K;
+    p.up_blocks = (p.I + UP_BLOCK - 1) / UP_BLOCK;
+    p.dn_blocks = (p.D + DOWN_BLOCK - 1) / DOWN_BLOCK;
+    p.comb_blocks = (p.D + COMBINE_BLOCK - 1) / COMBINE_BLOCK;
+    n[ST_GATE] = (p.E + 3) / 4;
+    n[ST_FC1] = p.L ? p.L / DENSE_TILE : 0;
+    n[ST_SHUP] = p.SI / DENSE_TILE;
+    n[ST_ROUTE] = rows;
+    n[ST_SHDN] = p.SI ? p.H / DENSE_TILE : 0;
+    n[ST_SCHED] = p.single_row ? 0 : 1;
+    n[ST_UP] = p.umax * p.up_blocks;
+    n[ST_DOWN] = p.umax * p.dn_blocks;
+    n[ST_COMBINE] = inline_combine ? 0 : rows * p.comb_blocks;
+    n[ST_FC2] = p.L ? p.H / DENSE_TILE : 0;
+    p.item_base[0] = 0;
+    for (int s = 0; s < NSTAGE; ++s) p.item_base[s + 1] = p.item_base[s] + n[s];
+}
+
+template <int G>
+static void launch_group(const LayerParams &p, int first, int last, hipStream_t st) {
+    const int items = p.item_base[last + 1] - p.item_base[first];
+    if (items > 0) hipLaunchKernelGGL(moe_group_kernel<G>, dim3(items), dim3(WG_THREADS), 0, st, p);
+}
+
+extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
+    if (rows < 1 || rows > h->cfg.max_rows)
+        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
+    const size_t bytes = (size_t)rows * h->cfg.hidden * 2;
+    const char *a = (const char *)hidden_in, *b = (const char *)out;
+    if (a != b && a < b + bytes && b < a + bytes)
+        return fail(MOE_ERR_ALIAS, "out partially overlaps hidden_in");
+    LayerParams p = h->base;
+    p.x = (const uint16_t *)hidden_in;
+    p.out = (uint16_t *)out;
+    plan_items(p, rows);
+    hipStream_t st = h->stream;
+    launch_group<0>(p, ST_GATE, ST_SHUP, st);
+    launch_group<1>(p, ST_ROUTE, ST_SHDN, st);
+    launch_group<2>(p, ST_SCHED, ST_SCHED, st);
+    launch_group<3>(p, ST_UP, ST_UP, st);
+    launch_group<4>(p, ST_DOWN, ST_DOWN, st);
+    launch_group<5>(p, ST_COMBINE, ST_COMBINE, st);
+    launch_group<6>(p, ST_FC2, ST_FC2, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    h->last_rows = rows;
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
+                                       int32_t group) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
+    if (rows < 1 || rows > h->cfg.max_rows)
+        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
+    if (group < 0 || group > 6) return fail(MOE_ERR_INVALID_ARG, "group %d outside 0..6", group);
+    LayerParams p = h->base;
+    p.x = (const uint16_t *)hidden_in;
+    p.out = (uint16_t *)out;
+    plan_items(p, rows);
+    hipStream_t st = h->stream;
+    switch (group) {
+    case 0: launch_group<0>(p, ST_GATE, ST_SHUP, st); break;
+    case 1: launch_group<1>(p, ST_ROUTE, ST_SHDN, st); break;
+    case 2: launch_group<2>(p, ST_SCHED, ST_SCHED, st); break;
+    case 3: launch_group<3>(p, ST_UP, ST_UP, st); break;
+    case 4: launch_group<4>(p, ST_DOWN, ST_DOWN, st); break;
+    case 5: launch_group<5>(p, ST_COMBINE, ST_COMBINE, st); break;
+    default: launch_group<6>(p, ST_FC2, ST_FC2, st); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group) {
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows || group < 0 || group > 6) return -1;
+    LayerParams p = h->base;
+    plan_items(p, rows);
+    static const int first[7] = {ST_GATE, ST_ROUTE, ST_SCHED, ST_UP, ST_DOWN, ST_COMBINE, ST_FC2};
+    static const int last[7] = {ST_SHUP, ST_SHDN, ST_SCHED, ST_UP, ST_DOWN, ST_COMBINE, ST_FC2};
+    return p.item_base[last[group] + 1] - p.item_base[first[group]];
+}
+
+extern "C" int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (!h->last_rows) return fail(MOE_ERR_INVALID_ARG, "no forward yet");
+    const size_t n = (size_t)h->last_rows * h->cfg.top_k;
+    hipError_t e = hipSuccess;
+    if (idx_dev) e = hipMemcpyAsync(idx_dev, h->base.idx, n * 4, hipMemcpyDeviceToDevice, h->stream);
+    if (e == hipSuccess && w_dev) e = hipMemcpyAsync(w_dev, h->base.wts, n * 4, hipMemcpyDeviceToDevice, h->stream);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "routing copy: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_read_stage(moe_latent_t *h, int32_t stage, void *dst_dev, size_t bytes) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (!dst_dev) return fail(MOE_ERR_INVALID_ARG, "dst is NULL");
+    if (!h->last_rows) return fail(MOE_ERR_INVALID_ARG, "no forward yet");
+    const LayerParams &p = h->base;
+    const size_t R = h->last_rows;
+    const void *src = nullptr;
+    size_t avail = 0;
+    switch (stage) {
+    case MOE_STAGE_LOGITS: src = p.logits; avail = R * p.E * (p.router_f32 ? 4 : 2); break;
+    case MOE_STAGE_LATENT:
+        if (!p.L) return fail(MOE_ERR_INVALID_ARG, "non-latent layer: the latent is hidden_in");
+        src = p.u; avail = R * p.L * 2; break;
+    case MOE_STAGE_EXPERT_ACT: src = p.eact; avail = R * p.K * p.I * 2; break;
+    case MOE_STAGE_EXPERT_OUT: src = p.eout; avail = R * p.K * p.D * 2; break;
+    case MOE_STAGE_COMBINE: src = p.comb; avail = R * p.D * 2; break;
+    case MOE_STAGE_SHARED_ACT:
+        if (!p.SI) return fail(MOE_ERR_INVALID_ARG, "no shared expert");
+        src = p.shact; avail = R * p.SI * 2; break;
+    case MOE_STAGE_SHARED_OUT:
+        if (!p.SI) return fail(MOE_ERR_INVALID_ARG, "no shared expert");
+        src = p.shout; avail = R * p.H * 2; break;
+    default: return fail(MOE_ERR_INVALID_ARG, "unknown stage %d", stage);
+    }
+    if (bytes > avail) return fail(MOE_ERR_INVALID_ARG, "stage %d holds %zu bytes, %zu asked", stage, avail, bytes);
+    hipError_t e = hipMemcpyAsync(dst_dev, src, bytes, hipMemcpyDeviceToDevice, h->stream);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stage copy: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_status(moe_latent_t *h) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    hipError_t e = hipStreamSynchronize(h->stream);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream: %s", hipGetErrorString(e));
+    uint32_t flag = 0;
+    e = hipMemcpy(&flag, h->base.err, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "reading the error flag: %s", hipGetErrorString(e));
+    if (flag) {
+        (void)clear_flag(h);
+        (void)hipStreamSynchronize(h->stream);
+        return fail(MOE_ERR_DEVICE_CHECK, "device-side error flag %u (2: a route found no candidate, "
+                    "4: an invalid schedule)", flag);
+    }
+    return MOE_OK;
+}

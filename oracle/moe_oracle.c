@@ -347,6 +347,85 @@ void oracle_combine(const float *y, const float *w, int k, int D, float *out)
     }
 }
 
+/* ---------------------------------------------------------------- stages of the layer */
+
+enum { ORC_ST_LATENT = 2, ORC_ST_EXPERT_ACT = 3, ORC_ST_EXPERT_OUT = 4, ORC_ST_COMBINE = 5,
+       ORC_ST_SHARED_ACT = 6, ORC_ST_SHARED_OUT = 7, ORC_ST_FC2 = 8, ORC_ST_FINAL = 9 };
+
+/* One stage of one row, from that stage's own input (fp32 values of what the layer holds):
+ *   ORC_ST_LATENT      in = x [H]        -> u = rnd(W1 . x) [L]
+ *   ORC_ST_EXPERT_ACT  in = u [D], e     -> a = rnd(relu(rnd(U_e . u))^2) [I]
+ *   ORC_ST_EXPERT_OUT  in = a [I], e     -> y = rnd(D_e . a) [D]
+ *   ORC_ST_SHARED_ACT  in = x [H]        -> a' = rnd(relu(rnd(Su . x))^2) [SI]
+ *   ORC_ST_SHARED_OUT  in = a' [SI]      -> sh = rnd(Sd . a') [H]
+ *   ORC_ST_FC2         in = c [L]        -> m = rnd(W2 . c) [H]
+ *   ORC_ST_FINAL       in = x, in2 = m, in3 = sh (NULL: +0) [H] -> out = rnd(x + rnd(m + sh))
+ * out gets the rounded values, pre (if not NULL) the fp32 value before the last rounding.
+ * Returns 0, or -1 for a stage this configuration does not have. */
+int oracle_stage(const orc_cfg *cfg, const orc_weights *W, int stage, int e, const float *in,
+                 const float *in2, const float *in3, float *out, float *pre)
+{
+    int H = cfg->hidden, L = cfg->latent, I = cfg->expert_inter, SI = cfg->shared_inter;
+    int gs = cfg->group_size, D = L ? L : H;
+    int n = 0;
+    float *tmp = NULL;
+    switch (stage) {
+    case ORC_ST_LATENT:
+        if (!L) return -1;
+        n = L;
+        tmp = malloc(sizeof(float) * n);
+        oracle_dense(W->fc1_w, in, L, H, tmp);
+        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
+        break;
+    case ORC_ST_EXPERT_ACT:
+        n = I;
+        tmp = malloc(sizeof(float) * n);
+        oracle_q4_matvec(W->up_q + (size_t)e * I * (D / 8), W->up_s + (size_t)e * I * (D / gs),
+                         W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, tmp);
+        for (int i = 0; i < n; ++i) out[i] = relu_sq(cfg, rnd(cfg, tmp[i]));
+        break;
+    case ORC_ST_EXPERT_OUT:
+        n = D;
+        tmp = malloc(sizeof(float) * n);
+        oracle_q4_matvec(W->dn_q + (size_t)e * D * (I / 8), W->dn_s + (size_t)e * D * (I / gs),
+                         W->dn_b + (size_t)e * D * (I / gs), in, D, I, gs, tmp);
+        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
+        break;
+    case ORC_ST_SHARED_ACT:
+        if (!SI) return -1;
+        n = SI;
+        tmp = malloc(sizeof(float) * n);
+        oracle_dense(W->sh_up, in, SI, H, tmp);
+        for (int i = 0; i < n; ++i) out[i] = relu_sq(cfg, rnd(cfg, tmp[i]));
+        break;
+    case ORC_ST_SHARED_OUT:
+        if (!SI) return -1;
+        n = H;
+        tmp = malloc(sizeof(float) * n);
+        oracle_dense(W->sh_dn, in, H, SI, tmp);
+        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
+        break;
+    case ORC_ST_FC2:
+        if (!L) return -1;
+        n = H;
+        tmp = malloc(sizeof(float) * n);
+        oracle_dense(W->fc2_w, in, H, L, tmp);
+        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
+        break;
+    case ORC_ST_FINAL:
+        n = H;
+        tmp = malloc(sizeof(float) * n);
+        for (int i = 0; i < n; ++i) tmp[i] = in[i] + rnd(cfg, in2[i] + (in3 ? in3[i] : 0.0f));
+        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
+        break;
+    default:
+        return -1;
+    }
+    if (pre) memcpy(pre, tmp, sizeof(float) * n);
+    free(tmp);
+    return 0;
+}
+
 /* ---------------------------------------------------------------- the layer, one row */
 
 /* x_bits: [H] activation bits. Writes out_bits[H] (rounded), out_f32[H] (the value
@@ -362,13 +441,13 @@ int oracle_forward_row(const orc_cfg *cfg, const orc_weights *W, const uint16_t 
     if (H <= 0 || H % 512 || D % gs || I % gs || gs % 8 || K > 64) return -1;
     int rc = -2;
     float *x = malloc(sizeof(float) * H), *z = malloc(sizeof(float) * E);
-    float *u = malloc(sizeof(float) * D), *h = malloc(sizeof(float) * I);
+    float *u = malloc(sizeof(float) * D);
     float *a = malloc(sizeof(float) * (size_t)K * I), *y = malloc(sizeof(float) * (size_t)K * D);
     float *c = malloc(sizeof(float) * D), *m = malloc(sizeof(float) * H);
     float *sh = malloc(sizeof(float) * H), *tmp = malloc(sizeof(float) * (H > D ? H : D));
     float *gsh = SI ? malloc(sizeof(float) * SI) : NULL;
-    float *wrow = malloc(sizeof(float) * H);
-    if (!x || !z || !u || !h || !a || !y || !c || !m || !sh || !tmp || !wrow || (SI && !gsh))
+    float *wrow = malloc(sizeof(float) * H), *outv = malloc(sizeof(float) * H);
+    if (!x || !z || !u || !a || !y || !c || !m || !sh || !tmp || !wrow || !outv || (SI && !gsh))
         goto done;
 
     for (int k = 0; k < H; ++k) x[k] = act_load(cfg, x_bits[k]);
@@ -385,51 +464,31 @@ int oracle_forward_row(const orc_cfg *cfg, const orc_weights *W, const uint16_t 
     /* O2-O7 */
     rc = oracle_route(cfg, z, W->corr_bias, idx, w, st ? st->s : NULL);
     if (rc) goto done;
-
+    rc = -2;
     /* O8 latent projection */
-    if (L) {
-        oracle_dense(W->fc1_w, x, L, H, tmp);
-        for (int l = 0; l < L; ++l) u[l] = rnd(cfg, tmp[l]);
-    } else {
-        memcpy(u, x, sizeof(float) * H);
-    }
+    if (L) oracle_stage(cfg, W, ORC_ST_LATENT, 0, x, NULL, NULL, u, NULL);
+    else memcpy(u, x, sizeof(float) * H);
     /* O9 routed experts */
     for (int j = 0; j < K; ++j) {
-        int e = idx[j];
-        const uint32_t *uq = W->up_q + (size_t)e * I * (D / 8);
-        const uint16_t *us = W->up_s + (size_t)e * I * (D / gs), *ub = W->up_b + (size_t)e * I * (D / gs);
-        oracle_q4_matvec(uq, us, ub, u, I, D, gs, h);
-        for (int i = 0; i < I; ++i) a[(size_t)j * I + i] = relu_sq(cfg, rnd(cfg, h[i]));
-        const uint32_t *dq = W->dn_q + (size_t)e * D * (I / 8);
-        const uint16_t *ds = W->dn_s + (size_t)e * D * (I / gs), *db = W->dn_b + (size_t)e * D * (I / gs);
-        oracle_q4_matvec(dq, ds, db, a + (size_t)j * I, D, I, gs, tmp);
-        for (int d = 0; d < D; ++d) y[(size_t)j * D + d] = rnd(cfg, tmp[d]);
+        oracle_stage(cfg, W, ORC_ST_EXPERT_ACT, idx[j], u, NULL, NULL, a + (size_t)j * I, NULL);
+        oracle_stage(cfg, W, ORC_ST_EXPERT_OUT, idx[j], a + (size_t)j * I, NULL, NULL, y + (size_t)j * D, NULL);
     }
     /* O10 combine */
     oracle_combine(y, w, K, D, tmp);
     for (int d = 0; d < D; ++d) c[d] = rnd(cfg, tmp[d]);
     /* O11 back to hidden */
-    if (L) {
-        oracle_dense(W->fc2_w, c, H, L, tmp);
-        for (int n = 0; n < H; ++n) m[n] = rnd(cfg, tmp[n]);
-    } else {
-        memcpy(m, c, sizeof(float) * H);
-    }
+    if (L) oracle_stage(cfg, W, ORC_ST_FC2, 0, c, NULL, NULL, m, NULL);
+    else memcpy(m, c, sizeof(float) * H);
     /* O12 shared expert on the layer input */
     if (SI) {
-        oracle_dense(W->sh_up, x, SI, H, gsh);
-        for (int i = 0; i < SI; ++i) gsh[i] = relu_sq(cfg, rnd(cfg, gsh[i]));
-        oracle_dense(W->sh_dn, gsh, H, SI, tmp);
-        for (int n = 0; n < H; ++n) sh[n] = rnd(cfg, tmp[n]);
+        oracle_stage(cfg, W, ORC_ST_SHARED_ACT, 0, x, NULL, NULL, gsh, NULL);
+        oracle_stage(cfg, W, ORC_ST_SHARED_OUT, 0, gsh, NULL, NULL, sh, NULL);
     } else {
         for (int n = 0; n < H; ++n) sh[n] = 0.0f;
     }
     /* O13 + shared, + residual */
-    for (int n = 0; n < H; ++n) {
-        float v = x[n] + rnd(cfg, m[n] + sh[n]);
-        if (out_f32) out_f32[n] = v;
-        out_bits[n] = act_store(cfg, v);
-    }
+    oracle_stage(cfg, W, ORC_ST_FINAL, 0, x, m, sh, outv, out_f32);
+    for (int n = 0; n < H; ++n) out_bits[n] = act_store(cfg, outv[n]);
     if (st) {
         if (st->z) memcpy(st->z, z, sizeof(float) * E);
         if (st->u) memcpy(st->u, u, sizeof(float) * D);
@@ -441,8 +500,8 @@ int oracle_forward_row(const orc_cfg *cfg, const orc_weights *W, const uint16_t 
     }
     rc = 0;
 done:
-    free(x); free(z); free(u); free(h); free(a); free(y); free(c); free(m); free(sh);
-    free(tmp); free(gsh); free(wrow);
+    free(x); free(z); free(u); free(a); free(y); free(c); free(m); free(sh);
+    free(tmp); free(gsh); free(wrow); free(outv);
     return rc;
 }
 

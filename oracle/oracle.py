@@ -88,6 +88,9 @@ def lib():
                   "oracle_f16_to_f32_n"):
             getattr(f, n).restype = None
             getattr(f, n).argtypes = [_P, _P, ctypes.c_long]
+        f.oracle_stage.restype = ctypes.c_int
+        f.oracle_stage.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), ctypes.c_int,
+                                   ctypes.c_int, _P, _P, _P, _P, _P]
         f.oracle_gate_c64_rows.restype = None
         f.oracle_gate_c64_rows.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
     return _lib
@@ -165,6 +168,32 @@ def forward(dims, arrays: Dict[str, np.ndarray], x: Optional[np.ndarray] = None,
         res["a"] = res["a"].reshape(n, K, I)
         res["y"] = res["y"].reshape(n, K, D)
     return res
+
+
+STAGES = {"latent": 2, "expert_act": 3, "expert_out": 4, "shared_act": 6, "shared_out": 7,
+          "fc2": 8, "final": 9}
+
+
+def stage(dims, arrays: Dict[str, np.ndarray], name: str, inp: np.ndarray, expert: int = 0,
+          in2: Optional[np.ndarray] = None, in3: Optional[np.ndarray] = None):
+    """One stage of one row from its own input (fp32 values). Returns (rounded values as
+    fp32, fp32 value before the last rounding)."""
+    L = lib()
+    b = _Bound(dims, arrays)
+    D = dims.latent or dims.hidden
+    n = {"latent": dims.latent, "expert_act": dims.expert_inter, "expert_out": D,
+         "shared_act": dims.shared_inter, "shared_out": dims.hidden, "fc2": dims.hidden,
+         "final": dims.hidden}[name]
+    inp = np.ascontiguousarray(inp, np.float32)
+    in2 = _c(in2, np.float32)
+    in3 = _c(in3, np.float32)
+    out = np.zeros(n, np.float32)
+    pre = np.zeros(n, np.float32)
+    rc = L.oracle_stage(ctypes.byref(b.cfg), ctypes.byref(b.w), STAGES[name], int(expert), _ptr(inp),
+                        _ptr(in2), _ptr(in3), _ptr(out), _ptr(pre))
+    if rc:
+        raise ValueError(f"oracle_stage {name} failed: {rc}")
+    return out, pre
 
 
 def route(dims, z: np.ndarray, bias: Optional[np.ndarray]):

@@ -1,0 +1,287 @@
+"""Parity of the HIP layer (through the C ABI) with the CPU oracle, on the seeded workloads.
+
+Bars (the oracle's readings):
+* routing indices and weights: bit for bit;
+* gate logits: bit for bit (both sides use the same fixed summation order);
+* combine: bit for bit when the oracle combines the GPU's own expert outputs and weights;
+* layer outputs: relative error in the 2-norm <= 5e-3 and in the max-norm <= 2e-2 against
+  the oracle's fp32 value before its final rounding (so only the GPU's own last rounding
+  and fp32 summation-order differences count);
+* each row of a multi-row pass equals its own one-row pass bit for bit.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from latent_mixture_experts_bf16_amd import synth
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+REL_RMS = 5e-3
+REL_MAX = 2e-2
+
+
+def _LY():
+    from latent_mixture_experts_bf16_amd import layer as LY
+    return LY
+
+
+def _x_dev(dims, x_bits):
+    return _LY().to_device(x_bits)
+
+
+def _act(dims, bits):
+    return O.act_to_f32(dims, bits)
+
+
+def out_errors(dims, got_bits, ref_f32):
+    got = _act(dims, got_bits).astype(np.float64)
+    ref = ref_f32.astype(np.float64)
+    d = got - ref
+    rel_rms = np.sqrt((d ** 2).mean()) / np.sqrt((ref ** 2).mean())
+    rel_max = np.abs(d).max() / np.abs(ref).max()
+    return rel_rms, rel_max
+
+
+def assert_out_close(dims, got_bits, ref_f32, what=""):
+    assert np.isfinite(_act(dims, got_bits)).all(), what
+    rel_rms, rel_max = out_errors(dims, got_bits, ref_f32)
+    print(f"{what}: rel_rms {rel_rms:.2e} rel_max {rel_max:.2e}", flush=True)
+    assert rel_rms <= REL_RMS and rel_max <= REL_MAX, (what, rel_rms, rel_max)
+
+
+def act_ulp(dims, v):
+    """Unit in the last place of each value in the activation dtype."""
+    v = np.abs(np.asarray(v, np.float32))
+    if dims.act_dtype == 2:
+        return np.spacing(v.astype(np.float16)).astype(np.float64)
+    return np.spacing(v).astype(np.float64) * 65536.0
+
+
+def stage_close(dims, got, ref, what, ulps=1):
+    ref_vals, ref_pre = ref
+    got = np.asarray(got, np.float64)
+    rv = ref_vals.astype(np.float64)
+    rms = np.sqrt((rv ** 2).mean()) + 1e-30
+    err = np.abs(got - rv)
+    tol = ulps * act_ulp(dims, ref_vals) + 1e-4 * rms
+    eq = float((got == rv).mean())
+    assert eq >= 0.99 and (err <= tol).all(), (what, eq, float((err / tol).max()))
+
+
+_data = {}
+
+
+def workload(cid, rows=None, layer=0, instance=0):
+    key = (cid, rows, layer, instance)
+    if key not in _data:
+        if len(_data) > 3:
+            _data.clear()
+        dims, arrays = next(synth.workload_layers(cid, instance=instance, rows=rows, layers=[layer]))
+        _data[key] = (dims, arrays)
+    return _data[key]
+
+
+def run_gpu(dims, arrays, rows=None, variant=None, max_rows=None, x=None):
+    x = arrays["x"] if x is None else x
+    rows = x.shape[0] if rows is None else rows
+    lay = _LY().DeviceLayer(dims, arrays, max_rows or rows, variant=variant)
+    xd = _x_dev(dims, x)
+    out = torch.empty_like(xd)
+    lay.forward(xd, out, rows)
+    torch.cuda.synchronize()
+    lay.status()
+    return lay, xd, out
+
+
+# ---------------------------------------------------------------------------------- per config
+
+@pytest.mark.parametrize("cid", [0, 1, 3])
+def test_layer_matches_oracle(cid):
+    dims, arrays = workload(cid)
+    rows = arrays["x"].shape[0]
+    ref = O.forward(dims, arrays, stages=True)
+    lay, xd, out = run_gpu(dims, arrays)
+    idx, w = lay.routing(rows)
+    assert np.array_equal(idx, ref["idx"]), (idx, ref["idx"])
+    assert np.array_equal(w.view(np.uint32), ref["w"].view(np.uint32))
+    # gate logits: bit for bit
+    z = lay.stage("logits", rows)
+    zf = z if dims.router_dtype == 3 else O.bf16_to_f32(z)
+    assert np.array_equal(zf.reshape(rows, -1).view(np.uint32), ref["z"].view(np.uint32))
+    # combine of the GPU's own expert outputs: bit for bit
+    D = dims.latent or dims.hidden
+    y = _act(dims, lay.stage("expert_out", rows)).reshape(rows, dims.top_k, D)
+    c = lay.stage("combine", rows)
+    for r in range(rows):
+        cc = O.combine(y[r], w[r])
+        want = O.f32_to_f16(cc) if dims.act_dtype == 2 else O.f32_to_bf16(cc)
+        assert np.array_equal(c[r], want)
+    # every other stage, fed its own GPU input: equal to the oracle's stage up to fp32
+    # summation order -- one unit in the last place (plus 1e-4 of the stage's RMS for sums
+    # that cancel); after relu^2 five: a one-unit flip of the rounded pre-activation h moves
+    # h^2 by 2*h*ulp(h), up to 4 units of h^2 when h^2 falls in the lower half of its binade
+    x = _act(dims, arrays["x"])
+    I = dims.expert_inter
+    u = _act(dims, lay.stage("latent", rows)) if dims.latent else x
+    a = _act(dims, lay.stage("expert_act", rows)).reshape(rows, dims.top_k, I)
+    for r in range(rows):
+        if dims.latent:
+            stage_close(dims, u[r], O.stage(dims, arrays, "latent", x[r]), "latent")
+        for j in range(dims.top_k):
+            e = int(idx[r, j])
+            stage_close(dims, a[r, j], O.stage(dims, arrays, "expert_act", u[r], e), "expert_act", ulps=5)
+            stage_close(dims, y[r, j], O.stage(dims, arrays, "expert_out", a[r, j], e), "expert_out")
+        if dims.shared_inter:
+            sa = _act(dims, lay.stage("shared_act", rows))
+            so = _act(dims, lay.stage("shared_out", rows))
+            stage_close(dims, sa[r], O.stage(dims, arrays, "shared_act", x[r]), "shared_act", ulps=5)
+            stage_close(dims, so[r], O.stage(dims, arrays, "shared_out", sa[r]), "shared_out")
+    assert_out_close(dims, out.cpu().numpy().view(np.uint16), ref["out_f32"], f"cfg{cid}")
+    lay.close()
+
+
+@pytest.mark.skip(reason="the one-launch fused variant is disabled: its first GPU run did not "
+                         "complete and the cause is not yet found; see DESIGN.md")
+def test_fused_and_staged_launches_agree_bitwise():
+    for cid in (0, 1):
+        dims, arrays = workload(cid)
+        outs = []
+        for variant in (0, 1, 0):
+            lay, xd, out = run_gpu(dims, arrays, variant=variant)
+            outs.append((out.cpu().numpy(), *lay.routing(xd.shape[0])))
+            lay.close()
+        for o in outs[1:]:
+            for a, b in zip(outs[0], o):
+                assert np.array_equal(a, b)
+
+
+def test_repeated_forwards_are_deterministic():
+    dims, arrays = workload(1)
+    lay = _LY().DeviceLayer(dims, arrays, 1)
+    xd = _x_dev(dims, arrays["x"])
+    first = None
+    for _ in range(5):
+        out = torch.empty_like(xd)
+        lay.forward(xd, out)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        if first is None:
+            first = o
+        assert np.array_equal(o, first)
+    lay.status()
+    lay.close()
+
+
+def test_sixteen_rows_equal_sixteen_single_row_passes():
+    """The 16-row E=496 workload (prompt rows pushed through the decode kernels 16 at a time,
+    TensorFold pull request 1038, «Not yet / next»): each row equals its own 1-row pass bit
+    for bit, and all rows match the oracle."""
+    dims, arrays = workload(2)
+    lay, xd, out = run_gpu(dims, arrays)
+    multi = out.cpu().numpy()
+    idx16, w16 = lay.routing(16)
+    for r in range(16):
+        o1 = torch.empty_like(xd[r:r + 1])
+        lay.forward(xd[r:r + 1].contiguous(), o1, 1)
+        torch.cuda.synchronize()
+        assert np.array_equal(o1.cpu().numpy()[0], multi[r]), r
+        i1, w1 = lay.routing(1)
+        assert np.array_equal(i1[0], idx16[r]) and np.array_equal(w1[0], w16[r])
+    lay.status()
+    ref = O.forward(dims, arrays)
+    assert np.array_equal(idx16, ref["idx"])
+    assert np.array_equal(w16.view(np.uint32), ref["w"].view(np.uint32))
+    assert_out_close(dims, multi.view(np.uint16), ref["out_f32"], "cfg2 16 rows")
+    lay.close()
+
+
+@pytest.mark.parametrize("rows", [1, 2, 9, 16, 17, 64, 256])
+def test_tiny_layer_ragged_and_max_rows(rows):
+    """Row counts that span several 16-row tiles with a ragged tail, up to max_rows = 256."""
+    dims, arrays = workload(0, rows=rows)
+    ref = O.forward(dims, arrays)
+    lay, xd, out = run_gpu(dims, arrays, max_rows=256)
+    idx, w = lay.routing(rows)
+    assert np.array_equal(idx, ref["idx"])
+    assert np.array_equal(w.view(np.uint32), ref["w"].view(np.uint32))
+    assert_out_close(dims, out.cpu().numpy().view(np.uint16), ref["out_f32"], f"cfg0 rows {rows}")
+    lay.close()
+
+
+def test_in_place_output():
+    dims, arrays = workload(0, rows=9)
+    ref = O.forward(dims, arrays)
+    lay = _LY().DeviceLayer(dims, arrays, 9)
+    xd = _x_dev(dims, arrays["x"])
+    lay.forward(xd, xd)          # out == hidden_in
+    torch.cuda.synchronize()
+    lay.status()
+    assert_out_close(dims, xd.cpu().numpy().view(np.uint16), ref["out_f32"], "in place")
+    lay.close()
+
+
+@pytest.mark.parametrize("layer", list(range(8)))
+def test_eight_layer_stack_64_rows(layer):
+    """One layer of the 8-layer, 64-row stack (expert counts cycling 240..496): routing of all
+    64 rows bit for bit, outputs of sampled rows against the oracle."""
+    dims, arrays = workload(4, layer=layer)
+    lay, xd, out = run_gpu(dims, arrays)
+    idx, w = lay.routing(64)
+    got = out.cpu().numpy().view(np.uint16)
+    x = O.bf16_to_f32(arrays["x"])
+    z = O.bf16_to_f32(O.f32_to_bf16(O.gate_c64(x, O.bf16_to_f32(arrays["gate_w"]))))
+    for r in range(64):
+        i_ref, w_ref, _ = O.route(dims, z[r], arrays["corr_bias"])
+        assert np.array_equal(idx[r], i_ref), r
+        assert np.array_equal(w[r].view(np.uint32), w_ref.view(np.uint32)), r
+    sample = [0, 17 + layer, 63]
+    ref = O.forward(dims, arrays, rows=sample)
+    assert_out_close(dims, got[sample], ref["out_f32"], f"cfg4 layer {layer}")
+    lay.close()
+    del lay, xd, out
+    _data.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------------- the boundary
+
+def test_rows_and_alias_refused():
+    from latent_mixture_experts_bf16_amd import binding as B
+    dims, arrays = workload(0, rows=4)
+    lay = _LY().DeviceLayer(dims, arrays, 4)
+    xd = _x_dev(dims, arrays["x"])
+    out = torch.empty_like(xd)
+    assert B.STATUS[B.moe_latent_forward_rc(lay.handle, 5, xd.data_ptr(), out.data_ptr())] == "MOE_ERR_ROWS"
+    assert B.STATUS[B.moe_latent_forward_rc(lay.handle, 0, xd.data_ptr(), out.data_ptr())] == "MOE_ERR_ROWS"
+    assert B.STATUS[B.moe_latent_forward_rc(lay.handle, 4, xd.data_ptr(), xd.data_ptr() + 2)] == "MOE_ERR_ALIAS"
+    lay.close()
+
+
+def test_create_destroy_leaves_nothing_allocated():
+    from latent_mixture_experts_bf16_amd import binding as B
+    dims, arrays = workload(0)
+    before = B.moe_latent_live_allocations()
+    lay = _LY().DeviceLayer(dims, arrays, 8)
+    assert B.moe_latent_live_allocations() > before
+    lay.close()
+    assert B.moe_latent_live_allocations() == before
+
+
+def test_variant_zero_is_refused():
+    from latent_mixture_experts_bf16_amd import binding as B
+    dims, arrays = workload(0)
+    lay = _LY().DeviceLayer(dims, arrays, 1)
+    with pytest.raises(B.MoeError):
+        B.moe_latent_set_variant(lay.handle, 0)
+    B.moe_latent_set_variant(lay.handle, 1)
+    lay.close()
+
+
+def test_wrong_architecture_and_device_checks_pass_on_gfx950():
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
