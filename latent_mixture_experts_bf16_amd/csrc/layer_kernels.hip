@@ -92,29 +92,79 @@ __device__ __forceinline__ void nibbles8(uint32_t w, float *q) {
 
 // ------------------------------------------------------------------ gate
 
-// Item: 4 experts (one per wave), all rows. Fixed summation order described above.
+// Item: NW experts (one per wave), all rows. Fixed summation order described above. The
+// loads of a row are issued before its arithmetic; bf16 gate rows of up to 4096 inputs stay
+// in registers across the rows of the pass.
+template <int NW>
 __device__ __forceinline__ void gate_item(const LayerParams &p, int item) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = item * 4 + wave;
+    const int e = item * NW + wave;
     if (e >= p.E) return;
     const int nj = p.H / 512;
+    if (!p.router_f32 && nj <= 8) {
+        const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
+        uint4 wv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < nj) wv[j] = *(const uint4 *)(wr + 512 * j);
+        for (int r = 0; r < p.rows; ++r) {
+            const uint16_t *xr = p.x + (size_t)r * p.H + 8 * lane;
+            uint4 xv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < nj) xv[j] = *(const uint4 *)(xr + 512 * j);
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < nj) {
+                    float xf[8], wf[8];
+                    unpack8(p.act_f16, xv[j], xf);
+                    unpack8(0, wv[j], wf);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
+            if (lane == 0) ((uint16_t *)p.logits)[(size_t)r * p.E + e] = f2bf(acc);
+        }
+        return;
+    }
     for (int r = 0; r < p.rows; ++r) {
         const uint16_t *xr = p.x + (size_t)r * p.H;
         float acc = 0.0f;
-        for (int j = 0; j < nj; ++j) {
-            const int k0 = 512 * j + 8 * lane;
-            float xf[8], wf[8];
-            unpack8(p.act_f16, *(const uint4 *)(xr + k0), xf);
-            if (p.router_f32) {
-                const float4 *wp = (const float4 *)(p.gate_w32 + (size_t)e * p.H + k0);
-                const float4 a = wp[0], b = wp[1];
-                wf[0] = a.x; wf[1] = a.y; wf[2] = a.z; wf[3] = a.w;
-                wf[4] = b.x; wf[5] = b.y; wf[6] = b.z; wf[7] = b.w;
-            } else {
-                unpack8(0, *(const uint4 *)(p.gate_w16 + (size_t)e * p.H + k0), wf);
+        for (int j0 = 0; j0 < nj; j0 += 4) {
+            uint4 xv[4], wv[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (j0 + q < nj) {
+                    const int k0 = 512 * (j0 + q) + 8 * lane;
+                    xv[q] = *(const uint4 *)(xr + k0);
+                    if (p.router_f32) {
+                        wv[q][0] = *(const uint4 *)(p.gate_w32 + (size_t)e * p.H + k0);
+                        wv[q][1] = *(const uint4 *)(p.gate_w32 + (size_t)e * p.H + k0 + 4);
+                    } else {
+                        wv[q][0] = *(const uint4 *)(p.gate_w16 + (size_t)e * p.H + k0);
+                    }
+                }
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
+            for (int q = 0; q < 4; ++q) {
+                if (j0 + q < nj) {
+                    float xf[8], wf[8];
+                    unpack8(p.act_f16, xv[q], xf);
+                    if (p.router_f32) {
+                        const uint32_t w8[8] = {wv[q][0].x, wv[q][0].y, wv[q][0].z, wv[q][0].w,
+                                                wv[q][1].x, wv[q][1].y, wv[q][1].z, wv[q][1].w};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) wf[i] = __uint_as_float(w8[i]);
+                    } else {
+                        unpack8(0, wv[q][0], wf);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
+                }
+            }
         }
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
@@ -149,22 +199,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+template <int NT>
 struct RouteLds {
     float s[MAX_EXPERTS];
     float b[MAX_EXPERTS];
     float gam[256];
     int keep[256];
-    uint64_t best[4];
+    uint64_t best[NT / 64];
     int picks[MAX_TOPK];
 };
 
 // Item: one row (TensorFold pull request 1038, «Per operator and row invariance»:
 // group_expert_select at k = 9; pull request 1295, «What this changes»: sigmoid top-8 with
 // per-expert norm and sum).
-__device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds &L) {
+template <int NT>
+__device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds<NT> &L) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int E = p.E, G = p.G, per = p.E / p.G;
-    for (int e = tid; e < E; e += WG_THREADS) {
+    for (int e = tid; e < E; e += NT) {
         const float z = p.router_f32 ? ((const float *)p.logits)[(size_t)r * E + e]
                                      : bf2f(((const uint16_t *)p.logits)[(size_t)r * E + e]);
         const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
@@ -173,7 +225,7 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     }
     __syncthreads();
     // group scores: one thread per group, two best members by rank
-    for (int g = tid; g < G; g += WG_THREADS) {
+    for (int g = tid; g < G; g += NT) {
         uint64_t k1 = 0, k2 = 0;
         int i1 = -1, i2 = -1;
         for (int e = g * per; e < (g + 1) * per; ++e) {
@@ -185,7 +237,7 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     }
     __syncthreads();
     // kept groups: rank among groups < topk_group
-    for (int g = tid; g < G; g += WG_THREADS) {
+    for (int g = tid; g < G; g += NT) {
         const uint64_t kg = rank_key(L.gam[g], g);
         int rank = 0;
         for (int h = 0; h < G; ++h) rank += rank_key(L.gam[h], h) > kg;
@@ -193,25 +245,25 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     }
     __syncthreads();
     // top-k among candidates: k rounds of a workgroup-wide max of 64-bit keys
-    uint64_t mine[MAX_EXPERTS / WG_THREADS];
+    uint64_t mine[MAX_EXPERTS / NT];
 #pragma unroll
-    for (int m = 0; m < MAX_EXPERTS / WG_THREADS; ++m) {
-        const int e = tid + m * WG_THREADS;
+    for (int m = 0; m < MAX_EXPERTS / NT; ++m) {
+        const int e = tid + m * NT;
         mine[m] = (e < E && L.keep[e / per]) ? rank_key(L.b[e], e) : 0ull;
     }
     for (int j = 0; j < p.K; ++j) {
         uint64_t v = 0;
 #pragma unroll
-        for (int m = 0; m < MAX_EXPERTS / WG_THREADS; ++m) v = mine[m] > v ? mine[m] : v;
+        for (int m = 0; m < MAX_EXPERTS / NT; ++m) v = mine[m] > v ? mine[m] : v;
         v = wave_max_u64(v);
         if (lane == 0) L.best[wave] = v;
         __syncthreads();
         uint64_t w = L.best[0];
 #pragma unroll
-        for (int q = 1; q < 4; ++q) w = L.best[q] > w ? L.best[q] : w;
+        for (int q = 1; q < NT / 64; ++q) w = L.best[q] > w ? L.best[q] : w;
         int e = (int)(0xFFFFFFFFu - (uint32_t)w);
 #pragma unroll
-        for (int m = 0; m < MAX_EXPERTS / WG_THREADS; ++m)
+        for (int m = 0; m < MAX_EXPERTS / NT; ++m)
             if (mine[m] == w) mine[m] = 0ull;
         if (w == 0ull || e < 0 || e >= E) {   // no candidate left: excluded by the host checks
             e = 0;
@@ -323,78 +375,94 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
 
 enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
 
+template <int NW>
 struct DenseLds {
-    f32x4 part[4][4][64];   // [wave][row tile][lane]
+    f32x4 part[NW][2][64];   // [wave][row tile][lane]
 };
 
 // Item: outputs n0..n0+15 of W [N][K] (bf16, row-major) against X [rows][K] (bf16), all rows.
-// Wave w sums a contiguous quarter (or half / all) of K; per 128 inputs each lane holds 32
-// consecutive k of one weight row (64 B) and of one input row, fed to 4 MFMAs of 32.
-template <int EPI>
+// K is split over up to NW waves in contiguous slices (each a multiple of 128); per 128
+// inputs each lane holds 32 consecutive k of one weight row (64 B) and of one input row,
+// fed to 4 MFMAs of 32. A wave first issues the loads of up to 4 such steps of its weight
+// slice, then multiplies. The slices' partial sums are joined in wave order.
+template <int EPI, int NW>
 __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t *__restrict__ W,
-                           const uint16_t *__restrict__ X, int K, int n0, DenseLds &L) {
+                                           const uint16_t *__restrict__ X, int K, int n0, DenseLds<NW> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nr = lane & 15, grp = lane >> 4;
-    const int nsplit = (K % 512 == 0) ? 4 : ((K % 256 == 0) ? 2 : 1);
-    const int kw = K / nsplit;
+    int nsplit = NW;
+    while (nsplit > 1 && K % (128 * nsplit)) nsplit >>= 1;
+    const int kw = K / nsplit, nit = kw / 128;
     const int nrt = (p.rows + 15) >> 4;
-    for (int rt0 = 0; rt0 < nrt; rt0 += 4) {
-        f32x4 acc[4];
+    constexpr int RT = 2;   // row tiles (16 rows each) per pass over the weights
+    for (int rt0 = 0; rt0 < nrt; rt0 += RT) {
+        f32x4 acc[RT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < RT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (wave < nsplit) {
             const uint16_t *wrow = W + (size_t)(n0 + nr) * K + wave * kw + 32 * grp;
-            for (int kb = 0; kb < kw; kb += 128) {
-                const uint4 *wp = (const uint4 *)(wrow + kb);
-                const uint4 a0 = wp[0], a1 = wp[1], a2 = wp[2], a3 = wp[3];
+            const size_t xoff = (size_t)wave * kw + 32 * grp;
+            for (int i0 = 0; i0 < nit; i0 += 4) {
+                uint4 a[4][4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int row = (rt0 + t) * 16 + nr;
-                    if (rt0 + t < nrt) {
-                        uint4 b0 = {0, 0, 0, 0}, b1 = b0, b2 = b0, b3 = b0;
-                        if (row < p.rows) {
-                            const uint4 *xp = (const uint4 *)(X + (size_t)row * K + wave * kw + 32 * grp + kb);
-                            b0 = xp[0]; b1 = xp[1]; b2 = xp[2]; b3 = xp[3];
+                for (int q = 0; q < 4; ++q) {
+                    if (i0 + q < nit) {
+                        const uint4 *wp = (const uint4 *)(wrow + 128 * (i0 + q));
+                        a[q][0] = wp[0]; a[q][1] = wp[1]; a[q][2] = wp[2]; a[q][3] = wp[3];
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (i0 + q < nit) {
+                        const int kb = 128 * (i0 + q);
+#pragma unroll
+                        for (int t = 0; t < RT; ++t) {
+                            const int row = (rt0 + t) * 16 + nr;
+                            if (rt0 + t < nrt) {
+                                uint4 b0 = {0, 0, 0, 0}, b1 = b0, b2 = b0, b3 = b0;
+                                if (row < p.rows) {
+                                    const uint4 *xp = (const uint4 *)(X + (size_t)row * K + xoff + kb);
+                                    b0 = xp[0]; b1 = xp[1]; b2 = xp[2]; b3 = xp[3];
+                                }
+                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, a[q][0]), __builtin_bit_cast(bf16x8, b0), acc[t], 0, 0, 0);
+                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, a[q][1]), __builtin_bit_cast(bf16x8, b1), acc[t], 0, 0, 0);
+                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, a[q][2]), __builtin_bit_cast(bf16x8, b2), acc[t], 0, 0, 0);
+                                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, a[q][3]), __builtin_bit_cast(bf16x8, b3), acc[t], 0, 0, 0);
+                            }
                         }
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b0), acc[t], 0, 0, 0);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1), acc[t], 0, 0, 0);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a2), __builtin_bit_cast(bf16x8, b2), acc[t], 0, 0, 0);
-                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a3), __builtin_bit_cast(bf16x8, b3), acc[t], 0, 0, 0);
                     }
                 }
             }
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) L.part[wave][t][lane] = acc[t];
+        for (int t = 0; t < RT; ++t) L.part[wave][t][lane] = acc[t];
         __syncthreads();
-        // wave t4 finishes row tile rt0 + t4: partials joined in wave order
-        {
+        // wave t finishes row tile rt0 + t: partials joined in wave order
+        if (wave < RT && rt0 + wave < nrt) {
             const int t = wave;
-            if (rt0 + t < nrt) {
-                f32x4 v = L.part[0][t][lane];
-                for (int q = 1; q < nsplit; ++q) v = v + L.part[q][t][lane];
-                const int row = (rt0 + t) * 16 + nr;
-                if (row < p.rows) {
+            f32x4 v = L.part[0][t][lane];
+            for (int q = 1; q < nsplit; ++q) v = v + L.part[q][t][lane];
+            const int row = (rt0 + t) * 16 + nr;
+            if (row < p.rows) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + 4 * grp + i;
-                        const float a = v[i];
-                        if (EPI == EPI_FC1) {
-                            p.u[(size_t)row * p.L + n] = f2bf(a);
-                        } else if (EPI == EPI_SHUP) {
-                            p.shact[(size_t)row * p.SI + n] = f2bf(relu_sq(0, rnd(0, a)));
-                        } else if (EPI == EPI_SHDN) {
-                            p.shout[(size_t)row * p.H + n] = f2bf(a);
-                        } else {
-                            const float m = rnd(0, a);
-                            const float sh = p.SI ? bf2f(p.shout[(size_t)row * p.H + n]) : 0.0f;
-                            const float xv = bf2f(p.x[(size_t)row * p.H + n]);
-                            p.out[(size_t)row * p.H + n] = f2bf(xv + rnd(0, m + sh));
-                        }
+                for (int i = 0; i < 4; ++i) {
+                    const int n = n0 + 4 * grp + i;
+                    const float a = v[i];
+                    if (EPI == EPI_FC1) {
+                        p.u[(size_t)row * p.L + n] = f2bf(a);
+                    } else if (EPI == EPI_SHUP) {
+                        p.shact[(size_t)row * p.SI + n] = f2bf(relu_sq(0, rnd(0, a)));
+                    } else if (EPI == EPI_SHDN) {
+                        p.shout[(size_t)row * p.H + n] = f2bf(a);
+                    } else {
+                        const float m = rnd(0, a);
+                        const float sh = p.SI ? bf2f(p.shout[(size_t)row * p.H + n]) : 0.0f;
+                        const float xv = bf2f(p.x[(size_t)row * p.H + n]);
+                        p.out[(size_t)row * p.H + n] = f2bf(xv + rnd(0, m + sh));
                     }
                 }
             }
@@ -405,12 +473,33 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
 
 // ------------------------------------------------------------------ routed experts (4-bit)
 
+// LDS of one expert item: a block of NB output rows' codes, scales and biases (NB chosen on
+// the host so that they fit).
+struct ExpertLds {
+    uint4 q[EXPERT_LDS_CODES / 16];
+    uint16_t s[EXPERT_LDS_SCALES / 2];
+    uint16_t b[EXPERT_LDS_SCALES / 2];
+};
+
+// Copy `units` 16-byte units from global src to LDS dst with direct global->LDS loads
+// (each wave moves 1 KB per instruction, lane i the i-th 16 bytes).
+__device__ __forceinline__ void stage_lds(const uint4 *src, uint4 *dst, int units) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int u0 = wave * 64; u0 < units; u0 += WG_THREADS) {
+        if (u0 + lane < units)
+            __builtin_amdgcn_global_load_lds((const void *)(src + u0 + lane),
+                                             (__attribute__((address_space(3))) void *)(dst + u0), 16, 0, 0);
+    }
+}
+
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
-// pair (row, pick) of that slot. Each output row's K inputs are split in chunks of 32 (one
-// 16-byte load of codes); a row is handled by Cp lanes (Cp = chunks rounded up to a power of
-// two, at most 64; NCH chunks per lane when there are more than 64).
-template <int NCH, int RB, bool UP>
-__device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int blk) {
+// pair (row, pick) of that slot. The block's 4-bit codes, scales and biases are first staged
+// in LDS (all the item's weight bytes in flight at once; each is read from HBM once, whatever
+// the number of rows). Each output row's inputs are split in chunks of 32 (16 bytes of
+// codes); a row is handled by Cp lanes (Cp = chunks rounded up to a power of two, at most
+// 64; NCH chunks per lane when there are more than 64).
+template <int NCH, bool UP>
+__device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int blk, ExpertLds &L) {
     const int U = p.sched[SCH_U];
     if (slot >= U) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -423,106 +512,86 @@ __device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int 
         return;
     }
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
-    const int NB = UP ? UP_BLOCK : DOWN_BLOCK;
-    const int n0 = blk * NB, n1 = min(N, n0 + NB);
-    const int C = Kin >> 5;
+    const int NB = UP ? p.up_nb : p.dn_nb;
+    const int n0 = blk * NB;
+    const int C = Kin >> 5, G64 = Kin >> 6;
+    const size_t qrow = (size_t)(Kin >> 3);
+    const uint32_t *Q = (UP ? p.up_q : p.dn_q) + ((size_t)e * N + n0) * qrow;
+    const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G64;
+    const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G64;
+    stage_lds((const uint4 *)Q, L.q, NB * C);
+    stage_lds((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
+    stage_lds((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
+
     int Cp = 1;
     while (Cp < C && Cp < 64) Cp <<= 1;
     const int rpp = 64 / Cp;
     const int lrow = lane / Cp, c0 = lane % Cp;
-    const size_t qrow = (size_t)(Kin >> 3), grow = (size_t)(Kin >> 6);
-    const uint32_t *Q = (UP ? p.up_q : p.dn_q) + (size_t)e * N * qrow;
-    const uint16_t *S = (UP ? p.up_s : p.dn_s) + (size_t)e * N * grow;
-    const uint16_t *B = (UP ? p.up_b : p.dn_b) + (size_t)e * N * grow;
     const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    for (int rb0 = 0; rb0 < R; rb0 += RB) {
-        // per pair: the row of the input, and each of this lane's chunks summed; with one
-        // chunk per lane the chunk itself is also kept in registers (fp32), with more it is
-        // re-read from cache for every output row
-        const uint16_t *xrow[RB];
-        float xf[RB][NCH == 1 ? 32 : 1];
-        float xs[RB][NCH];
-        int pr[RB];
+    for (int r = 0; r < R; ++r) {
+        int pr = p.sched[SCH_PAIRS + off + r];
+        if (pr >= NP) pr = NP - 1;
+        const uint16_t *xrow = xin + (UP ? (size_t)(pr / p.K) * Kin : (size_t)pr * Kin);
+        // this lane's input chunks: summed, and with one chunk per lane also kept in
+        // registers (fp32); with more they are re-read from cache for every output row
+        float xf[NCH == 1 ? 32 : 1];
+        float xs[NCH];
 #pragma unroll
-        for (int rr = 0; rr < RB; ++rr) {
-            pr[rr] = (rb0 + rr < R) ? p.sched[SCH_PAIRS + off + rb0 + rr] : -1;
-            if (pr[rr] >= NP) pr[rr] = -1;
-            xrow[rr] = xin + (pr[rr] < 0 ? 0 : (UP ? (size_t)(pr[rr] / p.K) * Kin : (size_t)pr[rr] * Kin));
+        for (int m = 0; m < NCH; ++m) {
+            const int c = c0 + 64 * m;
+            float t[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) t[i] = 0.0f;
+            if (c < C) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], &t[8 * q4]);
+            }
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) sum = sum + t[i];
+            xs[m] = sum;
+            if constexpr (NCH == 1) {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xf[i] = t[i];
+            }
+        }
+        for (int nb = wave * rpp; nb < NB; nb += 4 * rpp) {
+            const int nl = nb + lrow;                 // row within the block
+            float acc = 0.0f;
 #pragma unroll
             for (int m = 0; m < NCH; ++m) {
                 const int c = c0 + 64 * m;
-                float t[32];
+                if (nl < NB && c < C) {
+                    const uint4 qv = L.q[nl * C + c];
+                    const float sc = bf2f(L.s[nl * G64 + (c >> 1)]);
+                    const float bi = bf2f(L.b[nl * G64 + (c >> 1)]);
+                    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+                    float part = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 32; ++i) t[i] = 0.0f;
-                if (pr[rr] >= 0 && c < C) {
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        float qf[8], xv[8];
+                        nibbles8(qw[q4], qf);
+                        if constexpr (NCH == 1) {
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        unpack8(p.act_f16, ((const uint4 *)(xrow[rr] + 32 * c))[q4], &t[8 * q4]);
-                }
-                float sum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) sum = sum + t[i];
-                xs[rr][m] = sum;
-                if constexpr (NCH == 1) {
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) xf[rr][i] = t[i];
-                }
-            }
-        }
-        for (int nb = n0 + wave * rpp; nb < n1; nb += 4 * rpp) {
-            const int n = nb + lrow;
-            float acc[RB];
-#pragma unroll
-            for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.0f;
-            if (n < n1) {
-#pragma unroll
-                for (int m = 0; m < NCH; ++m) {
-                    const int c = c0 + 64 * m;
-                    if (c < C) {
-                        const uint4 qv = *(const uint4 *)(Q + (size_t)n * qrow + 4 * c);
-                        const float sc = bf2f(S[(size_t)n * grow + (c >> 1)]);
-                        const float bi = bf2f(B[(size_t)n * grow + (c >> 1)]);
-                        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-                        float part[RB];
-#pragma unroll
-                        for (int rr = 0; rr < RB; ++rr) part[rr] = 0.0f;
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            float qf[8];
-                            nibbles8(qw[q4], qf);
-#pragma unroll
-                            for (int rr = 0; rr < RB; ++rr) {
-                                float xv[8];
-                                if constexpr (NCH == 1) {
-#pragma unroll
-                                    for (int i = 0; i < 8; ++i) xv[i] = xf[rr][8 * q4 + i];
-                                } else if (pr[rr] >= 0) {
-                                    unpack8(p.act_f16, ((const uint4 *)(xrow[rr] + 32 * c))[q4], xv);
-                                } else {
-#pragma unroll
-                                    for (int i = 0; i < 8; ++i) xv[i] = 0.0f;
-                                }
-#pragma unroll
-                                for (int i = 0; i < 8; ++i) part[rr] = __builtin_fmaf(qf[i], xv[i], part[rr]);
-                            }
+                            for (int i = 0; i < 8; ++i) xv[i] = xf[8 * q4 + i];
+                        } else {
+                            unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], xv);
                         }
 #pragma unroll
-                        for (int rr = 0; rr < RB; ++rr) {
-                            acc[rr] = __builtin_fmaf(sc, part[rr], acc[rr]);
-                            acc[rr] = __builtin_fmaf(bi, xs[rr][m], acc[rr]);
-                        }
+                        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qf[i], xv[i], part);
                     }
+                    acc = __builtin_fmaf(sc, part, acc);
+                    acc = __builtin_fmaf(bi, xs[m], acc);
                 }
             }
-#pragma unroll
-            for (int rr = 0; rr < RB; ++rr) {
-                float v = acc[rr];
-                for (int d = Cp >> 1; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
-                if (c0 == 0 && n < n1 && pr[rr] >= 0) {
-                    if (UP) p.eact[(size_t)pr[rr] * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, v)));
-                    else p.eout[(size_t)pr[rr] * p.D + n] = f2act(p.act_f16, v);
-                }
+            for (int d = Cp >> 1; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
+            if (c0 == 0 && nl < NB) {
+                const int n = n0 + nl;
+                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, acc)));
+                else p.eout[(size_t)pr * p.D + n] = f2act(p.act_f16, acc);
             }
         }
     }
@@ -564,75 +633,100 @@ __device__ __forceinline__ void combine_item(const LayerParams &p, int item) {
 // ------------------------------------------------------------------ driver
 
 constexpr int MAX_LATENT = 6144;
+constexpr int DW = DENSE_THREADS / 64;    // waves of a dense workgroup
 
 struct Fc2Lds {
-    DenseLds dense;
+    DenseLds<DW> dense;
     uint16_t c[MAX_LATENT];   // the row's combine, when formed inline
 };
 
-union ItemLds {
-    RouteLds route;
-    SchedLds sched;
-    DenseLds dense;
-    Fc2Lds fc2;
+// Launch groups: stages [first, last] of one launch (no item of a group depends on another
+// item of the same group), its workgroup size and its LDS.
+template <int G> struct Group;
+template <> struct Group<0> {
+    static constexpr int first = ST_GATE, last = ST_SHUP, threads = DENSE_THREADS;
+    union Lds { DenseLds<DW> dense; };
+};
+template <> struct Group<1> {
+    static constexpr int first = ST_ROUTE, last = ST_SHDN, threads = DENSE_THREADS;
+    union Lds { RouteLds<DENSE_THREADS> route; DenseLds<DW> dense; };
+};
+template <> struct Group<2> {
+    static constexpr int first = ST_SCHED, last = ST_SCHED, threads = WG_THREADS;
+    union Lds { SchedLds sched; };
+};
+template <> struct Group<3> {
+    static constexpr int first = ST_UP, last = ST_UP, threads = WG_THREADS;
+    union Lds { ExpertLds ex; };
+};
+template <> struct Group<4> {
+    static constexpr int first = ST_DOWN, last = ST_DOWN, threads = WG_THREADS;
+    union Lds { ExpertLds ex; };
+};
+template <> struct Group<5> {
+    static constexpr int first = ST_COMBINE, last = ST_COMBINE, threads = WG_THREADS;
+    union Lds { int unused; };
+};
+template <> struct Group<7> {   // expert up for inputs wider than 2048 (several chunks per lane)
+    static constexpr int first = ST_UP, last = ST_UP, threads = WG_THREADS;
+    union Lds { ExpertLds ex; };
+};
+template <> struct Group<8> {   // expert down for intermediates wider than 2048
+    static constexpr int first = ST_DOWN, last = ST_DOWN, threads = WG_THREADS;
+    union Lds { ExpertLds ex; };
+};
+template <> struct Group<6> {
+    static constexpr int first = ST_FC2, last = ST_FC2, threads = DENSE_THREADS;
+    union Lds { DenseLds<DW> dense; Fc2Lds fc2; };
 };
 
-// Launch groups: stages [first, last] of one launch (no item of a group waits on another).
-template <int G> struct Group;
-template <> struct Group<0> { static constexpr int first = ST_GATE, last = ST_SHUP; };
-template <> struct Group<1> { static constexpr int first = ST_ROUTE, last = ST_SHDN; };
-template <> struct Group<2> { static constexpr int first = ST_SCHED, last = ST_SCHED; };
-template <> struct Group<3> { static constexpr int first = ST_UP, last = ST_UP; };
-template <> struct Group<4> { static constexpr int first = ST_DOWN, last = ST_DOWN; };
-template <> struct Group<5> { static constexpr int first = ST_COMBINE, last = ST_COMBINE; };
-template <> struct Group<6> { static constexpr int first = ST_FC2, last = ST_FC2; };
-
-template <int S>
-__device__ __forceinline__ void run_stage(const LayerParams &p, int local, ItemLds &lds) {
+template <int G, int S, class LdsT>
+__device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds) {
+    constexpr bool wide = G >= 7;
     if constexpr (S == ST_GATE) {
-        gate_item(p, local);
+        gate_item<DW>(p, local);
     } else if constexpr (S == ST_FC1) {
-        dense_item<EPI_FC1>(p, p.fc1, p.x, p.H, local * DENSE_TILE, lds.dense);
+        dense_item<EPI_FC1, DW>(p, p.fc1, p.x, p.H, local * DENSE_TILE, lds.dense);
     } else if constexpr (S == ST_SHUP) {
-        dense_item<EPI_SHUP>(p, p.su, p.x, p.H, local * DENSE_TILE, lds.dense);
+        dense_item<EPI_SHUP, DW>(p, p.su, p.x, p.H, local * DENSE_TILE, lds.dense);
     } else if constexpr (S == ST_ROUTE) {
-        route_item(p, local, lds.route);
+        route_item<DENSE_THREADS>(p, local, lds.route);
     } else if constexpr (S == ST_SHDN) {
-        dense_item<EPI_SHDN>(p, p.sd, p.shact, p.SI, local * DENSE_TILE, lds.dense);
+        dense_item<EPI_SHDN, DW>(p, p.sd, p.shact, p.SI, local * DENSE_TILE, lds.dense);
     } else if constexpr (S == ST_SCHED) {
         sched_item(p, lds.sched);
     } else if constexpr (S == ST_UP) {
         const int slot = local / p.up_blocks, blk = local % p.up_blocks;
-        if (p.D > 2048) expert_item<3, 1, true>(p, slot, blk);
-        else expert_item<1, 2, true>(p, slot, blk);
+        if constexpr (wide) expert_item<3, true>(p, slot, blk, lds.ex);
+        else expert_item<1, true>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_DOWN) {
         const int slot = local / p.dn_blocks, blk = local % p.dn_blocks;
-        if (p.I > 2048) expert_item<3, 1, false>(p, slot, blk);
-        else expert_item<1, 2, false>(p, slot, blk);
+        if constexpr (wide) expert_item<3, false>(p, slot, blk, lds.ex);
+        else expert_item<1, false>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_COMBINE) {
         combine_item(p, local);
     } else if constexpr (S == ST_FC2) {
         if (p.single_row) {
             // one-row pass: form the whole combine in LDS first (the same arithmetic as the
             // combine stage); the first item also stores it for inspection
-            for (int d = threadIdx.x; d < p.L; d += WG_THREADS) {
+            for (int d = threadIdx.x; d < p.L; d += DENSE_THREADS) {
                 const uint16_t c = f2bf(combine_value(p, 0, d));
                 lds.fc2.c[d] = c;
                 if (local == 0) p.comb[d] = c;
             }
             __syncthreads();
-            dense_item<EPI_FC2>(p, p.fc2, lds.fc2.c, p.L, local * DENSE_TILE, lds.fc2.dense);
+            dense_item<EPI_FC2, DW>(p, p.fc2, lds.fc2.c, p.L, local * DENSE_TILE, lds.fc2.dense);
         } else {
-            dense_item<EPI_FC2>(p, p.fc2, p.comb, p.L, local * DENSE_TILE, lds.dense);
+            dense_item<EPI_FC2, DW>(p, p.fc2, p.comb, p.L, local * DENSE_TILE, lds.dense);
         }
     }
 }
 
-template <int G, int S>
-__device__ __forceinline__ void dispatch(const LayerParams &p, int it, ItemLds &lds) {
+template <int G, int S, class LdsT>
+__device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds) {
     if constexpr (S <= Group<G>::last) {
         if (it < p.item_base[S + 1]) {
-            run_stage<S>(p, it - p.item_base[S], lds);
+            run_stage<G, S>(p, it - p.item_base[S], lds);
             return;
         }
         dispatch<G, S + 1>(p, it, lds);
@@ -640,8 +734,9 @@ __device__ __forceinline__ void dispatch(const LayerParams &p, int it, ItemLds &
 }
 
 template <int G>
-__global__ void __launch_bounds__(WG_THREADS) moe_group_kernel(LayerParams p) {
-    __shared__ ItemLds lds;
+__global__ void __launch_bounds__(Group<G>::threads) __attribute__((amdgpu_waves_per_eu(4, 8)))
+moe_group_kernel(LayerParams p) {
+    __shared__ typename Group<G>::Lds lds;
     const int it = p.item_base[Group<G>::first] + (int)blockIdx.x;
     if (it >= p.item_base[Group<G>::last + 1]) return;
     dispatch<G, Group<G>::first>(p, it, lds);
@@ -654,6 +749,8 @@ template __global__ void moe_group_kernel<3>(LayerParams);
 template __global__ void moe_group_kernel<4>(LayerParams);
 template __global__ void moe_group_kernel<5>(LayerParams);
 template __global__ void moe_group_kernel<6>(LayerParams);
+template __global__ void moe_group_kernel<7>(LayerParams);
+template __global__ void moe_group_kernel<8>(LayerParams);
 
 // zero a small device buffer (the error flag) without a memset node in captured graphs
 __global__ void moe_clear_kernel(uint32_t *ctr, int n) {

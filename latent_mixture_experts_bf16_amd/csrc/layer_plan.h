@@ -42,9 +42,11 @@ enum : int {
     SCH_COUNT = SCH_PAIRS + MAX_ROWS * MAX_TOPK,
 };
 
-constexpr int WG_THREADS = 256;   // 4 waves of 64
-constexpr int UP_BLOCK = 64;      // routed up-projection outputs per item
-constexpr int DOWN_BLOCK = 32;    // routed down-projection outputs per item
+constexpr int WG_THREADS = 256;   // 4 waves of 64 (schedule, expert and combine items)
+constexpr int DENSE_THREADS = 512;  // 8 waves (gate, route, dense projections)
+constexpr int EXPERT_LDS_CODES = 16384;   // LDS bytes for one expert item's codes
+constexpr int EXPERT_LDS_SCALES = 1024;   // ... and for its scales (and again its biases)
+constexpr int EXPERT_MAX_BLOCK = 32;      // output rows of one expert item at most
 constexpr int COMBINE_BLOCK = 256;
 constexpr int DENSE_TILE = 16;    // outputs per dense item
 
@@ -82,6 +84,7 @@ struct LayerParams {
     // work-item table: items of stage s are [item_base[s], item_base[s + 1])
     int item_base[NSTAGE + 1];
     int umax;              // slots enumerated by ST_UP / ST_DOWN items
+    int up_nb, dn_nb;      // output rows of one routed up / down item
     int up_blocks, dn_blocks, comb_blocks;
     int single_row;        // rows == 1: route writes the schedule, fc2 items combine inline
 };

@@ -19,7 +19,7 @@
 #include "layer_plan.h"
 
 namespace moe {
-template <int G> __global__ void moe_group_kernel(LayerParams p);
+template <int G> __global__ void moe_group_kernel(LayerParams p);   // G = 0..8
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 }  // namespace moe
 
@@ -79,6 +79,17 @@ static const char *dt_name(int dt) {
     }
 }
 
+// Output rows of one expert item: the largest power of two <= 32 whose codes, scales and
+// biases fit the item's LDS, that divides N, and whose scales fill whole 16-byte units.
+static int expert_block(int N, int Kin) {
+    for (int nb = EXPERT_MAX_BLOCK; nb > 1; nb >>= 1) {
+        if (N % nb == 0 && (size_t)nb * Kin / 2 <= EXPERT_LDS_CODES &&
+            (size_t)nb * (Kin / 64) * 2 <= EXPERT_LDS_SCALES && ((size_t)nb * Kin) % 512 == 0)
+            return nb;
+    }
+    return 1;
+}
+
 static int check_config(const moe_latent_config &c) {
     if (c.hidden <= 0 || c.n_experts <= 0 || c.n_group <= 0 || c.topk_group <= 0 || c.top_k <= 0 ||
         c.expert_inter <= 0 || c.latent < 0 || c.shared_inter < 0)
@@ -109,6 +120,12 @@ static int check_config(const moe_latent_config &c) {
     if (c.expert_inter % 64 || c.expert_inter > 6144 || D > 6144)
         return fail(MOE_ERR_SHAPE, "config: expert dims (in %d, inter %d) must be multiples of 64, <= 6144",
                     D, c.expert_inter);
+    {
+        const int nb_up = expert_block(c.expert_inter, D), nb_dn = expert_block(D, c.expert_inter);
+        if (((size_t)nb_up * D) % 512 || ((size_t)nb_dn * c.expert_inter) % 512)
+            return fail(MOE_ERR_SHAPE, "config: no expert block fits the item LDS for in %d, inter %d", D,
+                        c.expert_inter);
+    }
     if (c.act_dtype != MOE_DT_BF16 && c.act_dtype != MOE_DT_F16)
         return fail(MOE_ERR_DTYPE, "config: act_dtype %s (bf16 or f16)", dt_name(c.act_dtype));
     if (c.act_dtype == MOE_DT_F16 && (c.latent || c.shared_inter))
@@ -352,10 +369,12 @@ static void plan_items(LayerParams &p, int rows) {
     p.single_row = rows == 1;
     const bool inline_combine = p.single_row && p.L > 0;
     p.umax = p.E < rows * p.K ? p.E : rows * p.K;
-    p.up_blocks = (p.I + UP_BLOCK - 1) / UP_BLOCK;
-    p.dn_blocks = (p.D + DOWN_BLOCK - 1) / DOWN_BLOCK;
+    p.up_nb = expert_block(p.I, p.D);
+    p.dn_nb = expert_block(p.D, p.I);
+    p.up_blocks = p.I / p.up_nb;
+    p.dn_blocks = p.D / p.dn_nb;
     p.comb_blocks = (p.D + COMBINE_BLOCK - 1) / COMBINE_BLOCK;
-    n[ST_GATE] = (p.E + 3) / 4;
+    n[ST_GATE] = (p.E + DENSE_THREADS / 64 - 1) / (DENSE_THREADS / 64);
     n[ST_FC1] = p.L ? p.L / DENSE_TILE : 0;
     n[ST_SHUP] = p.SI / DENSE_TILE;
     n[ST_ROUTE] = rows;
@@ -369,10 +388,14 @@ static void plan_items(LayerParams &p, int rows) {
     for (int s = 0; s < NSTAGE; ++s) p.item_base[s + 1] = p.item_base[s] + n[s];
 }
 
+// workgroup size of each launch group (must match the kernels' Group<G>::threads)
+static const int kGroupThreads[9] = {DENSE_THREADS, DENSE_THREADS, WG_THREADS, WG_THREADS, WG_THREADS,
+                                     WG_THREADS, DENSE_THREADS, WG_THREADS, WG_THREADS};
+
 template <int G>
 static void launch_group(const LayerParams &p, int first, int last, hipStream_t st) {
     const int items = p.item_base[last + 1] - p.item_base[first];
-    if (items > 0) hipLaunchKernelGGL(moe_group_kernel<G>, dim3(items), dim3(WG_THREADS), 0, st, p);
+    if (items > 0) hipLaunchKernelGGL(moe_group_kernel<G>, dim3(items), dim3(kGroupThreads[G]), 0, st, p);
 }
 
 extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
@@ -392,8 +415,10 @@ extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hid
     launch_group<0>(p, ST_GATE, ST_SHUP, st);
     launch_group<1>(p, ST_ROUTE, ST_SHDN, st);
     launch_group<2>(p, ST_SCHED, ST_SCHED, st);
-    launch_group<3>(p, ST_UP, ST_UP, st);
-    launch_group<4>(p, ST_DOWN, ST_DOWN, st);
+    if (p.D > 2048) launch_group<7>(p, ST_UP, ST_UP, st);
+    else launch_group<3>(p, ST_UP, ST_UP, st);
+    if (p.I > 2048) launch_group<8>(p, ST_DOWN, ST_DOWN, st);
+    else launch_group<4>(p, ST_DOWN, ST_DOWN, st);
     launch_group<5>(p, ST_COMBINE, ST_COMBINE, st);
     launch_group<6>(p, ST_FC2, ST_FC2, st);
     hipError_t e = hipGetLastError();
@@ -418,8 +443,14 @@ extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void
     case 0: launch_group<0>(p, ST_GATE, ST_SHUP, st); break;
     case 1: launch_group<1>(p, ST_ROUTE, ST_SHDN, st); break;
     case 2: launch_group<2>(p, ST_SCHED, ST_SCHED, st); break;
-    case 3: launch_group<3>(p, ST_UP, ST_UP, st); break;
-    case 4: launch_group<4>(p, ST_DOWN, ST_DOWN, st); break;
+    case 3:
+        if (p.D > 2048) launch_group<7>(p, ST_UP, ST_UP, st);
+        else launch_group<3>(p, ST_UP, ST_UP, st);
+        break;
+    case 4:
+        if (p.I > 2048) launch_group<8>(p, ST_DOWN, ST_DOWN, st);
+        else launch_group<4>(p, ST_DOWN, ST_DOWN, st);
+        break;
     case 5: launch_group<5>(p, ST_COMBINE, ST_COMBINE, st); break;
     default: launch_group<6>(p, ST_FC2, ST_FC2, st); break;
     }
