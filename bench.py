@@ -23,8 +23,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-GROUP_NAMES = {0: "gate+fc1+shared_up", 1: "route+shared_down", 2: "schedule", 3: "expert_up",
-               4: "expert_down", 5: "combine", 6: "fc2+shared+residual"}
+# launches of one forward (the library's launch groups) and the stages each one runs
+LAUNCHES_ONE_ROW = [("gate+fc1+shared_up+route", ["gate", "fc1", "shup", "route"]),
+                    ("shared_down_a+expert_up", ["shdn_a", "up"]),
+                    ("shared_down_b+expert_down+combine", ["shdn_b", "down"]),
+                    ("fc2+shared+residual", ["fc2"])]
+LAUNCHES_MULTI_ROW = [("gate+fc1+shared_up", ["gate", "fc1", "shup"]),
+                      ("route+schedule+shared_down_a", ["route", "shdn_a"]),
+                      ("expert_up+shared_down_b", ["up", "shdn_b"]),
+                      ("expert_down+combine", ["down"]),
+                      ("fc2+shared+residual", ["fc2"])]
 
 
 def parse():
@@ -39,25 +47,26 @@ def parse():
     return ap.parse_args()
 
 
-def group_bytes(dims, rows, n_distinct):
-    """Algorithmic bytes each launch group must move for one pass: every weight byte read
-    once (routed experts: only the distinct experts the pass picked), activations in and out."""
+def stage_bytes(dims, rows, n_distinct):
+    """Algorithmic bytes of each stage of one pass: every weight byte read once (routed
+    experts: only the distinct experts the pass picked), activations in and out."""
     H, L, E, I, SI, K = dims.hidden, dims.latent, dims.n_experts, dims.expert_inter, dims.shared_inter, dims.top_k
     D = L or H
     a = 2  # activation bytes
-    gate_w = E * H * (4 if dims.router_dtype == 3 else 2)
     expert = D * I // 2 + (D * I // 64) * 4            # codes + bf16 scale and bias per 64
-    g = {}
-    g[0] = gate_w + L * H * 2 + SI * H * 2 + rows * H * a + rows * E * 2 + rows * L * a + rows * SI * a
-    g[1] = (E * 4 if dims.has_bias else 0) + rows * E * 2 + rows * K * 8 + H * SI * 2 + rows * SI * a + rows * H * a
-    g[2] = rows * K * 8
-    g[3] = n_distinct * expert + rows * D * a + rows * K * I * a
-    g[4] = n_distinct * expert + rows * K * I * a + rows * K * D * a
-    g[5] = (rows * K * D * a + rows * K * 4 + rows * D * a) if (rows > 1 or not L) else 0
-    if not L:
-        g[5] += 2 * rows * H * a
-    g[6] = (H * L * 2 + rows * (D if rows > 1 else K * D) * a + 3 * rows * H * a) if L else 0
-    return g
+    half = (H // 16 // 2) * 16
+    return {
+        "gate": E * H * (4 if dims.router_dtype == 3 else 2) + rows * H * a + rows * E * 2,
+        "fc1": L * H * 2 + rows * L * a,
+        "shup": SI * H * 2 + rows * SI * a,
+        "route": (E * 4 if dims.has_bias else 0) + rows * E * 2 + rows * K * 8,
+        "shdn_a": half * SI * 2 + rows * SI * a + rows * half * a if SI else 0,
+        "up": n_distinct * expert + rows * D * a + rows * K * I * a,
+        "shdn_b": (H - half) * SI * 2 + rows * SI * a + rows * (H - half) * a if SI else 0,
+        "down": n_distinct * expert + rows * K * I * a + rows * K * D * a + rows * K * 4 + rows * D * a
+                + (2 * rows * H * a if not L else 0),
+        "fc2": (H * L * 2 + rows * D * a + 3 * rows * H * a) if L else 0,
+    }
 
 
 def main():
@@ -111,8 +120,9 @@ def main():
     for lay in layers:
         idx, _ = lay.routing(rows)
         distinct.append(len(np.unique(idx)))
-    gb = [group_bytes(dims, rows, u) for u in distinct]
-    step_bytes = float(np.mean([sum(g.values()) for g in gb]))
+    sb = [stage_bytes(dims, rows, u) for u in distinct]
+    step_bytes = float(np.mean([sum(g.values()) for g in sb]))
+    launches = LAUNCHES_ONE_ROW if rows == 1 else LAUNCHES_MULTI_ROW
 
     # graphs: one sweep over all instances, and one graph per instance for a remainder
     def capture(fn):
@@ -151,7 +161,7 @@ def main():
     # each launch group on its own: replay graphs of that group over all instances
     group_stats = {}
     reps = max(20, args.steps // (4 * inst))
-    for gid in range(7):
+    for gid, (gname, stages) in enumerate(launches):
         if B.moe_latent_group_items(layers[0].handle, rows, gid) <= 0:
             continue
         with torch.cuda.stream(s):
@@ -166,8 +176,8 @@ def main():
             b.record(s)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (reps * inst)
-        gbytes = float(np.mean([g[gid] for g in gb]))
-        group_stats[gid] = {"name": GROUP_NAMES[gid], "us": round(us, 3), "bytes": int(gbytes),
+        gbytes = float(np.mean([sum(g[st] for st in stages) for g in sb]))
+        group_stats[gid] = {"name": gname, "us": round(us, 3), "bytes": int(gbytes),
                             "gbps": round(gbytes / (us * 1e-6) / 1e9, 1)}
         del gg
     for lay in layers:
@@ -220,11 +230,12 @@ def main():
                    "shared_inter": dims.shared_inter, "weight_instances": inst},
         "layer_hbm": {"bytes_per_step": int(step_bytes), "achieved_gbps": round(layer_gbps, 1),
                       "frac": round(layer_gbps / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": f"moe_group_kernel<{dom}> ({d['name']})",
+        "roofline": {"bound": "hbm", "kernel": f"launch {dom}: moe_stage_kernel ({d['name']})",
                      "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]},
-        "groups": {GROUP_NAMES[k]: v for k, v in group_stats.items()},
+        "launches": {v["name"]: {"us": v["us"], "bytes": v["bytes"], "gbps": v["gbps"]}
+                     for v in group_stats.values()},
         "cpu_baseline": cpu,
         "parity": parity,
     }

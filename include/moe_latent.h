@@ -128,7 +128,7 @@ int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
  * layer order; «Per operator and row invariance»: each row of a multi-row pass equals its
  * own one-row pass). hidden_in: [rows][H] activations (act_dtype); out: [rows][H] (same
  * dtype). out == hidden_in (in place) is allowed; any other overlap is refused. Enqueued on
- * the handle's stream as up to seven launches (no host synchronisation, no allocation, no
+ * the handle's stream as four or five launches (no host synchronisation, no allocation, no
  * memset: it can be captured in a HIP graph); returns launch errors only -- device-side
  * faults surface at the caller's next synchronisation / moe_latent_status(). The handle is
  * not reentrant: forwards on one handle must not overlap in time on different streams. */
@@ -137,12 +137,16 @@ int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, voi
 /* Release the workspace and the handle (NULL-safe). Synchronises the handle's stream. */
 void moe_latent_destroy(moe_latent_t *h);
 
-/* Launch groups of a forward, in order (stages that share a launch do not depend on each
- * other): 0 gate + fc1 + shared up; 1 route + shared down; 2 schedule (multi-row passes);
- * 3 routed expert up; 4 routed expert down; 5 combine (multi-row or non-latent passes);
- * 6 fc2 + shared + residual (forms the combine itself in a one-row pass). */
+/* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (the last
+ * gate workgroup routes the row); 1 shared down (first half) + routed expert up; 2 shared
+ * down (second half) + routed expert down (the last workgroup of each output block combines
+ * it); 3 fc2 + shared + residual. Multi-row pass: 0 as above without the route; 1 route (the
+ * last route workgroup builds the expert schedule) + shared down (first half); 2 routed
+ * expert up + shared down (second half); 3 routed expert down + combine; 4 fc2 + shared +
+ * residual. A non-latent layer has no fc1 / fc2 / shared launches: its combine adds the
+ * residual. */
 
-/* Enqueue only launch group `group` (0..6) of a forward of `rows` rows, for timing one
+/* Enqueue only launch group `group` of a forward of `rows` rows, for timing one
  * kernel on its own. Its inputs are what the earlier groups of the same forward wrote, so
  * call it after a full moe_latent_forward with the same rows, hidden_in and out; it then
  * rewrites the same values. A group with no work for this pass enqueues nothing. */
@@ -157,9 +161,9 @@ int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
 int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
 
 /* Execution variant. 1 (the default and the only one available): the forward is a chain of
- * launches on the handle's stream, stages that do not depend on each other sharing one.
- * 0 (one fused launch per forward, a dependency-ordered work queue) is reserved and refused
- * with MOE_ERR_INVALID_ARG: that variant is disabled until a failure of it is understood. */
+ * launches on the handle's stream (see the launch groups above). 0 (one fused launch per
+ * forward, a dependency-ordered work queue) is reserved and refused with
+ * MOE_ERR_INVALID_ARG: that variant is disabled until a failure of it is understood. */
 int moe_latent_set_variant(moe_latent_t *h, int32_t variant);
 
 /* Copy the last forward's routing to device buffers, enqueued on the handle's stream:

@@ -4,11 +4,19 @@ Argument marshalling only: every step of the layer runs in the HIP kernels of th
 library. The functions carry the C names. Device buffers are passed as integer device
 addresses (e.g. a torch tensor's data_ptr()); streams as integer hipStream_t handles.
 If the library has not been built this module raises at import -- there is no fallback.
+
+torch (when installed) is imported before the library is loaded, so that the library binds
+to the HIP runtime torch brings: a process must drive the GPU through one HIP runtime.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+
+try:  # load torch's HIP runtime first (see above)
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover
+    pass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_latent.so")

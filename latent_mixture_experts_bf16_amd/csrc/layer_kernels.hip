@@ -1,11 +1,14 @@
 // layer_kernels.hip -- HIP kernels of one latent mixture-of-experts decode layer (gfx950).
 //
 // A forward is a table of work items (tiles of each stage, see layer_plan.h) run as a short
-// chain of launches on one stream. Stages that do not depend on each other share a launch:
-//   [gate, fc1, shared up] -> [route, shared down] -> [schedule] -> [expert up] ->
-//   [expert down] -> [combine] -> [fc2 + shared + residual]
-// (for a one-row pass the route writes the schedule and each fc2 item forms the combine
-// itself, so that pass is five launches). One workgroup of 4 waves runs one item.
+// chain of launches on one stream; stages that do not depend on each other share a launch,
+// and steps that need every item of a stage (route after the gate, schedule after the
+// route, combine after the experts of a block) are run by the last item to finish:
+//   one row:   [gate, fc1, shared up; route] -> [shared down A, expert up] ->
+//              [shared down B, expert down; combine] -> [fc2 + shared + residual]
+//   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
+//              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]
+// One workgroup of 8 waves runs one item.
 //
 // Arithmetic of each stage (TensorFold pull request 1038, «What's in it»: gate gemv ->
 // route top-k -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj -> +
@@ -90,6 +93,57 @@ __device__ __forceinline__ void nibbles8(uint32_t w, float *q) {
     q[7] = (float)(hi >> 24);
 }
 
+// ------------------------------------------------------------------ cross-workgroup data
+
+// Data a "last arriver" reads from other workgroups of the same launch is written through to
+// memory and read around the caches (agent-scope relaxed atomic stores and loads); the
+// counter is only bumped once those stores have completed. No L2 write-back or invalidate.
+__device__ __forceinline__ void st_shared16(uint16_t *p, uint16_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint16_t ld_shared16(const uint16_t *p) {
+    return __hip_atomic_load(const_cast<uint16_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_shared32(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_shared32(const int32_t *p) {
+    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sharedf(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_sharedf(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's vector memory operations (the stores above) have completed
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));   // vmcnt(0) only
+}
+
+// Count this item done on *c once its write-through stores have completed. Returns true, in
+// every thread of the item, for the item that brings the count to `target`: that item then
+// reads the other items' data with read-around loads, and resets the counter for the next
+// forward. Nothing waits: the other items just finish.
+__device__ __forceinline__ bool last_arriver(uint32_t *c, uint32_t target, int *s_flag) {
+    wait_vmem();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old + 1 == target;
+        if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    if (last) {
+        wait_vmem();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    return last;
+}
+
 // ------------------------------------------------------------------ gate
 
 // Item: NW experts (one per wave), all rows. Fixed summation order described above. The
@@ -126,7 +180,7 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item) {
             }
 #pragma unroll
             for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-            if (lane == 0) ((uint16_t *)p.logits)[(size_t)r * p.E + e] = f2bf(acc);
+            if (lane == 0) st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
         }
         return;
     }
@@ -169,8 +223,8 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item) {
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
         if (lane == 0) {
-            if (p.router_f32) ((float *)p.logits)[(size_t)r * p.E + e] = acc;
-            else ((uint16_t *)p.logits)[(size_t)r * p.E + e] = f2bf(acc);
+            if (p.router_f32) st_shared32((int32_t *)p.logits + (size_t)r * p.E + e, __float_as_int(acc));
+            else st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
         }
     }
 }
@@ -188,114 +242,141 @@ __device__ __forceinline__ uint64_t rank_key(float v, int id) {
     return ((uint64_t)o << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+
+// Number of keys in v[0..n) larger than k (v in LDS, 16-byte aligned). Batches of 16
+// independent broadcast reads keep the LDS pipeline full.
+__device__ __forceinline__ int count_greater(const uint64_t *v, int n, uint64_t k) {
+    int c = 0, f = 0;
+    for (; f + 16 <= n; f += 16) {
+        uint64_t t[16];
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, d, 64);
-        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
+        for (int q = 0; q < 16; ++q) t[q] = v[f + q];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) c += t[q] > k;
     }
-    return v;
+    for (; f < n; ++f) c += v[f] > k;
+    return c;
+}
+
+// The same for any alignment of v.
+__device__ __forceinline__ int count_greater_any(const uint64_t *v, int n, uint64_t k) {
+    int c = 0, f = 0;
+    for (; f + 8 <= n; f += 8) {
+        uint64_t t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t[q] = v[f + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c += t[q] > k;
+    }
+    for (; f < n; ++f) c += v[f] > k;
+    return c;
 }
 
 template <int NT>
 struct RouteLds {
     float s[MAX_EXPERTS];
     float b[MAX_EXPERTS];
-    float gam[256];
+    alignas(16) uint64_t key[MAX_EXPERTS];    // rank keys of the biased scores; 0 once excluded
+    alignas(16) uint64_t gkey[256];           // rank keys of the group scores
+    int top[256][2];              // the two best members of each group
     int keep[256];
-    uint64_t best[NT / 64];
     int picks[MAX_TOPK];
 };
 
 // Item: one row (TensorFold pull request 1038, «Per operator and row invariance»:
 // group_expert_select at k = 9; pull request 1295, «What this changes»: sigmoid top-8 with
-// per-expert norm and sum).
+// per-expert norm and sum). Every selection is by rank: an element's rank is the number of
+// elements whose 64-bit key is larger, counted by the element's own thread from LDS (keys
+// are unique, so ranks are a permutation and no thread waits on another's choice).
 template <int NT>
 __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds<NT> &L) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int E = p.E, G = p.G, per = p.E / p.G;
     for (int e = tid; e < E; e += NT) {
-        const float z = p.router_f32 ? ((const float *)p.logits)[(size_t)r * E + e]
-                                     : bf2f(((const uint16_t *)p.logits)[(size_t)r * E + e]);
+        // both loads are issued before either value is used
+        const float bias = p.has_bias ? p.bias[e] : 0.0f;
+        const uint32_t raw = p.router_f32 ? (uint32_t)ld_shared32((const int32_t *)p.logits + (size_t)r * E + e)
+                                          : (uint32_t)ld_shared16((const uint16_t *)p.logits + (size_t)r * E + e);
+        const float z = p.router_f32 ? __uint_as_float(raw) : __uint_as_float(raw << 16);
         const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
+        const float b = p.has_bias ? s + bias : s;
         L.s[e] = s;
-        L.b[e] = p.has_bias ? s + p.bias[e] : s;
+        L.b[e] = b;
+        L.key[e] = rank_key(b, e);
     }
+    if (tid < MAX_TOPK) L.picks[tid] = -1;
     __syncthreads();
-    // group scores: one thread per group, two best members by rank
-    for (int g = tid; g < G; g += NT) {
-        uint64_t k1 = 0, k2 = 0;
-        int i1 = -1, i2 = -1;
-        for (int e = g * per; e < (g + 1) * per; ++e) {
-            const uint64_t k = rank_key(L.b[e], e);
-            if (i1 < 0 || k > k1) { k2 = k1; i2 = i1; k1 = k; i1 = e; }
-            else if (i2 < 0 || k > k2) { k2 = k; i2 = e; }
+    if (p.TG < G) {
+        // the two best members of each group: rank of each expert inside its group
+        for (int e = tid; e < E; e += NT) {
+            const uint64_t k = L.key[e];
+            const int g = e / per;
+            const int rank = count_greater_any(L.key + g * per, per, k);
+            if (rank < 2) L.top[g][rank] = e;
         }
-        L.gam[g] = (i2 >= 0) ? L.b[i1] + L.b[i2] : L.b[i1];
-    }
-    __syncthreads();
-    // kept groups: rank among groups < topk_group
-    for (int g = tid; g < G; g += NT) {
-        const uint64_t kg = rank_key(L.gam[g], g);
-        int rank = 0;
-        for (int h = 0; h < G; ++h) rank += rank_key(L.gam[h], h) > kg;
-        L.keep[g] = rank < p.TG;
-    }
-    __syncthreads();
-    // top-k among candidates: k rounds of a workgroup-wide max of 64-bit keys
-    uint64_t mine[MAX_EXPERTS / NT];
-#pragma unroll
-    for (int m = 0; m < MAX_EXPERTS / NT; ++m) {
-        const int e = tid + m * NT;
-        mine[m] = (e < E && L.keep[e / per]) ? rank_key(L.b[e], e) : 0ull;
-    }
-    for (int j = 0; j < p.K; ++j) {
-        uint64_t v = 0;
-#pragma unroll
-        for (int m = 0; m < MAX_EXPERTS / NT; ++m) v = mine[m] > v ? mine[m] : v;
-        v = wave_max_u64(v);
-        if (lane == 0) L.best[wave] = v;
         __syncthreads();
-        uint64_t w = L.best[0];
-#pragma unroll
-        for (int q = 1; q < NT / 64; ++q) w = L.best[q] > w ? L.best[q] : w;
-        int e = (int)(0xFFFFFFFFu - (uint32_t)w);
-#pragma unroll
-        for (int m = 0; m < MAX_EXPERTS / NT; ++m)
-            if (mine[m] == w) mine[m] = 0ull;
-        if (w == 0ull || e < 0 || e >= E) {   // no candidate left: excluded by the host checks
-            e = 0;
-            if (tid == 0) atomicOr(p.err, 2u);
+        for (int g = tid; g < G; g += NT) {
+            const float gam = per > 1 ? L.b[L.top[g][0]] + L.b[L.top[g][1]] : L.b[L.top[g][0]];
+            L.gkey[g] = rank_key(gam, g);
         }
-        if (tid == 0) L.picks[j] = e;
+        __syncthreads();
+        for (int g = tid; g < G; g += NT) {
+            const uint64_t kg = L.gkey[g];
+            L.keep[g] = count_greater(L.gkey, G, kg) < p.TG;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += NT)
+            if (!L.keep[e / per]) L.key[e] = 0ull;
         __syncthreads();
     }
-    if (tid == 0) {
-        float S = L.s[L.picks[0]];
-        for (int j = 1; j < p.K; ++j) S = S + L.s[L.picks[j]];
-        for (int j = 0; j < p.K; ++j) {
-            const float sj = L.s[L.picks[j]];
-            const float v = p.norm_topk ? sj / S : sj;
-            p.idx[(size_t)r * p.K + j] = L.picks[j];
-            p.wts[(size_t)r * p.K + j] = v * p.rho;
+    // the top_k candidates: rank among the remaining keys
+    for (int e = tid; e < E; e += NT) {
+        const uint64_t k = L.key[e];
+        if (k == 0ull) continue;
+        const int rank = count_greater(L.key, E, k);
+        if (rank < p.K) L.picks[rank] = e;
+    }
+    __syncthreads();
+    // thread j < K finishes pick j: every such thread reads all picks (a missing one, which
+    // the host checks exclude, counts as expert 0), sums the picked scores in pick order and
+    // writes its index and weight; a one-row pass also gets its schedule here, slot u holding
+    // the u-th smallest picked expert
+    if (tid < p.K) {
+        const int j = tid;
+        int pk[MAX_TOPK];
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < MAX_TOPK; ++i) {
+            pk[i] = i < p.K ? L.picks[i] : 0;
+            if (pk[i] < 0 || pk[i] >= E) { pk[i] = 0; missing = true; }
         }
+        if (missing && j == 0) atomicOr(p.err, 2u);
+        float sv[MAX_TOPK];
+#pragma unroll
+        for (int i = 0; i < MAX_TOPK; ++i) sv[i] = i < p.K ? L.s[pk[i]] : 0.0f;
+        float S = sv[0];
+#pragma unroll
+        for (int i = 1; i < MAX_TOPK; ++i)
+            if (i < p.K) S = S + sv[i];
+        float sj = sv[0];
+        int ej = pk[0], u = 0;
+#pragma unroll
+        for (int i = 0; i < MAX_TOPK; ++i) if (i == j) { sj = sv[i]; ej = pk[i]; }
+#pragma unroll
+        for (int i = 0; i < MAX_TOPK; ++i)
+            if (i < p.K) u += pk[i] < ej || (pk[i] == ej && i < j);
+        const float v = p.norm_topk ? sj / S : sj;
+        st_shared32(p.idx + (size_t)r * p.K + j, ej);
+        p.wts[(size_t)r * p.K + j] = v * p.rho;
         if (p.single_row) {
-            // schedule of a one-row pass: one slot per pick, slots in increasing expert id
-            int order[MAX_TOPK];
-            for (int j = 0; j < p.K; ++j) {
-                int a = j;
-                while (a > 0 && L.picks[order[a - 1]] > L.picks[j]) { order[a] = order[a - 1]; --a; }
-                order[a] = j;
+            p.sched[SCH_EXPERT + u] = ej;
+            p.sched[SCH_OFF + u] = u;
+            p.sched[SCH_FIRST + u] = j;
+            p.sched[SCH_PAIRS + u] = j;
+            if (j == 0) {
+                p.sched[SCH_OFF + p.K] = p.K;
+                p.sched[SCH_U] = p.K;
             }
-            for (int u = 0; u < p.K; ++u) {
-                p.sched[SCH_EXPERT + u] = L.picks[order[u]];
-                p.sched[SCH_OFF + u] = u;
-                p.sched[SCH_PAIRS + u] = order[u];
-            }
-            p.sched[SCH_OFF + p.K] = p.K;
-            p.sched[SCH_U] = p.K;
         }
     }
 }
@@ -303,6 +384,7 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
 // ------------------------------------------------------------------ schedule
 
 struct SchedLds {
+    int slot[MAX_EXPERTS];   // slot of each picked expert
     int cnt[MAX_EXPERTS];
     int off[MAX_EXPERTS + 1];
     int cur[MAX_EXPERTS];
@@ -316,7 +398,7 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
     const int tid = threadIdx.x, E = p.E, NP = p.rows * p.K;
     for (int e = tid; e < E; e += WG_THREADS) { L.cnt[e] = 0; L.cur[e] = 0; }
     __syncthreads();
-    for (int i = tid; i < NP; i += WG_THREADS) atomicAdd(&L.cnt[p.idx[i]], 1);
+    for (int i = tid; i < NP; i += WG_THREADS) atomicAdd(&L.cnt[ld_shared32(p.idx + i)], 1);
     __syncthreads();
     // exclusive scans of cnt (pair offsets) and of (cnt > 0) (slot ids), 4 experts per thread
     const int per_t = (E + WG_THREADS - 1) / WG_THREADS;
@@ -342,6 +424,7 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             if (L.cnt[e] > 0) {
                 p.sched[SCH_EXPERT + run_slots] = e;
                 p.sched[SCH_OFF + run_slots] = run_pairs;
+                L.slot[e] = run_slots;
                 ++run_slots;
             }
             run_pairs += L.cnt[e];
@@ -353,7 +436,7 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
     }
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) {
-        const int e = p.idx[i];
+        const int e = ld_shared32(p.idx + i);
         L.pairs[L.off[e] + atomicAdd(&L.cur[e], 1)] = i;
     }
     __syncthreads();
@@ -366,9 +449,38 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             while (b >= 0 && L.pairs[o + b] > v) { L.pairs[o + b + 1] = L.pairs[o + b]; --b; }
             L.pairs[o + b + 1] = v;
         }
+        if (n > 0) p.sched[SCH_FIRST + L.slot[e]] = L.pairs[o];
     }
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) p.sched[SCH_PAIRS + i] = L.pairs[i];
+}
+
+// ------------------------------------------------------------------ combine
+
+// The combine of row r at latent output d, before rounding (lane order described at the top).
+// COH: the expert outputs were written by the same launch (read around the non-coherent
+// caches); otherwise by an earlier one (plain loads).
+template <bool COH>
+__device__ __forceinline__ float combine_value(const LayerParams &p, int r, int d) {
+    // all MAX_TOPK loads are issued unconditionally (picks past K re-read pick K - 1) so that
+    // none waits for another; the picks past K are then left out of the sum
+    float w[MAX_TOPK];
+    uint16_t v[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        const size_t pr = (size_t)r * p.K + (j < p.K ? j : p.K - 1);
+        w[j] = p.wts[pr];
+        v[j] = COH ? ld_shared16(p.eout + pr * p.D + d) : p.eout[pr * p.D + d];
+    }
+    float T[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) T[t] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        const float t = T[j & 7] + w[j] * act2f(p.act_f16, v[j]);
+        T[j & 7] = j < p.K ? t : T[j & 7];
+    }
+    return ((T[0] + T[4]) + (T[2] + T[6])) + ((T[1] + T[5]) + (T[3] + T[7]));
 }
 
 // ------------------------------------------------------------------ dense bf16 tiles (MFMA)
@@ -378,39 +490,110 @@ enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
 template <int NW>
 struct DenseLds {
     f32x4 part[NW][2][64];   // [wave][row tile][lane]
+    uint16_t xc[4096];       // fc2 of a one-row pass: the item's slice of the combine
 };
 
-// Item: outputs n0..n0+15 of W [N][K] (bf16, row-major) against X [rows][K] (bf16), all rows.
-// K is split over up to NW waves in contiguous slices (each a multiple of 128); per 128
-// inputs each lane holds 32 consecutive k of one weight row (64 B) and of one input row,
-// fed to 4 MFMAs of 32. A wave first issues the loads of up to 4 such steps of its weight
-// slice, then multiplies. The slices' partial sums are joined in wave order.
+// Inputs of the fc2 epilogue (shared expert output and residual) of 4 outputs.
+struct EpiIn {
+    float sh[4], xv[4];
+};
+
+__device__ __forceinline__ EpiIn epi_load(const LayerParams &p, int row, int n) {
+    // two 8-byte loads (n is a multiple of 4); the shared output buffer exists even when the
+    // layer has no shared expert
+    const uint2 sh = *(const uint2 *)(p.shout + (size_t)row * p.H + n);
+    const uint2 xv = *(const uint2 *)(p.x + (size_t)row * p.H + n);
+    const uint32_t shw[2] = {sh.x, sh.y}, xw[2] = {xv.x, xv.y};
+    EpiIn v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float s16 = __uint_as_float((i & 1 ? shw[i >> 1] >> 16 : shw[i >> 1] & 0xFFFFu) << 16);
+        v.sh[i] = p.SI ? s16 : 0.0f;
+        v.xv[i] = __uint_as_float((i & 1 ? xw[i >> 1] >> 16 : xw[i >> 1] & 0xFFFFu) << 16);
+    }
+    return v;
+}
+
+__device__ __forceinline__ void fc2_out(const LayerParams &p, int row, int n, float a, float sh, float xv) {
+    const float m = rnd(0, a);
+    p.out[(size_t)row * p.H + n] = f2bf(xv + rnd(0, m + sh));
+}
+
+__device__ __forceinline__ void dense_epilogue(const LayerParams &p, int epi, int row, int n, float a) {
+    if (epi == EPI_FC1) {
+        p.u[(size_t)row * p.L + n] = f2bf(a);
+    } else if (epi == EPI_SHUP) {
+        p.shact[(size_t)row * p.SI + n] = f2bf(relu_sq(0, rnd(0, a)));
+    } else if (epi == EPI_SHDN) {
+        p.shout[(size_t)row * p.H + n] = f2bf(a);
+    } else {
+        // both loads unconditional (the shared output buffer always exists), so they overlap
+        const float sh = bf2f(p.shout[(size_t)row * p.H + n]);
+        const float xv = bf2f(p.x[(size_t)row * p.H + n]);
+        fc2_out(p, row, n, a, p.SI ? sh : 0.0f, xv);
+    }
+}
+
+// Item: part `split` (of `ks`) of K for outputs n0..n0+15 of W [N][K] (bf16, row-major)
+// against X [rows][K] (bf16), all rows. Inside the item K is split again over up to NW waves
+// in contiguous slices (each a multiple of 128); per 128 inputs each lane holds 32
+// consecutive k of one weight row (64 B) and of one input row, fed to 4 MFMAs of 32. A wave
+// issues the loads of up to 4 such steps of its weight slice, then multiplies. The waves'
+// partial sums are joined in wave order; with ks > 1 the item's partial goes to the
+// workspace and the last of the ks items to finish adds them in split order and applies the
+// epilogue. For the fc2 of a one-row pass (p.inline_comb) the item first computes its slice
+// of the combine into LDS, while its first weights are in flight.
 template <int EPI, int NW>
 __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t *__restrict__ W,
-                                           const uint16_t *__restrict__ X, int K, int n0, DenseLds<NW> &L) {
+                                           const uint16_t *__restrict__ X, int K, int tile, int split, int ks,
+                                           float *part, uint32_t *ctr, DenseLds<NW> &L, int *s_flag) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nr = lane & 15, grp = lane >> 4;
+    const int n0 = tile * DENSE_TILE;
+    const int kpart = K / ks, kbase = split * kpart;
     int nsplit = NW;
-    while (nsplit > 1 && K % (128 * nsplit)) nsplit >>= 1;
-    const int kw = K / nsplit, nit = kw / 128;
+    while (nsplit > 1 && kpart % (128 * nsplit)) nsplit >>= 1;
+    const int kw = kpart / nsplit, nit = kw / 128;
     const int nrt = (p.rows + 15) >> 4;
+    float *mypart = part + ((size_t)(tile * ks + split) * p.rows) * DENSE_TILE;
     constexpr int RT = 2;   // row tiles (16 rows each) per pass over the weights
+    const bool inl = EPI == EPI_FC2 && p.inline_comb;
+    const uint16_t *wrow = W + (size_t)(n0 + nr) * K + kbase + wave * kw + 32 * grp;
+    const size_t xoff = (size_t)kbase + wave * kw + 32 * grp;
+
+    uint4 a[4][4];
+    auto load_w = [&](int i0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (i0 + q < nit) {
+                const uint4 *wp = (const uint4 *)(wrow + 128 * (i0 + q));
+                a[q][0] = wp[0]; a[q][1] = wp[1]; a[q][2] = wp[2]; a[q][3] = wp[3];
+            }
+        }
+    };
+    if (wave < nsplit) load_w(0);
+    // the fc2 epilogue's inputs, when one pass finishes every row here
+    const bool epi_pre = EPI == EPI_FC2 && ks == 1 && nrt <= RT;
+    EpiIn pre = {};
+    if (epi_pre && wave < nrt) {
+        const int row = wave * 16 + nr;
+        if (row < p.rows) pre = epi_load(p, row, n0 + 4 * grp);
+    }
+    if (inl) {
+        for (int i = threadIdx.x; i < kpart; i += NW * 64) {
+            const uint16_t c = f2bf(combine_value<false>(p, 0, kbase + i));
+            L.xc[i] = c;
+            if (tile == 0) p.comb[kbase + i] = c;
+        }
+        __syncthreads();
+    }
     for (int rt0 = 0; rt0 < nrt; rt0 += RT) {
         f32x4 acc[RT];
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (wave < nsplit) {
-            const uint16_t *wrow = W + (size_t)(n0 + nr) * K + wave * kw + 32 * grp;
-            const size_t xoff = (size_t)wave * kw + 32 * grp;
             for (int i0 = 0; i0 < nit; i0 += 4) {
-                uint4 a[4][4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (i0 + q < nit) {
-                        const uint4 *wp = (const uint4 *)(wrow + 128 * (i0 + q));
-                        a[q][0] = wp[0]; a[q][1] = wp[1]; a[q][2] = wp[2]; a[q][3] = wp[3];
-                    }
-                }
+                if (rt0 > 0 || i0 > 0) load_w(i0);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (i0 + q < nit) {
@@ -421,7 +604,8 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
                             if (rt0 + t < nrt) {
                                 uint4 b0 = {0, 0, 0, 0}, b1 = b0, b2 = b0, b3 = b0;
                                 if (row < p.rows) {
-                                    const uint4 *xp = (const uint4 *)(X + (size_t)row * K + xoff + kb);
+                                    const uint4 *xp = inl ? (const uint4 *)(L.xc + wave * kw + 32 * grp + kb)
+                                                          : (const uint4 *)(X + (size_t)row * K + xoff + kb);
                                     b0 = xp[0]; b1 = xp[1]; b2 = xp[2]; b3 = xp[3];
                                 }
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -450,24 +634,22 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
             if (row < p.rows) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = n0 + 4 * grp + i;
-                    const float a = v[i];
-                    if (EPI == EPI_FC1) {
-                        p.u[(size_t)row * p.L + n] = f2bf(a);
-                    } else if (EPI == EPI_SHUP) {
-                        p.shact[(size_t)row * p.SI + n] = f2bf(relu_sq(0, rnd(0, a)));
-                    } else if (EPI == EPI_SHDN) {
-                        p.shout[(size_t)row * p.H + n] = f2bf(a);
-                    } else {
-                        const float m = rnd(0, a);
-                        const float sh = p.SI ? bf2f(p.shout[(size_t)row * p.H + n]) : 0.0f;
-                        const float xv = bf2f(p.x[(size_t)row * p.H + n]);
-                        p.out[(size_t)row * p.H + n] = f2bf(xv + rnd(0, m + sh));
-                    }
+                    if (ks > 1) st_sharedf(mypart + (size_t)row * DENSE_TILE + 4 * grp + i, v[i]);
+                    else if (epi_pre) fc2_out(p, row, n0 + 4 * grp + i, v[i], pre.sh[i], pre.xv[i]);
+                    else dense_epilogue(p, EPI, row, n0 + 4 * grp + i, v[i]);
                 }
             }
         }
         __syncthreads();
+    }
+    if (ks > 1 && last_arriver(ctr + tile, (uint32_t)ks, s_flag)) {
+        for (int i = threadIdx.x; i < p.rows * DENSE_TILE; i += NW * 64) {
+            const int row = i / DENSE_TILE, nn = i % DENSE_TILE;
+            const float *pp = part + ((size_t)tile * ks * p.rows + row) * DENSE_TILE + nn;
+            float v = ld_sharedf(pp);
+            for (int q = 1; q < ks; ++q) v = v + ld_sharedf(pp + (size_t)q * p.rows * DENSE_TILE);
+            dense_epilogue(p, EPI, row, n0 + nn, v);
+        }
     }
 }
 
@@ -499,17 +681,21 @@ __device__ __forceinline__ void stage_lds(const uint4 *src, uint4 *dst, int unit
 // codes); a row is handled by Cp lanes (Cp = chunks rounded up to a power of two, at most
 // 64; NCH chunks per lane when there are more than 64).
 template <int NCH, bool UP>
-__device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int blk, ExpertLds &L) {
-    const int U = p.sched[SCH_U];
-    if (slot >= U) return;
+__device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the number of slots and the slot's record: independent loads (slots past U hold stale
+    // entries, which are not used)
+    const int U = p.sched[SCH_U];
     const int e = p.sched[SCH_EXPERT + slot];
     const int off = p.sched[SCH_OFF + slot];
-    const int R = p.sched[SCH_OFF + slot + 1] - off;
+    const int off1 = p.sched[SCH_OFF + slot + 1];
+    int pr = p.sched[SCH_FIRST + slot];
+    const int R = off1 - off;
     const int NP = p.rows * p.K;
-    if (e < 0 || e >= p.E || off < 0 || R < 0 || off + R > NP) {   // never for a valid schedule
+    if (slot >= U) return U;
+    if (e < 0 || e >= p.E || off < 0 || R < 1 || off1 > NP || pr < 0 || pr >= NP) {   // never for a valid schedule
         if (threadIdx.x == 0) atomicOr(p.err, 4u);
-        return;
+        return 0;
     }
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
     const int NB = UP ? p.up_nb : p.dn_nb;
@@ -528,13 +714,26 @@ __device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int 
     const int rpp = 64 / Cp;
     const int lrow = lane / Cp, c0 = lane % Cp;
     const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
+    // the first pair's input chunk is loaded while the weights stream in
+    uint4 xr[4] = {};
+    if (NCH == 1 && c0 < C) {
+        const uint16_t *xrow = xin + (UP ? (size_t)(pr / p.K) * Kin : (size_t)pr * Kin);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) xr[q4] = ((const uint4 *)(xrow + 32 * c0))[q4];
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int r = 0; r < R; ++r) {
-        int pr = p.sched[SCH_PAIRS + off + r];
-        if (pr >= NP) pr = NP - 1;
+        if (r > 0) {
+            pr = p.sched[SCH_PAIRS + off + r];
+            if (pr < 0 || pr >= NP) pr = NP - 1;
+        }
         const uint16_t *xrow = xin + (UP ? (size_t)(pr / p.K) * Kin : (size_t)pr * Kin);
+        if (NCH == 1 && r > 0 && c0 < C) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) xr[q4] = ((const uint4 *)(xrow + 32 * c0))[q4];
+        }
         // this lane's input chunks: summed, and with one chunk per lane also kept in
         // registers (fp32); with more they are re-read from cache for every output row
         float xf[NCH == 1 ? 32 : 1];
@@ -546,8 +745,13 @@ __device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int 
 #pragma unroll
             for (int i = 0; i < 32; ++i) t[i] = 0.0f;
             if (c < C) {
+                if constexpr (NCH == 1) {
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], &t[8 * q4]);
+                    for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, xr[q4], &t[8 * q4]);
+                } else {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], &t[8 * q4]);
+                }
             }
             float sum = 0.0f;
 #pragma unroll
@@ -558,7 +762,7 @@ __device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int 
                 for (int i = 0; i < 32; ++i) xf[i] = t[i];
             }
         }
-        for (int nb = wave * rpp; nb < NB; nb += 4 * rpp) {
+        for (int nb = wave * rpp; nb < NB; nb += (WG_THREADS / 64) * rpp) {
             const int nl = nb + lrow;                 // row within the block
             float acc = 0.0f;
 #pragma unroll
@@ -591,166 +795,119 @@ __device__ __forceinline__ void expert_item(const LayerParams &p, int slot, int 
             if (c0 == 0 && nl < NB) {
                 const int n = n0 + nl;
                 if (UP) p.eact[(size_t)pr * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, acc)));
-                else p.eout[(size_t)pr * p.D + n] = f2act(p.act_f16, acc);
+                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(p.act_f16, acc));
             }
         }
     }
+    return U;
 }
 
 // ------------------------------------------------------------------ combine
 
-// The combine of row r at latent output d, before rounding (lane order described at the top).
-__device__ __forceinline__ float combine_value(const LayerParams &p, int r, int d) {
-    float T[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) T[t] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < MAX_TOPK; ++j) {
-        if (j < p.K) {
-            const size_t pr = (size_t)r * p.K + j;
-            const float pj = p.wts[pr] * act2f(p.act_f16, p.eout[pr * p.D + d]);
-            T[j & 7] = T[j & 7] + pj;
+// Combine of latent outputs [n0, n0 + nb) for every row of the pass (the last down item of
+// that block to finish runs it); a non-latent layer also adds the residual here (fc2 is the
+// identity and there is no shared expert).
+__device__ __forceinline__ void combine_block(const LayerParams &p, int n0, int nb) {
+    for (int i = threadIdx.x; i < p.rows * nb; i += WG_THREADS) {
+        const int r = i / nb, d = n0 + i % nb;
+        const uint16_t c = f2act(p.act_f16, combine_value<true>(p, r, d));
+        p.comb[(size_t)r * p.D + d] = c;
+        if (!p.L) {
+            const float m = act2f(p.act_f16, c), sh = 0.0f;
+            const float xv = act2f(p.act_f16, p.x[(size_t)r * p.H + d]);
+            p.out[(size_t)r * p.H + d] = f2act(p.act_f16, xv + rnd(p.act_f16, m + sh));
         }
-    }
-    return ((T[0] + T[4]) + (T[2] + T[6])) + ((T[1] + T[5]) + (T[3] + T[7]));
-}
-
-// Item: (row, 256 outputs).
-__device__ __forceinline__ void combine_item(const LayerParams &p, int item) {
-    const int r = item / p.comb_blocks, blk = item % p.comb_blocks;
-    const int d = blk * COMBINE_BLOCK + threadIdx.x;
-    if (d >= p.D) return;
-    const uint16_t c = f2act(p.act_f16, combine_value(p, r, d));
-    p.comb[(size_t)r * p.D + d] = c;
-    if (!p.L) {
-        // non-latent: fc2 is the identity and there is no shared expert
-        const float m = act2f(p.act_f16, c), sh = 0.0f;
-        const float xv = act2f(p.act_f16, p.x[(size_t)r * p.H + d]);
-        p.out[(size_t)r * p.H + d] = f2act(p.act_f16, xv + rnd(p.act_f16, m + sh));
     }
 }
 
 // ------------------------------------------------------------------ driver
 
-constexpr int MAX_LATENT = 6144;
-constexpr int DW = DENSE_THREADS / 64;    // waves of a dense workgroup
+constexpr int NW = WG_THREADS / 64;    // waves of a workgroup
 
-struct Fc2Lds {
-    DenseLds<DW> dense;
-    uint16_t c[MAX_LATENT];   // the row's combine, when formed inline
-};
-
-// Launch groups: stages [first, last] of one launch (no item of a group depends on another
-// item of the same group), its workgroup size and its LDS.
-template <int G> struct Group;
-template <> struct Group<0> {
-    static constexpr int first = ST_GATE, last = ST_SHUP, threads = DENSE_THREADS;
-    union Lds { DenseLds<DW> dense; };
-};
-template <> struct Group<1> {
-    static constexpr int first = ST_ROUTE, last = ST_SHDN, threads = DENSE_THREADS;
-    union Lds { RouteLds<DENSE_THREADS> route; DenseLds<DW> dense; };
-};
-template <> struct Group<2> {
-    static constexpr int first = ST_SCHED, last = ST_SCHED, threads = WG_THREADS;
-    union Lds { SchedLds sched; };
-};
-template <> struct Group<3> {
-    static constexpr int first = ST_UP, last = ST_UP, threads = WG_THREADS;
-    union Lds { ExpertLds ex; };
-};
-template <> struct Group<4> {
-    static constexpr int first = ST_DOWN, last = ST_DOWN, threads = WG_THREADS;
-    union Lds { ExpertLds ex; };
-};
-template <> struct Group<5> {
-    static constexpr int first = ST_COMBINE, last = ST_COMBINE, threads = WG_THREADS;
-    union Lds { int unused; };
-};
-template <> struct Group<7> {   // expert up for inputs wider than 2048 (several chunks per lane)
-    static constexpr int first = ST_UP, last = ST_UP, threads = WG_THREADS;
-    union Lds { ExpertLds ex; };
-};
-template <> struct Group<8> {   // expert down for intermediates wider than 2048
-    static constexpr int first = ST_DOWN, last = ST_DOWN, threads = WG_THREADS;
-    union Lds { ExpertLds ex; };
-};
-template <> struct Group<6> {
-    static constexpr int first = ST_FC2, last = ST_FC2, threads = DENSE_THREADS;
-    union Lds { DenseLds<DW> dense; Fc2Lds fc2; };
+// Kernels: each covers the stages [FIRST, LAST] (the host launches any contiguous range of
+// items inside them); WIDE selects the expert variant for inputs wider than 2048.
+template <int FIRST, int LAST>
+struct StageLds {
+    static constexpr bool has(int s) { return FIRST <= s && s <= LAST; }
+    union U {
+        DenseLds<NW> dense;
+        RouteLds<WG_THREADS> route;
+        SchedLds sched;
+        ExpertLds ex;
+    };
 };
 
-template <int G, int S, class LdsT>
-__device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds) {
-    constexpr bool wide = G >= 7;
+template <int S, bool WIDE, class LdsT>
+__device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
-        gate_item<DW>(p, local);
+        gate_item<NW>(p, local);
+        if (p.single_row &&
+            last_arriver(p.ctr + CTR_GATE, (uint32_t)(p.item_base[ST_GATE + 1] - p.item_base[ST_GATE]), s_flag))
+            route_item<WG_THREADS>(p, 0, lds.route);
     } else if constexpr (S == ST_FC1) {
-        dense_item<EPI_FC1, DW>(p, p.fc1, p.x, p.H, local * DENSE_TILE, lds.dense);
+        const int ks = p.ks_fc1;
+        dense_item<EPI_FC1, NW>(p, p.fc1, p.x, p.H, local / ks, local % ks, ks, p.part_fc1, p.ctr + p.ctr_fc1,
+                                lds.dense, s_flag);
     } else if constexpr (S == ST_SHUP) {
-        dense_item<EPI_SHUP, DW>(p, p.su, p.x, p.H, local * DENSE_TILE, lds.dense);
+        const int ks = p.ks_shup;
+        dense_item<EPI_SHUP, NW>(p, p.su, p.x, p.H, local / ks, local % ks, ks, p.part_shup, p.ctr + p.ctr_shup,
+                                 lds.dense, s_flag);
     } else if constexpr (S == ST_ROUTE) {
-        route_item<DENSE_THREADS>(p, local, lds.route);
-    } else if constexpr (S == ST_SHDN) {
-        dense_item<EPI_SHDN, DW>(p, p.sd, p.shact, p.SI, local * DENSE_TILE, lds.dense);
-    } else if constexpr (S == ST_SCHED) {
-        sched_item(p, lds.sched);
+        route_item<WG_THREADS>(p, local, lds.route);
+        if (last_arriver(p.ctr + CTR_ROUTE, (uint32_t)p.rows, s_flag)) {
+            __syncthreads();
+            sched_item(p, lds.sched);
+        }
+    } else if constexpr (S == ST_SHDN_A || S == ST_SHDN_B) {
+        const int ks = p.ks_shdn;
+        const int it = local + (S == ST_SHDN_B ? p.item_base[ST_SHDN_A + 1] - p.item_base[ST_SHDN_A] : 0);
+        dense_item<EPI_SHDN, NW>(p, p.sd, p.shact, p.SI, it / ks, it % ks, ks, p.part_shdn, p.ctr + p.ctr_shdn,
+                                 lds.dense, s_flag);
     } else if constexpr (S == ST_UP) {
         const int slot = local / p.up_blocks, blk = local % p.up_blocks;
-        if constexpr (wide) expert_item<3, true>(p, slot, blk, lds.ex);
-        else expert_item<1, true>(p, slot, blk, lds.ex);
+        expert_item<WIDE ? 3 : 1, true>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_DOWN) {
         const int slot = local / p.dn_blocks, blk = local % p.dn_blocks;
-        if constexpr (wide) expert_item<3, false>(p, slot, blk, lds.ex);
-        else expert_item<1, false>(p, slot, blk, lds.ex);
-    } else if constexpr (S == ST_COMBINE) {
-        combine_item(p, local);
+        const int U = expert_item<WIDE ? 3 : 1, false>(p, slot, blk, lds.ex);
+        if (slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, s_flag))
+            combine_block(p, blk * p.dn_nb, p.dn_nb);
     } else if constexpr (S == ST_FC2) {
-        if (p.single_row) {
-            // one-row pass: form the whole combine in LDS first (the same arithmetic as the
-            // combine stage); the first item also stores it for inspection
-            for (int d = threadIdx.x; d < p.L; d += DENSE_THREADS) {
-                const uint16_t c = f2bf(combine_value(p, 0, d));
-                lds.fc2.c[d] = c;
-                if (local == 0) p.comb[d] = c;
-            }
-            __syncthreads();
-            dense_item<EPI_FC2, DW>(p, p.fc2, lds.fc2.c, p.L, local * DENSE_TILE, lds.fc2.dense);
-        } else {
-            dense_item<EPI_FC2, DW>(p, p.fc2, p.comb, p.L, local * DENSE_TILE, lds.dense);
-        }
+        const int ks = p.ks_fc2;
+        dense_item<EPI_FC2, NW>(p, p.fc2, p.comb, p.L, local / ks, local % ks, ks, p.part_fc2, p.ctr + p.ctr_fc2,
+                                lds.dense, s_flag);
     }
 }
 
-template <int G, int S, class LdsT>
-__device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds) {
-    if constexpr (S <= Group<G>::last) {
+template <int FIRST, int LAST, bool WIDE, int S, class LdsT>
+__device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds, int *s_flag) {
+    if constexpr (S <= LAST) {
         if (it < p.item_base[S + 1]) {
-            run_stage<G, S>(p, it - p.item_base[S], lds);
+            run_stage<S, WIDE>(p, it - p.item_base[S], lds, s_flag);
             return;
         }
-        dispatch<G, S + 1>(p, it, lds);
+        dispatch<FIRST, LAST, WIDE, S + 1>(p, it, lds, s_flag);
     }
 }
 
-template <int G>
-__global__ void __launch_bounds__(Group<G>::threads) __attribute__((amdgpu_waves_per_eu(4, 8)))
-moe_group_kernel(LayerParams p) {
-    __shared__ typename Group<G>::Lds lds;
-    const int it = p.item_base[Group<G>::first] + (int)blockIdx.x;
-    if (it >= p.item_base[Group<G>::last + 1]) return;
-    dispatch<G, Group<G>::first>(p, it, lds);
+// Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST]; with rev
+// set, workgroup 0 takes the last item (the hardware dispatches workgroups in index order, so
+// the later stage's items start first).
+template <int FIRST, int LAST, bool WIDE>
+__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(FIRST == ST_FC2 ? 2 : 4, 8)))
+moe_stage_kernel(LayerParams p, int lo, int hi, int rev) {
+    __shared__ typename StageLds<FIRST, LAST>::U lds;
+    __shared__ int s_flag;
+    const int it = rev ? hi - 1 - (int)blockIdx.x : lo + (int)blockIdx.x;
+    if (it >= hi) return;
+    dispatch<FIRST, LAST, WIDE, FIRST>(p, it, lds, &s_flag);
 }
 
-template __global__ void moe_group_kernel<0>(LayerParams);
-template __global__ void moe_group_kernel<1>(LayerParams);
-template __global__ void moe_group_kernel<2>(LayerParams);
-template __global__ void moe_group_kernel<3>(LayerParams);
-template __global__ void moe_group_kernel<4>(LayerParams);
-template __global__ void moe_group_kernel<5>(LayerParams);
-template __global__ void moe_group_kernel<6>(LayerParams);
-template __global__ void moe_group_kernel<7>(LayerParams);
-template __global__ void moe_group_kernel<8>(LayerParams);
+template __global__ void moe_stage_kernel<ST_GATE, ST_SHUP, false>(LayerParams, int, int, int);
+template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, false>(LayerParams, int, int, int);
+template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true>(LayerParams, int, int, int);
+template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, int, int, int);
+template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int);
+template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int);
 
 // zero a small device buffer (the error flag) without a memset node in captured graphs
 __global__ void moe_clear_kernel(uint32_t *ctr, int n) {

@@ -7,20 +7,22 @@ namespace moe {
 
 // Stages of one forward, in dependency order (TensorFold pull request 1038, «What's in
 // it»: gate gemv -> route -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj
-// -> + shared -> + residual). A stage only reads what earlier stages wrote.
+// -> + shared -> + residual). A stage only reads what earlier launches wrote, or what a
+// "last arriver" of the same launch reads after every item it depends on has counted itself
+// done (no item ever waits for another).
 enum Stage : int {
-    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order
+    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; for a one-row
+                   // pass the last gate item to finish also routes the row
     ST_FC1,        // u = rnd(W1 . x), 16 outputs per item (MFMA)
     ST_SHUP,       // shared expert up + relu^2, 16 outputs per item
-    ST_ROUTE,      // one row per item: sigmoid, group-limited top-k, weights (and, for a
-                   // one-row pass, the schedule)
-    ST_SHDN,       // shared expert down, 16 outputs per item
-    ST_SCHED,      // one item: distinct picked experts and their (row, pick) lists
+    ST_ROUTE,      // multi-row passes: one row per item; the last route item to finish builds
+                   // the schedule (distinct experts and their (row, pick) lists)
+    ST_SHDN_A,     // shared expert down, first half of the outputs
     ST_UP,         // routed expert up + relu^2: (slot, block of outputs) per item
-    ST_DOWN,       // routed expert down: (slot, block of outputs) per item
-    ST_COMBINE,    // weighted sum over the picks: (row, 256 latent outputs) per item
-    ST_FC2,        // m = rnd(W2 . c), out = rnd(x + rnd(m + sh)), 16 outputs per item (for a
-                   // one-row pass each item first forms the combine c itself)
+    ST_SHDN_B,     // shared expert down, second half of the outputs
+    ST_DOWN,       // routed expert down: (slot, block of outputs) per item; the last item of
+                   // each block to finish combines that block (and, non-latent, adds x)
+    ST_FC2,        // m = rnd(W2 . c), out = rnd(x + rnd(m + sh)), 16 outputs per item
     NSTAGE
 };
 
@@ -28,26 +30,32 @@ enum : int {
     MAX_EXPERTS = 1024,
     MAX_TOPK = 16,
     MAX_ROWS = 256,
+    // completion counters (uint32) of the last-arriver steps; the dense projections' tile
+    // counters follow (offsets in LayerParams)
+    CTR_GATE = 0,
+    CTR_ROUTE = 1,
+    CTR_BLOCK = 2,         // CTR_BLOCK + b: down items of output block b done
+    CTR_DENSE = 2048,
 };
 
 // schedule block (int32) in the workspace: [0] = U (distinct experts picked),
-// [SCH_EXPERT + u] = expert of slot u (increasing expert id), [SCH_OFF + u] = first pair
-// of slot u (U + 1 entries), [SCH_PAIRS + i] = pair row * top_k + pick, sorted by
-// (expert, row).
+// [SCH_EXPERT + u] = expert of slot u (increasing expert id), [SCH_OFF + u] = offset of
+// slot u's pairs (U + 1 entries), [SCH_FIRST + u] = slot u's first pair (a copy, so that an
+// item finds it without a dependent load), [SCH_PAIRS + i] = pair row * top_k + pick,
+// sorted by (expert, row).
 enum : int {
     SCH_U = 0,
     SCH_EXPERT = 1,
     SCH_OFF = SCH_EXPERT + MAX_EXPERTS,
-    SCH_PAIRS = SCH_OFF + MAX_EXPERTS + 1,
+    SCH_FIRST = SCH_OFF + MAX_EXPERTS + 1,
+    SCH_PAIRS = SCH_FIRST + MAX_EXPERTS,
     SCH_COUNT = SCH_PAIRS + MAX_ROWS * MAX_TOPK,
 };
 
-constexpr int WG_THREADS = 256;   // 4 waves of 64 (schedule, expert and combine items)
-constexpr int DENSE_THREADS = 512;  // 8 waves (gate, route, dense projections)
+constexpr int WG_THREADS = 512;   // 8 waves of 64 in every item
 constexpr int EXPERT_LDS_CODES = 16384;   // LDS bytes for one expert item's codes
 constexpr int EXPERT_LDS_SCALES = 1024;   // ... and for its scales (and again its biases)
 constexpr int EXPERT_MAX_BLOCK = 32;      // output rows of one expert item at most
-constexpr int COMBINE_BLOCK = 256;
 constexpr int DENSE_TILE = 16;    // outputs per dense item
 
 struct LayerParams {
@@ -79,14 +87,19 @@ struct LayerParams {
     uint16_t *eout;        // [rows*K][D]
     uint16_t *comb;        // [rows][D]
     uint16_t *shout;       // [rows][H]
+    uint32_t *ctr;         // completion counters, zero between forwards
+    int ctr_fc1, ctr_shup, ctr_shdn, ctr_fc2;   // first counter of each dense projection's tiles
+    int ks_fc1, ks_shup, ks_shdn, ks_fc2;       // items (K splits) per 16-output tile
+    float *part_fc1, *part_shup, *part_shdn, *part_fc2;   // split-K partial sums [tile][split][row][16]
     uint32_t *err;         // device error flag (bit 1: a route found no candidate, bit 2: an
                            // invalid schedule; neither happens for a valid configuration)
     // work-item table: items of stage s are [item_base[s], item_base[s + 1])
     int item_base[NSTAGE + 1];
     int umax;              // slots enumerated by ST_UP / ST_DOWN items
     int up_nb, dn_nb;      // output rows of one routed up / down item
-    int up_blocks, dn_blocks, comb_blocks;
-    int single_row;        // rows == 1: route writes the schedule, fc2 items combine inline
+    int up_blocks, dn_blocks;
+    int single_row;        // rows == 1: the last gate item routes and writes the schedule
+    int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
 };
 
 }  // namespace moe

@@ -19,7 +19,7 @@
 #include "layer_plan.h"
 
 namespace moe {
-template <int G> __global__ void moe_group_kernel(LayerParams p);   // G = 0..8
+template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int rev);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 }  // namespace moe
 
@@ -33,6 +33,7 @@ struct moe_latent {
     int last_rows;
     void *ws;               // one workspace allocation
     size_t ws_bytes;
+    int n_ctr;             // completion counters in the workspace
     uint32_t magic;
 };
 
@@ -234,21 +235,44 @@ static int check_device(int *dev_out, int *cus) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Items per 16-output tile of a dense projection over K inputs: each item takes K / splits
+// inputs (a multiple of 128); the last of a tile's items to finish adds their partial sums.
+// Up to K = 4096 a tile is one item (128 KB of weights, all in flight at once); wider
+// projections are cut in 4096-input parts.
+static int dense_splits_host(int K) { return K > 4096 && K % 4096 == 0 ? K / 4096 : 1; }
+
 static int setup_workspace(moe_latent *h) {
     const moe_latent_config &c = h->cfg;
     const size_t R = c.max_rows, E = c.n_experts, K = c.top_k, I = c.expert_inter, H = c.hidden;
     const size_t D = c.latent ? c.latent : c.hidden, SI = c.shared_inter, L = c.latent;
-    struct Region { size_t bytes; size_t off; } reg[11];
-    const size_t sizes[11] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
-                              R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
-                              R * H * 2, 256};
+    LayerParams &p = h->base;
+    p.ks_fc1 = dense_splits_host((int)H);
+    p.ks_shup = dense_splits_host((int)H);
+    p.ks_shdn = dense_splits_host(SI ? (int)SI : 1);
+    p.ks_fc2 = dense_splits_host(L ? (int)L : 1);
+    // dense tile counters after the fixed ones
+    p.ctr_fc1 = CTR_DENSE;
+    p.ctr_shup = p.ctr_fc1 + (int)(L / DENSE_TILE);
+    p.ctr_shdn = p.ctr_shup + (int)(SI / DENSE_TILE);
+    p.ctr_fc2 = p.ctr_shdn + (SI ? (int)(H / DENSE_TILE) : 0);
+    h->n_ctr = p.ctr_fc2 + (L ? (int)(H / DENSE_TILE) : 0);
+    // split-K partials: [tile][split][row][16] floats = N * splits * rows floats
+    const size_t part_fc1 = L * p.ks_fc1 * R * 4;
+    const size_t part_shup = SI * p.ks_shup * R * 4;
+    const size_t part_shdn = SI ? H * p.ks_shdn * R * 4 : 0;
+    const size_t part_fc2 = L ? H * p.ks_fc2 * R * 4 : 0;
+    enum { NREG = 16 };
+    struct Region { size_t bytes; size_t off; } reg[NREG];
+    const size_t sizes[NREG] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
+                                R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
+                                R * H * 2, 256, (size_t)h->n_ctr * 4, part_fc1, part_shup, part_shdn,
+                                part_fc2};
     size_t off = 0;
-    for (int i = 0; i < 11; ++i) { reg[i].bytes = sizes[i]; reg[i].off = off; off += align256(sizes[i]); }
+    for (int i = 0; i < NREG; ++i) { reg[i].bytes = sizes[i]; reg[i].off = off; off += align256(sizes[i]); }
     h->ws_bytes = off;
     hipError_t e = dev_alloc(&h->ws, off);
     if (e != hipSuccess) return fail(MOE_ERR_OOM, "workspace of %zu bytes: %s", off, hipGetErrorString(e));
     char *b = (char *)h->ws;
-    LayerParams &p = h->base;
     p.logits = b + reg[0].off;
     p.idx = (int32_t *)(b + reg[1].off);
     p.wts = (float *)(b + reg[2].off);
@@ -260,11 +284,19 @@ static int setup_workspace(moe_latent *h) {
     p.comb = (uint16_t *)(b + reg[8].off);
     p.shout = (uint16_t *)(b + reg[9].off);
     p.err = (uint32_t *)(b + reg[10].off);
+    p.ctr = (uint32_t *)(b + reg[11].off);
+    p.part_fc1 = (float *)(b + reg[12].off);
+    p.part_shup = (float *)(b + reg[13].off);
+    p.part_shdn = (float *)(b + reg[14].off);
+    p.part_fc2 = (float *)(b + reg[15].off);
     return MOE_OK;
 }
 
+// zero the error flag and the completion counters (at create, and after a device error)
 static hipError_t clear_flag(moe_latent *h) {
     hipLaunchKernelGGL(moe_clear_kernel, dim3(1), dim3(64), 0, h->stream, h->base.err, 64);
+    hipLaunchKernelGGL(moe_clear_kernel, dim3((h->n_ctr + 255) / 256), dim3(256), 0, h->stream, h->base.ctr,
+                       h->n_ctr);
     return hipGetLastError();
 }
 
@@ -354,12 +386,57 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
     return MOE_OK;
 }
 
+// Launch the items of stages [first, last] on stream st with the kernel covering them; rev:
+// the last stage's items are dispatched first.
+template <int KF, int KL, bool WIDE>
+static void launch_range(const LayerParams &p, int first, int last, hipStream_t st, int rev = 0) {
+    const int lo = p.item_base[first], hi = p.item_base[last + 1];
+    if (hi > lo)
+        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, rev);
+}
+
+// The launches of one forward, in order (see layer_kernels.hip): all of them (g == -1),
+// launch g only (g >= 0), or none (g == -2, to count them). Returns the number of launches.
+static int launch_plan(const LayerParams &p, hipStream_t st, int g) {
+    const bool wide = p.D > 2048 || p.I > 2048;
+    int n = 0;
+    auto go = [&](auto fn) { if (g == -1 || g == n) fn(); ++n; };
+    go([&] { launch_range<ST_GATE, ST_SHUP, false>(p, ST_GATE, ST_SHUP, st); });
+    if (p.single_row) {
+        // the routed expert items (on the critical path) are dispatched before the shared
+        // expert's down items that fill the rest of the machine
+        go([&] {
+            if (wide) launch_range<ST_ROUTE, ST_UP, true>(p, ST_ROUTE, ST_UP, st, 1);
+            else launch_range<ST_ROUTE, ST_UP, false>(p, ST_ROUTE, ST_UP, st, 1);
+        });
+        go([&] {
+            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_SHDN_B, ST_DOWN, st, 1);
+            else launch_range<ST_UP, ST_DOWN, false>(p, ST_SHDN_B, ST_DOWN, st, 1);
+        });
+    } else {
+        go([&] {
+            if (wide) launch_range<ST_ROUTE, ST_UP, true>(p, ST_ROUTE, ST_SHDN_A, st);
+            else launch_range<ST_ROUTE, ST_UP, false>(p, ST_ROUTE, ST_SHDN_A, st);
+        });
+        go([&] {
+            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_UP, ST_SHDN_B, st);
+            else launch_range<ST_UP, ST_DOWN, false>(p, ST_UP, ST_SHDN_B, st);
+        });
+        go([&] {
+            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_DOWN, ST_DOWN, st);
+            else launch_range<ST_UP, ST_DOWN, false>(p, ST_DOWN, ST_DOWN, st);
+        });
+    }
+    go([&] { launch_range<ST_FC2, ST_FC2, false>(p, ST_FC2, ST_FC2, st); });
+    return n;
+}
+
 extern "C" int moe_latent_set_variant(moe_latent_t *h, int32_t variant) {
     if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
     if (variant == 0)
         return fail(MOE_ERR_INVALID_ARG, "variant 0 (one fused launch per forward) is disabled: its first "
                     "GPU run did not complete and the cause is not yet found");
-    if (variant != 1) return fail(MOE_ERR_INVALID_ARG, "variant %d (1: launch groups)", variant);
+    if (variant != 1) return fail(MOE_ERR_INVALID_ARG, "variant %d (1: the launch chain)", variant);
     return MOE_OK;
 }
 
@@ -367,35 +444,26 @@ static void plan_items(LayerParams &p, int rows) {
     int n[NSTAGE];
     p.rows = rows;
     p.single_row = rows == 1;
-    const bool inline_combine = p.single_row && p.L > 0;
+    p.inline_comb = rows == 1 && p.L && p.L / p.ks_fc2 <= 4096;
     p.umax = p.E < rows * p.K ? p.E : rows * p.K;
     p.up_nb = expert_block(p.I, p.D);
     p.dn_nb = expert_block(p.D, p.I);
     p.up_blocks = p.I / p.up_nb;
     p.dn_blocks = p.D / p.dn_nb;
-    p.comb_blocks = (p.D + COMBINE_BLOCK - 1) / COMBINE_BLOCK;
-    n[ST_GATE] = (p.E + DENSE_THREADS / 64 - 1) / (DENSE_THREADS / 64);
-    n[ST_FC1] = p.L ? p.L / DENSE_TILE : 0;
-    n[ST_SHUP] = p.SI / DENSE_TILE;
-    n[ST_ROUTE] = rows;
-    n[ST_SHDN] = p.SI ? p.H / DENSE_TILE : 0;
-    n[ST_SCHED] = p.single_row ? 0 : 1;
+    // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's
+    // tiles are cut in two halves for two launches
+    const int shdn = p.SI ? p.H / DENSE_TILE : 0, ks_sd = p.ks_shdn;
+    n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64);
+    n[ST_FC1] = p.L ? p.L / DENSE_TILE * p.ks_fc1 : 0;
+    n[ST_SHUP] = p.SI / DENSE_TILE * p.ks_shup;
+    n[ST_ROUTE] = p.single_row ? 0 : rows;
+    n[ST_SHDN_A] = shdn / 2 * ks_sd;
     n[ST_UP] = p.umax * p.up_blocks;
+    n[ST_SHDN_B] = (shdn - shdn / 2) * ks_sd;
     n[ST_DOWN] = p.umax * p.dn_blocks;
-    n[ST_COMBINE] = inline_combine ? 0 : rows * p.comb_blocks;
-    n[ST_FC2] = p.L ? p.H / DENSE_TILE : 0;
+    n[ST_FC2] = p.L ? p.H / DENSE_TILE * p.ks_fc2 : 0;
     p.item_base[0] = 0;
     for (int s = 0; s < NSTAGE; ++s) p.item_base[s + 1] = p.item_base[s] + n[s];
-}
-
-// workgroup size of each launch group (must match the kernels' Group<G>::threads)
-static const int kGroupThreads[9] = {DENSE_THREADS, DENSE_THREADS, WG_THREADS, WG_THREADS, WG_THREADS,
-                                     WG_THREADS, DENSE_THREADS, WG_THREADS, WG_THREADS};
-
-template <int G>
-static void launch_group(const LayerParams &p, int first, int last, hipStream_t st) {
-    const int items = p.item_base[last + 1] - p.item_base[first];
-    if (items > 0) hipLaunchKernelGGL(moe_group_kernel<G>, dim3(items), dim3(kGroupThreads[G]), 0, st, p);
 }
 
 extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
@@ -411,16 +479,7 @@ extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hid
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    hipStream_t st = h->stream;
-    launch_group<0>(p, ST_GATE, ST_SHUP, st);
-    launch_group<1>(p, ST_ROUTE, ST_SHDN, st);
-    launch_group<2>(p, ST_SCHED, ST_SCHED, st);
-    if (p.D > 2048) launch_group<7>(p, ST_UP, ST_UP, st);
-    else launch_group<3>(p, ST_UP, ST_UP, st);
-    if (p.I > 2048) launch_group<8>(p, ST_DOWN, ST_DOWN, st);
-    else launch_group<4>(p, ST_DOWN, ST_DOWN, st);
-    launch_group<5>(p, ST_COMBINE, ST_COMBINE, st);
-    launch_group<6>(p, ST_FC2, ST_FC2, st);
+    launch_plan(p, h->stream, -1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     h->last_rows = rows;
@@ -433,39 +492,30 @@ extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void
     if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
     if (rows < 1 || rows > h->cfg.max_rows)
         return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
-    if (group < 0 || group > 6) return fail(MOE_ERR_INVALID_ARG, "group %d outside 0..6", group);
     LayerParams p = h->base;
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    hipStream_t st = h->stream;
-    switch (group) {
-    case 0: launch_group<0>(p, ST_GATE, ST_SHUP, st); break;
-    case 1: launch_group<1>(p, ST_ROUTE, ST_SHDN, st); break;
-    case 2: launch_group<2>(p, ST_SCHED, ST_SCHED, st); break;
-    case 3:
-        if (p.D > 2048) launch_group<7>(p, ST_UP, ST_UP, st);
-        else launch_group<3>(p, ST_UP, ST_UP, st);
-        break;
-    case 4:
-        if (p.I > 2048) launch_group<8>(p, ST_DOWN, ST_DOWN, st);
-        else launch_group<4>(p, ST_DOWN, ST_DOWN, st);
-        break;
-    case 5: launch_group<5>(p, ST_COMBINE, ST_COMBINE, st); break;
-    default: launch_group<6>(p, ST_FC2, ST_FC2, st); break;
-    }
+    const int n = launch_plan(p, nullptr, -2);   // counts the launches, launches nothing
+    if (group < 0 || group >= n) return fail(MOE_ERR_INVALID_ARG, "group %d outside 0..%d", group, n - 1);
+    launch_plan(p, h->stream, group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 
 extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group) {
-    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows || group < 0 || group > 6) return -1;
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
     LayerParams p = h->base;
     plan_items(p, rows);
-    static const int first[7] = {ST_GATE, ST_ROUTE, ST_SCHED, ST_UP, ST_DOWN, ST_COMBINE, ST_FC2};
-    static const int last[7] = {ST_SHUP, ST_SHDN, ST_SCHED, ST_UP, ST_DOWN, ST_COMBINE, ST_FC2};
-    return p.item_base[last[group] + 1] - p.item_base[first[group]];
+    const int n = launch_plan(p, nullptr, -2);
+    if (group < 0 || group >= n) return 0;
+    // items of the launch: the stage ranges of launch_plan
+    static const int one[4][2] = {{ST_GATE, ST_SHUP}, {ST_ROUTE, ST_UP}, {ST_SHDN_B, ST_DOWN}, {ST_FC2, ST_FC2}};
+    static const int many[5][2] = {{ST_GATE, ST_SHUP}, {ST_ROUTE, ST_SHDN_A}, {ST_UP, ST_SHDN_B}, {ST_DOWN, ST_DOWN},
+                                   {ST_FC2, ST_FC2}};
+    const int *r = p.single_row ? one[group] : many[group];
+    return p.item_base[r[1] + 1] - p.item_base[r[0]];
 }
 
 extern "C" int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev) {

@@ -159,6 +159,41 @@ def test_fused_and_staged_launches_agree_bitwise():
                 assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("rows", [1, 9])
+def test_graph_replays_match_eager(rows):
+    """A forward captured in a HIP graph gives the eager bits on every replay, with eager
+    work (another forward on different rows) between the replays."""
+    from latent_mixture_experts_bf16_amd import binding as B
+    dims, arrays = workload(0, rows=9)
+    lay = _LY().DeviceLayer(dims, arrays, 9)
+    xd = _x_dev(dims, arrays["x"][:rows])
+    eager = torch.empty_like(xd)
+    lay.forward(xd, eager)
+    torch.cuda.synchronize()
+    ref = eager.cpu().numpy()
+    s = torch.cuda.Stream()
+    B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+    out = torch.empty_like(xd)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        lay.forward(xd, out)            # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            lay.forward(xd, out)
+    x_other = _x_dev(dims, arrays["x"][3:6])
+    other = torch.empty_like(x_other)
+    for i in range(5):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), i
+        with torch.cuda.stream(s):
+            lay.forward(x_other, other, 3)
+        torch.cuda.synchronize()
+    lay.status()
+    lay.close()
+
+
 def test_repeated_forwards_are_deterministic():
     dims, arrays = workload(1)
     lay = _LY().DeviceLayer(dims, arrays, 1)
@@ -278,6 +313,8 @@ def test_variant_zero_is_refused():
     lay = _LY().DeviceLayer(dims, arrays, 1)
     with pytest.raises(B.MoeError):
         B.moe_latent_set_variant(lay.handle, 0)
+    with pytest.raises(B.MoeError):
+        B.moe_latent_set_variant(lay.handle, 2)
     B.moe_latent_set_variant(lay.handle, 1)
     lay.close()
 
