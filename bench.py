@@ -14,6 +14,8 @@ bytes of one launch / its average duration, both measured here with HIP events o
 launch stream), and the CPU oracle timed on this host.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +30,14 @@ LAUNCHES_ONE_ROW = [("gate+fc1+shared_up+route", ["gate", "fc1", "shup", "route"
                     ("shared_down_a+expert_up", ["shdn_a", "up"]),
                     ("shared_down_b+expert_down+combine", ["shdn_b", "down"]),
                     ("fc2+shared+residual", ["fc2"])]
+# kernel of each one-row launch, as rocprofv3 names it (template arguments: first and last
+# stage of the kernel, wide expert variant)
+KERNELS_ONE_ROW = ["moe_stage_kernel<0, 2, false>", "moe_stage_kernel<3, 5, false>",
+                   "moe_stage_kernel<5, 7, false>", "moe_stage_kernel<8, 8, false>"]
+KERNEL_SOURCES = ["latent_mixture_experts_bf16_amd/csrc/layer_kernels.hip",
+                  "latent_mixture_experts_bf16_amd/csrc/layer_plan.h",
+                  "latent_mixture_experts_bf16_amd/csrc/moe_latent_api.hip"]
+COPY_MIB = 512   # size of the calibration copy (int32 negation: reads and writes COPY_MIB MiB)
 LAUNCHES_MULTI_ROW = [("gate+fc1+shared_up", ["gate", "fc1", "shup"]),
                       ("route+schedule+shared_down_a", ["route", "shdn_a"]),
                       ("expert_up+shared_down_b", ["up", "shdn_b"]),
@@ -44,7 +54,93 @@ def parse():
     ap.add_argument("--instances", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="run this many forwards eagerly, then one calibration copy, and exit "
+                         "(the workload of the rocprofv3 --pmc runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) into "
+                         "the traffic summary --pmc-out")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats output folder into a text summary "
+                         "written to --stats-out")
+    ap.add_argument("--pmc-out")
+    ap.add_argument("--stats-out")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.json")
+
+
+def _csv_rows(folder, name):
+    import csv
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", f"*{name}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{name} under {folder}")
+    return rows
+
+
+def _short(kernel_name):
+    for k in KERNELS_ONE_ROW:
+        if k.replace(" ", "") in kernel_name.replace(" ", ""):
+            return k
+    return "copy" if "elementwise" in kernel_name else None
+
+
+def summarize_pmc(args):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each layer kernel, scaled by the
+    same counters of the calibration copy of known size."""
+    import numpy as np
+    out = {}
+    for counter, folder in (("FETCH_SIZE", args.summarize_pmc[0]), ("WRITE_SIZE", args.summarize_pmc[1])):
+        per = {}
+        for r in _csv_rows(folder, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            k = _short(r.get("Kernel_Name", ""))
+            if k is None:
+                continue
+            per.setdefault(k, []).append(float(r["Counter_Value"]))
+        if "copy" not in per:
+            raise SystemExit(f"{counter}: the calibration copy kernel is missing")
+        copy_kib = float(np.max(per["copy"]))   # the big copy is the largest elementwise dispatch
+        factor = copy_kib / (COPY_MIB * 1024.0)
+        out[counter] = {"copy_kib": copy_kib, "factor": factor,
+                        "kernels": {k: {"dispatches": len(v), "kib_mean": float(np.mean(v)),
+                                        "bytes_scaled": float(np.mean(v)) * 1024.0 / factor}
+                                    for k, v in per.items() if k != "copy"}}
+    summary = {"workload": "bolt-latent-E240-rows1", "kernel_source_sha256": source_hash(),
+               "command": args.command, "copy_mib_read_and_written": COPY_MIB, "counters": out}
+    with open(args.pmc_out, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps(summary, indent=1))
+    return 0
+
+
+def summarize_stats(args):
+    rows = _csv_rows(args.summarize_stats, "kernel_stats.csv")
+    lines = [f"rocprofv3 kernel statistics ({args.command})", "",
+             f"{'kernel':70s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.3f} "
+                     f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f} {float(r['Percentage']):6.2f}")
+    txt = "\n".join(lines) + "\n"
+    with open(args.stats_out, "w") as fh:
+        fh.write(txt)
+    print(txt)
+    return 0
 
 
 def stage_bytes(dims, rows, n_distinct):
@@ -71,6 +167,10 @@ def stage_bytes(dims, rows, n_distinct):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        return summarize_pmc(args)
+    if args.summarize_stats:
+        return summarize_stats(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer's sharding "
@@ -108,6 +208,21 @@ def main():
     s = torch.cuda.Stream()
     for lay in layers:
         B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+    if args.profile_steps:
+        # the workload of the counter runs: eager forwards, then a copy of known size
+        with torch.cuda.stream(s):
+            for i in range(args.profile_steps):
+                layers[i % inst].forward(xs[i % inst], outs[i % inst], rows)
+            src = torch.ones(COPY_MIB << 18, dtype=torch.int32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        for lay in layers:
+            lay.status()
+            lay.close()
+        print(f"[bench] profile workload done: {args.profile_steps} forwards, one {COPY_MIB} MiB copy",
+              file=sys.stderr, flush=True)
+        return 0
     with torch.cuda.stream(s):
         for lay, x, o in zip(layers, xs, outs):
             lay.forward(x, o, rows)
@@ -184,6 +299,21 @@ def main():
         lay.status()
     dom = max(group_stats, key=lambda k: group_stats[k]["us"])
     d = group_stats[dom]
+    traffic, traffic_note = None, "no counter summary for this workload"
+    tf = traffic_file(wl.name)
+    if rows == 1 and os.path.exists(tf):
+        with open(tf) as fh:
+            pmc = json.load(fh)
+        if pmc.get("kernel_source_sha256") != source_hash():
+            traffic_note = "counter summary predates the current kernel source"
+        else:
+            kname = KERNELS_ONE_ROW[dom]
+            try:
+                traffic = int(pmc["counters"]["FETCH_SIZE"]["kernels"][kname]["bytes_scaled"] +
+                              pmc["counters"]["WRITE_SIZE"]["kernels"][kname]["bytes_scaled"])
+                traffic_note = f"FETCH_SIZE + WRITE_SIZE of {kname}, scaled by the calibration copy"
+            except KeyError:
+                traffic_note = f"{kname} missing from the counter summary"
     print(f"[bench] groups: {json.dumps(group_stats)}", file=sys.stderr, flush=True)
 
     # parity of instance 0 against the oracle, and the oracle timed on this host
@@ -232,7 +362,8 @@ def main():
                       "frac": round(layer_gbps / HBM_PEAK_GBPS, 4)},
         "roofline": {"bound": "hbm", "kernel": f"launch {dom}: moe_stage_kernel ({d['name']})",
                      "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_note": traffic_note,
                      "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]},
         "launches": {v["name"]: {"us": v["us"], "bytes": v["bytes"], "gbps": v["gbps"]}
                      for v in group_stats.values()},

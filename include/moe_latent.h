@@ -89,7 +89,8 @@ typedef struct {
     float routed_scaling;   /* rho */
 } moe_latent_config;
 
-/* The layer's weights (borrowed: the caller keeps every buffer alive until destroy).
+/* The layer's weights (borrowed: the caller keeps every buffer alive until destroy; every
+ * data pointer 16-byte aligned, MOE_ERR_LAYOUT otherwise).
  *   gate_w      [E][H]     bf16 (router_dtype BF16) or fp32 (F32)
  *   corr_bias   [E]        fp32 (only read when has_bias)
  *   fc1_w       [L][H]     bf16 (latent layers only)
@@ -127,7 +128,8 @@ int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
 /* One forward of `rows` independent rows (TensorFold pull request 1038, «What's in it»,
  * layer order; «Per operator and row invariance»: each row of a multi-row pass equals its
  * own one-row pass). hidden_in: [rows][H] activations (act_dtype); out: [rows][H] (same
- * dtype). out == hidden_in (in place) is allowed; any other overlap is refused. Enqueued on
+ * dtype); both 16-byte aligned (MOE_ERR_LAYOUT otherwise). out == hidden_in (in place) is
+ * allowed; any other overlap is refused. Enqueued on
  * the handle's stream as four or five launches (no host synchronisation, no allocation, no
  * memset: it can be captured in a HIP graph); returns launch errors only -- device-side
  * faults surface at the caller's next synchronisation / moe_latent_status(). The handle is
@@ -138,9 +140,10 @@ int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, voi
 void moe_latent_destroy(moe_latent_t *h);
 
 /* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (the last
- * gate workgroup routes the row); 1 shared down (first half) + routed expert up; 2 shared
- * down (second half) + routed expert down (the last workgroup of each output block combines
- * it); 3 fc2 + shared + residual. Multi-row pass: 0 as above without the route; 1 route (the
+ * gate workgroup routes the row); 1 routed expert up + shared down (first half); 2 routed
+ * expert down + shared down (second half); 3 combine + fc2 + shared + residual (each fc2
+ * workgroup combines the slice of the expert outputs it reads; a non-latent layer combines
+ * in group 2 instead). Multi-row pass: 0 as above without the route; 1 route (the
  * last route workgroup builds the expert schedule) + shared down (first half); 2 routed
  * expert up + shared down (second half); 3 routed expert down + combine; 4 fc2 + shared +
  * residual. A non-latent layer has no fc1 / fc2 / shared launches: its combine adds the
@@ -154,7 +157,7 @@ int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in
                             int32_t group);
 
 /* Number of workgroups launch group `group` runs for a pass of `rows` rows (0: nothing to
- * launch), or -1 for an invalid handle, rows or group. */
+ * launch, or no such group), or -1 for an invalid handle or rows. */
 int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
 
 /* Change the stream later forwards are enqueued on (e.g. a graph-capture stream). */

@@ -4,11 +4,12 @@
 // chain of launches on one stream; stages that do not depend on each other share a launch,
 // and steps that need every item of a stage (route after the gate, schedule after the
 // route, combine after the experts of a block) are run by the last item to finish:
-//   one row:   [gate, fc1, shared up; route] -> [shared down A, expert up] ->
-//              [shared down B, expert down; combine] -> [fc2 + shared + residual]
+//   one row:   [gate, fc1, shared up; route] -> [expert up, shared down A] ->
+//              [expert down, shared down B] -> [combine + fc2 + shared + residual]
 //   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
 //              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]
-// One workgroup of 8 waves runs one item.
+// One workgroup of 4 waves runs one item; a launch's items are sized (about 32-64 KB of
+// weights each) so that all of them are resident at once, four per compute unit.
 //
 // Arithmetic of each stage (TensorFold pull request 1038, «What's in it»: gate gemv ->
 // route top-k -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj -> +
@@ -37,6 +38,7 @@
 #include <stdint.h>
 
 #include "layer_plan.h"
+#include <type_traits>
 
 namespace moe {
 
@@ -261,12 +263,19 @@ __device__ __forceinline__ int count_greater(const uint64_t *v, int n, uint64_t 
 // The same for any alignment of v.
 __device__ __forceinline__ int count_greater_any(const uint64_t *v, int n, uint64_t k) {
     int c = 0, f = 0;
-    for (; f + 8 <= n; f += 8) {
-        uint64_t t[8];
+    for (; f + 16 <= n; f += 16) {
+        uint64_t t[16];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) t[q] = v[f + q];
+        for (int q = 0; q < 16; ++q) t[q] = v[f + q];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) c += t[q] > k;
+        for (int q = 0; q < 16; ++q) c += t[q] > k;
+    }
+    for (; f + 4 <= n; f += 4) {
+        uint64_t t[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = v[f + q];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c += t[q] > k;
     }
     for (; f < n; ++f) c += v[f] > k;
     return c;
@@ -276,10 +285,13 @@ template <int NT>
 struct RouteLds {
     float s[MAX_EXPERTS];
     float b[MAX_EXPERTS];
-    alignas(16) uint64_t key[MAX_EXPERTS];    // rank keys of the biased scores; 0 once excluded
+    alignas(16) uint64_t key[MAX_EXPERTS];    // rank keys of the biased scores
+    alignas(16) uint64_t ckey[MAX_EXPERTS];   // the candidates' keys (kept groups, in id order)
     alignas(16) uint64_t gkey[256];           // rank keys of the group scores
+    int rank[MAX_EXPERTS];                    // candidate ranks, summed over counting threads
     int top[256][2];              // the two best members of each group
-    int keep[256];
+    int keep[256];                // 1: the group is kept
+    int gslot[256];               // a kept group's position among the kept groups, else -1
     int picks[MAX_TOPK];
 };
 
@@ -305,7 +317,10 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
         L.key[e] = rank_key(b, e);
     }
     if (tid < MAX_TOPK) L.picks[tid] = -1;
+    for (int c = tid; c < E; c += NT) L.rank[c] = 0;
     __syncthreads();
+    const uint64_t *cand = L.key;   // candidates: every expert, or those of the kept groups
+    int nc = E;
     if (p.TG < G) {
         // the two best members of each group: rank of each expert inside its group
         for (int e = tid; e < E; e += NT) {
@@ -320,21 +335,37 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
             L.gkey[g] = rank_key(gam, g);
         }
         __syncthreads();
+        // kept groups: rank < TG; then each kept group's position among the kept ones
+        for (int g = tid; g < G; g += NT) L.keep[g] = count_greater(L.gkey, G, L.gkey[g]) < p.TG;
+        __syncthreads();
         for (int g = tid; g < G; g += NT) {
-            const uint64_t kg = L.gkey[g];
-            L.keep[g] = count_greater(L.gkey, G, kg) < p.TG;
+            int before = 0;
+            for (int h = 0; h < g; ++h) before += L.keep[h];
+            L.gslot[g] = L.keep[g] ? before : -1;
         }
         __syncthreads();
-        for (int e = tid; e < E; e += NT)
-            if (!L.keep[e / per]) L.key[e] = 0ull;
+        for (int e = tid; e < E; e += NT) {
+            const int g = e / per, slot = L.gslot[g];
+            if (slot >= 0) L.ckey[slot * per + (e - g * per)] = L.key[e];
+        }
         __syncthreads();
+        cand = L.ckey;
+        nc = p.TG * per;
     }
-    // the top_k candidates: rank among the remaining keys
-    for (int e = tid; e < E; e += NT) {
-        const uint64_t k = L.key[e];
-        if (k == 0ull) continue;
-        const int rank = count_greater(L.key, E, k);
-        if (rank < p.K) L.picks[rank] = e;
+    // the top_k candidates: rank among the candidates, counted by T threads per candidate
+    // (each over a contiguous part of the list) and summed in LDS
+    int T = 1;
+    while (T < 16 && 2 * T * nc <= NT) T *= 2;
+    for (int i = tid; i < nc * T; i += NT) {
+        const int c = i / T, part = i % T;
+        const int lo = part * nc / T, hi = (part + 1) * nc / T;
+        const int cnt = count_greater_any(cand + lo, hi - lo, cand[c]);
+        atomicAdd(&L.rank[c], cnt);
+    }
+    __syncthreads();
+    for (int c = tid; c < nc; c += NT) {
+        const int rank = L.rank[c];
+        if (rank < p.K) L.picks[rank] = (int)(0xFFFFFFFFu - (uint32_t)cand[c]);
     }
     __syncthreads();
     // thread j < K finishes pick j: every such thread reads all picks (a missing one, which
@@ -369,14 +400,9 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
         st_shared32(p.idx + (size_t)r * p.K + j, ej);
         p.wts[(size_t)r * p.K + j] = v * p.rho;
         if (p.single_row) {
-            p.sched[SCH_EXPERT + u] = ej;
-            p.sched[SCH_OFF + u] = u;
-            p.sched[SCH_FIRST + u] = j;
+            *(int4 *)(p.sched + SCH_REC + 4 * u) = make_int4(ej, u, 1, j);
             p.sched[SCH_PAIRS + u] = j;
-            if (j == 0) {
-                p.sched[SCH_OFF + p.K] = p.K;
-                p.sched[SCH_U] = p.K;
-            }
+            if (j == 0) p.sched[SCH_U] = p.K;
         }
     }
 }
@@ -421,19 +447,15 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
         const int e = tid * per_t + m;
         if (e < E) {
             L.off[e] = run_pairs;
-            if (L.cnt[e] > 0) {
-                p.sched[SCH_EXPERT + run_slots] = e;
-                p.sched[SCH_OFF + run_slots] = run_pairs;
-                L.slot[e] = run_slots;
-                ++run_slots;
-            }
+            L.slot[e] = run_slots;
+            run_slots += L.cnt[e] > 0;
             run_pairs += L.cnt[e];
         }
     }
-    if (tid == WG_THREADS - 1) {
-        p.sched[SCH_U] = run_slots;
-        p.sched[SCH_OFF + run_slots] = run_pairs;
-    }
+    if (tid == WG_THREADS - 1) p.sched[SCH_U] = run_slots;
+    // slots past U (up to the slots the item grid enumerates) are marked empty
+    const int U = L.scan[WG_THREADS - 1] >> 16, umax = E < NP ? E : NP;
+    for (int u = U + tid; u < umax; u += WG_THREADS) *(int4 *)(p.sched + SCH_REC + 4 * u) = make_int4(-1, 0, 0, 0);
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) {
         const int e = ld_shared32(p.idx + i);
@@ -449,7 +471,7 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             while (b >= 0 && L.pairs[o + b] > v) { L.pairs[o + b + 1] = L.pairs[o + b]; --b; }
             L.pairs[o + b + 1] = v;
         }
-        if (n > 0) p.sched[SCH_FIRST + L.slot[e]] = L.pairs[o];
+        if (n > 0) *(int4 *)(p.sched + SCH_REC + 4 * L.slot[e]) = make_int4(e, o, n, L.pairs[o]);
     }
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) p.sched[SCH_PAIRS + i] = L.pairs[i];
@@ -656,11 +678,15 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
 // ------------------------------------------------------------------ routed experts (4-bit)
 
 // LDS of one expert item: a block of NB output rows' codes, scales and biases (NB chosen on
-// the host so that they fit).
+// the host so that they fit), and the current pair's input row as fp32 with its sums per
+// chunk of 32. XMAX: the widest input row (2048, or 6144 in the wide variant).
+template <int XMAX>
 struct ExpertLds {
     uint4 q[EXPERT_LDS_CODES / 16];
     uint16_t s[EXPERT_LDS_SCALES / 2];
     uint16_t b[EXPERT_LDS_SCALES / 2];
+    float x[XMAX];          // input row (its bf16 bits are first staged in the upper half)
+    float xs[XMAX / 32];    // sum of each chunk of 32 inputs, in k order
 };
 
 // Copy `units` 16-byte units from global src to LDS dst with direct global->LDS loads
@@ -674,26 +700,52 @@ __device__ __forceinline__ void stage_lds(const uint4 *src, uint4 *dst, int unit
     }
 }
 
+// The staged input row (Kin 16-bit values in the upper half of L.x) to fp32 in place, and
+// its chunk sums. Every thread reads its values before any thread writes (barrier between).
+template <int XMAX>
+__device__ __forceinline__ void expand_x(const LayerParams &p, ExpertLds<XMAX> &L, int Kin) {
+    const uint16_t *xb = (const uint16_t *)(L.x + XMAX / 2);
+    constexpr int PER = XMAX / WG_THREADS;
+    float v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * WG_THREADS;
+        v[i] = k < Kin ? act2f(p.act_f16, xb[k]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * WG_THREADS;
+        if (k < Kin) L.x[k] = v[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < (Kin >> 5); c += WG_THREADS) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sum = sum + L.x[32 * c + i];
+        L.xs[c] = sum;
+    }
+    __syncthreads();
+}
+
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
-// pair (row, pick) of that slot. The block's 4-bit codes, scales and biases are first staged
-// in LDS (all the item's weight bytes in flight at once; each is read from HBM once, whatever
-// the number of rows). Each output row's inputs are split in chunks of 32 (16 bytes of
-// codes); a row is handled by Cp lanes (Cp = chunks rounded up to a power of two, at most
-// 64; NCH chunks per lane when there are more than 64).
-template <int NCH, bool UP>
-__device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds &L) {
+// pair (row, pick) of that slot. The block's 4-bit codes, scales and biases and the first
+// pair's input row are staged in LDS (all in flight at once; every weight byte is read from
+// HBM once, whatever the number of rows). Each output row's inputs are cut in chunks of 32
+// (16 bytes of codes); 8 lanes share a row, lane s taking chunks s, s + 8, ..., so a wave
+// covers 8 rows per pass and each lane adds acc += scale * sum(q * x) + bias * sum(x) per
+// chunk, in chunk order; the 8 lanes are then joined by a butterfly (4, 2, 1).
+template <bool UP, int XMAX>
+__device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // the number of slots and the slot's record: independent loads (slots past U hold stale
-    // entries, which are not used)
+    // the number of slots and the slot's record: independent loads
     const int U = p.sched[SCH_U];
-    const int e = p.sched[SCH_EXPERT + slot];
-    const int off = p.sched[SCH_OFF + slot];
-    const int off1 = p.sched[SCH_OFF + slot + 1];
-    int pr = p.sched[SCH_FIRST + slot];
-    const int R = off1 - off;
+    const int4 rec = *(const int4 *)(p.sched + SCH_REC + 4 * slot);
+    const int e = rec.x, off = rec.y, R = rec.z;
+    int pr = rec.w;
     const int NP = p.rows * p.K;
-    if (slot >= U) return U;
-    if (e < 0 || e >= p.E || off < 0 || R < 1 || off1 > NP || pr < 0 || pr >= NP) {   // never for a valid schedule
+    if (e == -1) return U;   // no expert in this slot for this pass
+    if (e < 0 || e >= p.E || off < 0 || R < 1 || off + R > NP || pr < 0 || pr >= NP) {   // never for a valid schedule
         if (threadIdx.x == 0) atomicOr(p.err, 4u);
         return 0;
     }
@@ -705,70 +757,44 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     const uint32_t *Q = (UP ? p.up_q : p.dn_q) + ((size_t)e * N + n0) * qrow;
     const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G64;
     const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G64;
+    const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
+    auto xrow = [&](int q) { return xin + (UP ? (size_t)(q / p.K) * Kin : (size_t)q * Kin); };
+    uint4 *xstage = (uint4 *)(L.x + XMAX / 2);
     stage_lds((const uint4 *)Q, L.q, NB * C);
     stage_lds((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
     stage_lds((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
-
-    int Cp = 1;
-    while (Cp < C && Cp < 64) Cp <<= 1;
-    const int rpp = 64 / Cp;
-    const int lrow = lane / Cp, c0 = lane % Cp;
-    const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
-    // the first pair's input chunk is loaded while the weights stream in
-    uint4 xr[4] = {};
-    if (NCH == 1 && c0 < C) {
-        const uint16_t *xrow = xin + (UP ? (size_t)(pr / p.K) * Kin : (size_t)pr * Kin);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) xr[q4] = ((const uint4 *)(xrow + 32 * c0))[q4];
-    }
+    stage_lds((const uint4 *)xrow(pr), xstage, Kin >> 3);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    const int s8 = lane & 7, r8 = lane >> 3;
+    constexpr int RPL = EXPERT_MAX_BLOCK / (8 * WG_THREADS / 64);   // rows per lane at most
     for (int r = 0; r < R; ++r) {
         if (r > 0) {
             pr = p.sched[SCH_PAIRS + off + r];
             if (pr < 0 || pr >= NP) pr = NP - 1;
+            __syncthreads();   // every lane is done with the previous row
+            stage_lds((const uint4 *)xrow(pr), xstage, Kin >> 3);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
-        const uint16_t *xrow = xin + (UP ? (size_t)(pr / p.K) * Kin : (size_t)pr * Kin);
-        if (NCH == 1 && r > 0 && c0 < C) {
+        expand_x(p, L, Kin);
+        float acc[RPL];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) xr[q4] = ((const uint4 *)(xrow + 32 * c0))[q4];
-        }
-        // this lane's input chunks: summed, and with one chunk per lane also kept in
-        // registers (fp32); with more they are re-read from cache for every output row
-        float xf[NCH == 1 ? 32 : 1];
-        float xs[NCH];
+        for (int j = 0; j < RPL; ++j) acc[j] = 0.0f;
+        for (int c = s8; c < C; c += 8) {
+            const float4 *xv4 = (const float4 *)(L.x + 32 * c);
+            float xf[32];
 #pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-            const int c = c0 + 64 * m;
-            float t[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) t[i] = 0.0f;
-            if (c < C) {
-                if constexpr (NCH == 1) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, xr[q4], &t[8 * q4]);
-                } else {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], &t[8 * q4]);
-                }
+            for (int q = 0; q < 8; ++q) {
+                const float4 t = xv4[q];
+                xf[4 * q] = t.x; xf[4 * q + 1] = t.y; xf[4 * q + 2] = t.z; xf[4 * q + 3] = t.w;
             }
-            float sum = 0.0f;
+            const float xsum = L.xs[c];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) sum = sum + t[i];
-            xs[m] = sum;
-            if constexpr (NCH == 1) {
-#pragma unroll
-                for (int i = 0; i < 32; ++i) xf[i] = t[i];
-            }
-        }
-        for (int nb = wave * rpp; nb < NB; nb += (WG_THREADS / 64) * rpp) {
-            const int nl = nb + lrow;                 // row within the block
-            float acc = 0.0f;
-#pragma unroll
-            for (int m = 0; m < NCH; ++m) {
-                const int c = c0 + 64 * m;
-                if (nl < NB && c < C) {
+            for (int j = 0; j < RPL; ++j) {
+                const int nl = j * (8 * WG_THREADS / 64) + wave * 8 + r8;   // row within the block
+                if (nl < NB) {
                     const uint4 qv = L.q[nl * C + c];
                     const float sc = bf2f(L.s[nl * G64 + (c >> 1)]);
                     const float bi = bf2f(L.b[nl * G64 + (c >> 1)]);
@@ -776,26 +802,28 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
                     float part = 0.0f;
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        float qf[8], xv[8];
+                        float qf[8];
                         nibbles8(qw[q4], qf);
-                        if constexpr (NCH == 1) {
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) xv[i] = xf[8 * q4 + i];
-                        } else {
-                            unpack8(p.act_f16, ((const uint4 *)(xrow + 32 * c))[q4], xv);
-                        }
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qf[i], xv[i], part);
+                        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qf[i], xf[8 * q4 + i], part);
                     }
-                    acc = __builtin_fmaf(sc, part, acc);
-                    acc = __builtin_fmaf(bi, xs[m], acc);
+                    acc[j] = __builtin_fmaf(sc, part, acc[j]);
+                    acc[j] = __builtin_fmaf(bi, xsum, acc[j]);
                 }
             }
-            for (int d = Cp >> 1; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-            if (c0 == 0 && nl < NB) {
+        }
+#pragma unroll
+        for (int j = 0; j < RPL; ++j) {
+            float v = acc[j];
+            v = v + __shfl_xor(v, 4, 64);
+            v = v + __shfl_xor(v, 2, 64);
+            v = v + __shfl_xor(v, 1, 64);
+            const int nl = j * (8 * WG_THREADS / 64) + wave * 8 + r8;
+            if (s8 == 0 && nl < NB) {
                 const int n = n0 + nl;
-                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, acc)));
-                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(p.act_f16, acc));
+                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, v)));
+                else if (p.inline_comb) p.eout[(size_t)pr * p.D + n] = f2act(p.act_f16, v);   // read next launch
+                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(p.act_f16, v));   // combined in this one
             }
         }
     }
@@ -826,14 +854,17 @@ constexpr int NW = WG_THREADS / 64;    // waves of a workgroup
 
 // Kernels: each covers the stages [FIRST, LAST] (the host launches any contiguous range of
 // items inside them); WIDE selects the expert variant for inputs wider than 2048.
-template <int FIRST, int LAST>
+struct NoLds {};
+
+template <int FIRST, int LAST, bool WIDE>
 struct StageLds {
     static constexpr bool has(int s) { return FIRST <= s && s <= LAST; }
+    static constexpr bool dense = has(ST_FC1) || has(ST_SHUP) || has(ST_SHDN_A) || has(ST_SHDN_B) || has(ST_FC2);
     union U {
-        DenseLds<NW> dense;
-        RouteLds<WG_THREADS> route;
-        SchedLds sched;
-        ExpertLds ex;
+        typename std::conditional<dense, DenseLds<NW>, NoLds>::type dense;
+        typename std::conditional<has(ST_GATE) || has(ST_ROUTE), RouteLds<WG_THREADS>, NoLds>::type route;
+        typename std::conditional<has(ST_ROUTE), SchedLds, NoLds>::type sched;
+        typename std::conditional<has(ST_UP) || has(ST_DOWN), ExpertLds<WIDE ? 6144 : 2048>, NoLds>::type ex;
     };
 };
 
@@ -865,10 +896,10 @@ __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT 
                                  lds.dense, s_flag);
     } else if constexpr (S == ST_UP) {
         const int slot = local / p.up_blocks, blk = local % p.up_blocks;
-        expert_item<WIDE ? 3 : 1, true>(p, slot, blk, lds.ex);
+        expert_item<true>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_DOWN) {
         const int slot = local / p.dn_blocks, blk = local % p.dn_blocks;
-        const int U = expert_item<WIDE ? 3 : 1, false>(p, slot, blk, lds.ex);
+        const int U = expert_item<false>(p, slot, blk, lds.ex);
         if (slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, s_flag))
             combine_block(p, blk * p.dn_nb, p.dn_nb);
     } else if constexpr (S == ST_FC2) {
@@ -895,7 +926,7 @@ __device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds
 template <int FIRST, int LAST, bool WIDE>
 __global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(FIRST == ST_FC2 ? 2 : 4, 8)))
 moe_stage_kernel(LayerParams p, int lo, int hi, int rev) {
-    __shared__ typename StageLds<FIRST, LAST>::U lds;
+    __shared__ typename StageLds<FIRST, LAST, WIDE>::U lds;
     __shared__ int s_flag;
     const int it = rev ? hi - 1 - (int)blockIdx.x : lo + (int)blockIdx.x;
     if (it >= hi) return;

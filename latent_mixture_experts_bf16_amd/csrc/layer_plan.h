@@ -38,24 +38,22 @@ enum : int {
     CTR_DENSE = 2048,
 };
 
-// schedule block (int32) in the workspace: [0] = U (distinct experts picked),
-// [SCH_EXPERT + u] = expert of slot u (increasing expert id), [SCH_OFF + u] = offset of
-// slot u's pairs (U + 1 entries), [SCH_FIRST + u] = slot u's first pair (a copy, so that an
-// item finds it without a dependent load), [SCH_PAIRS + i] = pair row * top_k + pick,
-// sorted by (expert, row).
+// schedule block (int32) in the workspace: [SCH_U] = U (distinct experts picked); the
+// record of slot u at [SCH_REC + 4u] = {expert, offset of its pairs, number of pairs, first
+// pair} (slots in increasing expert id; a slot past U holds expert -1), so that an item
+// reads its slot with one 16-byte load; [SCH_PAIRS + i] = pair row * top_k + pick, sorted by
+// (expert, row).
 enum : int {
     SCH_U = 0,
-    SCH_EXPERT = 1,
-    SCH_OFF = SCH_EXPERT + MAX_EXPERTS,
-    SCH_FIRST = SCH_OFF + MAX_EXPERTS + 1,
-    SCH_PAIRS = SCH_FIRST + MAX_EXPERTS,
+    SCH_REC = 4,
+    SCH_PAIRS = SCH_REC + 4 * MAX_EXPERTS,
     SCH_COUNT = SCH_PAIRS + MAX_ROWS * MAX_TOPK,
 };
 
-constexpr int WG_THREADS = 512;   // 8 waves of 64 in every item
-constexpr int EXPERT_LDS_CODES = 16384;   // LDS bytes for one expert item's codes
-constexpr int EXPERT_LDS_SCALES = 1024;   // ... and for its scales (and again its biases)
-constexpr int EXPERT_MAX_BLOCK = 32;      // output rows of one expert item at most
+constexpr int WG_THREADS = 256;   // 4 waves of 64 in every item (four items per CU at once)
+constexpr int EXPERT_LDS_CODES = 32768;   // LDS bytes for one expert item's codes
+constexpr int EXPERT_LDS_SCALES = 2048;   // ... and for its scales (and again its biases)
+constexpr int EXPERT_MAX_BLOCK = 64;      // output rows of one expert item at most
 constexpr int DENSE_TILE = 16;    // outputs per dense item
 
 struct LayerParams {

@@ -80,7 +80,7 @@ static const char *dt_name(int dt) {
     }
 }
 
-// Output rows of one expert item: the largest power of two <= 32 whose codes, scales and
+// Output rows of one expert item: the largest power of two <= 64 whose codes, scales and
 // biases fit the item's LDS, that divides N, and whose scales fill whole 16-byte units.
 static int expert_block(int N, int Kin) {
     for (int nb = EXPERT_MAX_BLOCK; nb > 1; nb >>= 1) {
@@ -167,6 +167,8 @@ static int check_tensor(const char *name, const moe_tensor &t, int dtype, int nd
         }
         st *= shape[i];
     }
+    if ((uintptr_t)t.data & 15)   // the kernels read every tensor with 16-byte loads
+        return fail(MOE_ERR_LAYOUT, "%s: data pointer not 16-byte aligned", name);
     return MOE_OK;
 }
 
@@ -237,9 +239,9 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Items per 16-output tile of a dense projection over K inputs: each item takes K / splits
 // inputs (a multiple of 128); the last of a tile's items to finish adds their partial sums.
-// Up to K = 4096 a tile is one item (128 KB of weights, all in flight at once); wider
-// projections are cut in 4096-input parts.
-static int dense_splits_host(int K) { return K > 4096 && K % 4096 == 0 ? K / 4096 : 1; }
+// Tiles of 4096 inputs and more are cut in parts of 2048 (64 KB of weights, all in flight
+// at once), so that a launch's items fit the machine in one round and spread evenly.
+static int dense_splits_host(int K) { return K >= 4096 && K % 2048 == 0 ? K / 2048 : 1; }
 
 static int setup_workspace(moe_latent *h) {
     const moe_latent_config &c = h->cfg;
@@ -466,15 +468,23 @@ static void plan_items(LayerParams &p, int rows) {
     for (int s = 0; s < NSTAGE; ++s) p.item_base[s + 1] = p.item_base[s] + n[s];
 }
 
-extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
+// The checks of a forward's arguments (shared by the forward and its launch groups).
+static int check_io(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
     if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
     if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
+    if (((uintptr_t)hidden_in | (uintptr_t)out) & 15)
+        return fail(MOE_ERR_LAYOUT, "hidden_in and out must be 16-byte aligned");
     if (rows < 1 || rows > h->cfg.max_rows)
         return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
     const size_t bytes = (size_t)rows * h->cfg.hidden * 2;
     const char *a = (const char *)hidden_in, *b = (const char *)out;
     if (a != b && a < b + bytes && b < a + bytes)
         return fail(MOE_ERR_ALIAS, "out partially overlaps hidden_in");
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
+    if (int rc = check_io(h, rows, hidden_in, out)) return rc;
     LayerParams p = h->base;
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
@@ -488,10 +498,7 @@ extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hid
 
 extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
                                        int32_t group) {
-    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
-    if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
-    if (rows < 1 || rows > h->cfg.max_rows)
-        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
+    if (int rc = check_io(h, rows, hidden_in, out)) return rc;
     LayerParams p = h->base;
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;

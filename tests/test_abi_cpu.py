@@ -112,6 +112,8 @@ def test_config_refusals(over, code, word):
     ("corr_bias", {"ptr": 0}, "MOE_ERR_MISSING_TENSOR", "corr_bias"),
     ("up_scales", {"shape": [240, 2048, 8]}, "MOE_ERR_LAYOUT", "up_scales"),
     ("shared_down", {"strides": [8192, 1]}, "MOE_ERR_LAYOUT", "shared_down"),
+    ("up_q", {"ptr": FAKE + 4}, "MOE_ERR_LAYOUT", "16-byte aligned"),
+    ("fc2_w", {"ptr": FAKE + 2}, "MOE_ERR_LAYOUT", "16-byte aligned"),
 ])
 def test_tensor_refusals(name, over, code, word):
     rc, h, msg = _create(BOLT, **{name: over})
