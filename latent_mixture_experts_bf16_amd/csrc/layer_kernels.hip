@@ -9,7 +9,8 @@
 //   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
 //              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]
 // One workgroup of 4 waves runs one item; a launch's items are sized (about 32-64 KB of
-// weights each) so that all of them are resident at once, four per compute unit.
+// weights each) so that all of them are resident at once (up to four per compute unit,
+// three in the expert launches, whose LDS holds a 32 KB block of codes).
 //
 // Arithmetic of each stage (TensorFold pull request 1038, «What's in it»: gate gemv ->
 // route top-k -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj -> +
@@ -24,7 +25,9 @@
 //            top groups, then top-k experts by (score desc, id asc), NaN lowest; weights
 //            = (s / sum of s in pick order) * rho.
 //   dense    (fc1, shared up/down, fc2): bf16 MFMA 16x16x32 tiles, K split over the 4
-//            waves of a workgroup and joined in a fixed order. A row's result never depends
+//            waves of a workgroup and joined in a fixed order (projections of 4096 inputs
+//            and more are also split over items, the last of which adds their partial
+//            sums in split order). A row's result never depends
 //            on the other rows of the pass (each output row of a tile is its own column of
 //            the MFMA), so a multi-row pass equals its one-row passes bit for bit.
 //   experts  4-bit affine weights w = q*scale + bias (groups of 64 along k); per 32 inputs
@@ -63,7 +66,11 @@ __device__ __forceinline__ uint16_t f2h(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-__device__ __forceinline__ float act2f(int f16, uint32_t h) { return f16 ? h2f(h) : bf2f(h); }
+// both conversions, then a select: no branch per element
+__device__ __forceinline__ float act2f(int f16, uint32_t h) {
+    const float a = h2f(h), b = bf2f(h);
+    return f16 ? a : b;
+}
 __device__ __forceinline__ uint16_t f2act(int f16, float v) { return f16 ? f2h(v) : f2bf(v); }
 __device__ __forceinline__ float rnd(int f16, float v) { return act2f(f16, f2act(f16, v)); }
 
@@ -82,9 +89,12 @@ __device__ __forceinline__ void unpack8(int f16, uint4 v, float *o) {
     }
 }
 
-// the 8 codes of one word, in k order (lowest nibble first), as fp32
+// the 8 codes of one word, in k order (lowest nibble first), as fp32: the even and the odd
+// nibbles are first masked into bytes, each then converted by a byte-to-float conversion
+// (the empty asm keeps the compiler from re-extracting single nibbles instead)
 __device__ __forceinline__ void nibbles8(uint32_t w, float *q) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(lo), "+v"(hi));
     q[0] = (float)(lo & 0xFFu);
     q[1] = (float)(hi & 0xFFu);
     q[2] = (float)((lo >> 8) & 0xFFu);
@@ -286,12 +296,12 @@ struct RouteLds {
     float s[MAX_EXPERTS];
     float b[MAX_EXPERTS];
     alignas(16) uint64_t key[MAX_EXPERTS];    // rank keys of the biased scores
-    alignas(16) uint64_t ckey[MAX_EXPERTS];   // the candidates' keys (kept groups, in id order)
+    alignas(16) uint64_t ckey[MAX_EXPERTS];   // the candidates' keys
     alignas(16) uint64_t gkey[256];           // rank keys of the group scores
     int rank[MAX_EXPERTS];                    // candidate ranks, summed over counting threads
+    int inr[MAX_EXPERTS];                     // each expert's rank inside its group
     int top[256][2];              // the two best members of each group
     int keep[256];                // 1: the group is kept
-    int gslot[256];               // a kept group's position among the kept groups, else -1
     int picks[MAX_TOPK];
 };
 
@@ -319,55 +329,57 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     if (tid < MAX_TOPK) L.picks[tid] = -1;
     for (int c = tid; c < E; c += NT) L.rank[c] = 0;
     __syncthreads();
-    const uint64_t *cand = L.key;   // candidates: every expert, or those of the kept groups
-    int nc = E;
-    if (p.TG < G) {
-        // the two best members of each group: rank of each expert inside its group
-        for (int e = tid; e < E; e += NT) {
-            const uint64_t k = L.key[e];
-            const int g = e / per;
-            const int rank = count_greater_any(L.key + g * per, per, k);
-            if (rank < 2) L.top[g][rank] = e;
-        }
-        __syncthreads();
+    // every expert's rank inside its group (without group selection: among all experts, which
+    // picks the top_k directly)
+    const bool grouped = p.TG < G;
+    const int gsz = grouped ? per : E;
+    for (int e = tid; e < E; e += NT) {
+        const int g = e / gsz;
+        const int rank = count_greater_any(L.key + g * gsz, gsz, L.key[e]);
+        L.inr[e] = rank;
+        if (grouped && rank < 2) L.top[g][rank] = e;
+        if (!grouped && rank < p.K) L.picks[rank] = e;
+    }
+    __syncthreads();
+    if (grouped) {
         for (int g = tid; g < G; g += NT) {
             const float gam = per > 1 ? L.b[L.top[g][0]] + L.b[L.top[g][1]] : L.b[L.top[g][0]];
             L.gkey[g] = rank_key(gam, g);
         }
         __syncthreads();
-        // kept groups: rank < TG; then each kept group's position among the kept ones
+        // kept groups: rank < TG
         for (int g = tid; g < G; g += NT) L.keep[g] = count_greater(L.gkey, G, L.gkey[g]) < p.TG;
         __syncthreads();
-        for (int g = tid; g < G; g += NT) {
-            int before = 0;
-            for (int h = 0; h < g; ++h) before += L.keep[h];
-            L.gslot[g] = L.keep[g] ? before : -1;
-        }
-        __syncthreads();
+        // candidates: a pick is among the top_k of its own group, so only those members of the
+        // kept groups enter; candidate slot = (kept groups before g) * KK + rank in the group
+        const int KK = p.K < per ? p.K : per;
         for (int e = tid; e < E; e += NT) {
-            const int g = e / per, slot = L.gslot[g];
-            if (slot >= 0) L.ckey[slot * per + (e - g * per)] = L.key[e];
+            const int g = e / per, rank = L.inr[e];
+            if (L.keep[g] && rank < KK) {
+                int before = 0;
+                for (int h = 0; h < g; ++h) before += L.keep[h];
+                L.ckey[before * KK + rank] = L.key[e];
+            }
         }
         __syncthreads();
-        cand = L.ckey;
-        nc = p.TG * per;
+        // the top_k of the candidates: rank among them, counted by T threads per candidate
+        // (each over a contiguous part of the list) and summed in LDS
+        const int nc = p.TG * KK;
+        int T = 1;
+        while (T < 16 && 2 * T * nc <= NT) T *= 2;
+        for (int i = tid; i < nc * T; i += NT) {
+            const int c = i / T, part = i % T;
+            const int lo = part * nc / T, hi = (part + 1) * nc / T;
+            const int cnt = count_greater_any(L.ckey + lo, hi - lo, L.ckey[c]);
+            atomicAdd(&L.rank[c], cnt);
+        }
+        __syncthreads();
+        for (int c = tid; c < nc; c += NT) {
+            const int rank = L.rank[c];
+            if (rank < p.K) L.picks[rank] = (int)(0xFFFFFFFFu - (uint32_t)L.ckey[c]);
+        }
+        __syncthreads();
     }
-    // the top_k candidates: rank among the candidates, counted by T threads per candidate
-    // (each over a contiguous part of the list) and summed in LDS
-    int T = 1;
-    while (T < 16 && 2 * T * nc <= NT) T *= 2;
-    for (int i = tid; i < nc * T; i += NT) {
-        const int c = i / T, part = i % T;
-        const int lo = part * nc / T, hi = (part + 1) * nc / T;
-        const int cnt = count_greater_any(cand + lo, hi - lo, cand[c]);
-        atomicAdd(&L.rank[c], cnt);
-    }
-    __syncthreads();
-    for (int c = tid; c < nc; c += NT) {
-        const int rank = L.rank[c];
-        if (rank < p.K) L.picks[rank] = (int)(0xFFFFFFFFu - (uint32_t)cand[c]);
-    }
-    __syncthreads();
     // thread j < K finishes pick j: every such thread reads all picks (a missing one, which
     // the host checks exclude, counts as expert 0), sums the picked scores in pick order and
     // writes its index and weight; a one-row pass also gets its schedule here, slot u holding
@@ -505,6 +517,36 @@ __device__ __forceinline__ float combine_value(const LayerParams &p, int r, int 
     return ((T[0] + T[4]) + (T[2] + T[6])) + ((T[1] + T[5]) + (T[3] + T[7]));
 }
 
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// The same combine at latent outputs d..d+3 (d a multiple of 4) of row r, the expert outputs
+// written by an earlier launch: one 8-byte load per pick, each output summed exactly as
+// combine_value does.
+__device__ __forceinline__ void combine4(const LayerParams &p, int r, int d, float *out) {
+    float w[MAX_TOPK];
+    uint2 v[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_TOPK; ++j) {
+        const size_t pr = (size_t)r * p.K + (j < p.K ? j : p.K - 1);
+        w[j] = p.wts[pr];
+        v[j] = *(const uint2 *)(p.eout + pr * p.D + d);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float T[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) T[t] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < MAX_TOPK; ++j) {
+            const uint32_t word = i < 2 ? v[j].x : v[j].y;
+            const uint32_t h = i & 1 ? word >> 16 : word & 0xFFFFu;
+            const float t = T[j & 7] + w[j] * act2f(p.act_f16, h);
+            T[j & 7] = j < p.K ? t : T[j & 7];
+        }
+        out[i] = ((T[0] + T[4]) + (T[2] + T[6])) + ((T[1] + T[5]) + (T[3] + T[7]));
+    }
+}
+
 // ------------------------------------------------------------------ dense bf16 tiles (MFMA)
 
 enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
@@ -602,10 +644,12 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
         if (row < p.rows) pre = epi_load(p, row, n0 + 4 * grp);
     }
     if (inl) {
-        for (int i = threadIdx.x; i < kpart; i += NW * 64) {
-            const uint16_t c = f2bf(combine_value<false>(p, 0, kbase + i));
-            L.xc[i] = c;
-            if (tile == 0) p.comb[kbase + i] = c;
+        for (int i = 4 * threadIdx.x; i < kpart; i += 4 * NW * 64) {
+            float c4[4];
+            combine4(p, 0, kbase + i, c4);
+            const uint2 c = {pack2(f2bf(c4[0]), f2bf(c4[1])), pack2(f2bf(c4[2]), f2bf(c4[3]))};
+            *(uint2 *)(L.xc + i) = c;
+            if (tile == 0) *(uint2 *)(p.comb + kbase + i) = c;
         }
         __syncthreads();
     }
@@ -678,15 +722,14 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
 // ------------------------------------------------------------------ routed experts (4-bit)
 
 // LDS of one expert item: a block of NB output rows' codes, scales and biases (NB chosen on
-// the host so that they fit), and the current pair's input row as fp32 with its sums per
-// chunk of 32. XMAX: the widest input row (2048, or 6144 in the wide variant).
+// the host so that they fit), and the current pair's input row (16-bit values). XMAX: the
+// widest input row (2048, or 6144 in the wide variant).
 template <int XMAX>
 struct ExpertLds {
     uint4 q[EXPERT_LDS_CODES / 16];
     uint16_t s[EXPERT_LDS_SCALES / 2];
     uint16_t b[EXPERT_LDS_SCALES / 2];
-    float x[XMAX];          // input row (its bf16 bits are first staged in the upper half)
-    float xs[XMAX / 32];    // sum of each chunk of 32 inputs, in k order
+    uint4 x[XMAX / 8];
 };
 
 // Copy `units` 16-byte units from global src to LDS dst with direct global->LDS loads
@@ -700,42 +743,42 @@ __device__ __forceinline__ void stage_lds(const uint4 *src, uint4 *dst, int unit
     }
 }
 
-// The staged input row (Kin 16-bit values in the upper half of L.x) to fp32 in place, and
-// its chunk sums. Every thread reads its values before any thread writes (barrier between).
-template <int XMAX>
-__device__ __forceinline__ void expand_x(const LayerParams &p, ExpertLds<XMAX> &L, int Kin) {
-    const uint16_t *xb = (const uint16_t *)(L.x + XMAX / 2);
-    constexpr int PER = XMAX / WG_THREADS;
-    float v[PER];
+// Sum each of the R values of v over the P lanes of a lane group (P, R powers of two,
+// R <= P <= 64; t = lane index in the group). Halving steps first: at distance d the lanes
+// with bit d set keep the upper half of their values and add their partner's, the others
+// the lower half; then plain butterflies. Afterwards v[0] of lane t holds the full sum of
+// value row(t) = the bits of t at P/2, P/4, ..., P/R read high to low. Fixed order.
+template <int R>
+__device__ __forceinline__ int reduce_rows(float *v, int P, int t) {
+    int n = R, d = P >> 1, row = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int k = threadIdx.x + i * WG_THREADS;
-        v[i] = k < Kin ? act2f(p.act_f16, xb[k]) : 0.0f;
-    }
-    __syncthreads();
+    for (int step = 0; (1 << step) < R; ++step) {
+        n >>= 1;
+        const bool upper = (t & d) != 0;
+        row = 2 * row + (upper ? 1 : 0);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int k = threadIdx.x + i * WG_THREADS;
-        if (k < Kin) L.x[k] = v[i];
+        for (int i = 0; i < R / 2; ++i) {
+            if (i < n) {
+                const float send = upper ? v[i] : v[i + n];
+                const float keep = upper ? v[i + n] : v[i];
+                v[i] = keep + __shfl_xor(send, d, 64);
+            }
+        }
+        d >>= 1;
     }
-    __syncthreads();
-    for (int c = threadIdx.x; c < (Kin >> 5); c += WG_THREADS) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sum = sum + L.x[32 * c + i];
-        L.xs[c] = sum;
-    }
-    __syncthreads();
+    for (; d >= 1; d >>= 1) v[0] = v[0] + __shfl_xor(v[0], d, 64);
+    return row;
 }
 
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
 // pair (row, pick) of that slot. The block's 4-bit codes, scales and biases and the first
 // pair's input row are staged in LDS (all in flight at once; every weight byte is read from
 // HBM once, whatever the number of rows). Each output row's inputs are cut in chunks of 32
-// (16 bytes of codes); 8 lanes share a row, lane s taking chunks s, s + 8, ..., so a wave
-// covers 8 rows per pass and each lane adds acc += scale * sum(q * x) + bias * sum(x) per
-// chunk, in chunk order; the 8 lanes are then joined by a butterfly (4, 2, 1).
-template <bool UP, int XMAX>
+// (16 bytes of codes). A group of P lanes (P = chunks rounded up to a power of two, at most
+// 64) covers the chunks of R output rows, lane t taking chunks t, t + P, ...: it keeps its
+// chunk's inputs in registers and adds, per row and chunk, scale * sum(q * x) + bias *
+// sum(x); reduce_rows then joins the P lanes of each row.
+template <bool UP, int XMAX, bool F16>
 __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     // the number of slots and the slot's record: independent loads
@@ -759,71 +802,87 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G64;
     const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
     auto xrow = [&](int q) { return xin + (UP ? (size_t)(q / p.K) * Kin : (size_t)q * Kin); };
-    uint4 *xstage = (uint4 *)(L.x + XMAX / 2);
-    stage_lds((const uint4 *)Q, L.q, NB * C);
+    int P = 1;
+    while (P < C && P < 64) P <<= 1;
+    const int gpw = 64 / P, t = lane % P, grp = lane / P;
+    const int NG = (WG_THREADS / 64) * gpw;   // lane groups of the item
+    int RG = NB / NG;                          // rows per lane group
+    if (RG < 1) RG = 1;
+    const int nch = (C + P - 1) / P;
+    const int RB = RG < 4 ? RG : 4;            // rows per batch
+    // batch b of group g covers rows b * 4 * NG + 4 g + (0..3)
     stage_lds((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
     stage_lds((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
-    stage_lds((const uint4 *)xrow(pr), xstage, Kin >> 3);
+    stage_lds((const uint4 *)xrow(pr), L.x, Kin >> 3);
+    stage_lds((const uint4 *)Q, L.q, NB * C);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-
-    const int s8 = lane & 7, r8 = lane >> 3;
-    constexpr int RPL = EXPERT_MAX_BLOCK / (8 * WG_THREADS / 64);   // rows per lane at most
+    auto row_of = [&](int rb, int ii) { return RB == 4 ? (rb / 4) * 4 * NG + 4 * (wave * gpw + grp) + ii
+                                                       : (wave * gpw + grp) * RG + rb + ii; };
     for (int r = 0; r < R; ++r) {
         if (r > 0) {
             pr = p.sched[SCH_PAIRS + off + r];
             if (pr < 0 || pr >= NP) pr = NP - 1;
-            __syncthreads();   // every lane is done with the previous row
-            stage_lds((const uint4 *)xrow(pr), xstage, Kin >> 3);
+            __syncthreads();   // every lane is done with the previous input row
+            stage_lds((const uint4 *)xrow(pr), L.x, Kin >> 3);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        expand_x(p, L, Kin);
-        float acc[RPL];
+        // the lane's input chunk (one chunk per lane unless the rows are wider than 2048)
+        float xf[32], xs = 0.0f;
+        auto load_x = [&](int c) {
 #pragma unroll
-        for (int j = 0; j < RPL; ++j) acc[j] = 0.0f;
-        for (int c = s8; c < C; c += 8) {
-            const float4 *xv4 = (const float4 *)(L.x + 32 * c);
-            float xf[32];
+            for (int q4 = 0; q4 < 4; ++q4) unpack8(F16, L.x[4 * c + q4], &xf[8 * q4]);
+            xs = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 t = xv4[q];
-                xf[4 * q] = t.x; xf[4 * q + 1] = t.y; xf[4 * q + 2] = t.z; xf[4 * q + 3] = t.w;
-            }
-            const float xsum = L.xs[c];
+            for (int i = 0; i < 32; ++i) xs = xs + xf[i];
+        };
+        if (nch == 1 && t < C) load_x(t);
+        for (int rb = 0; rb < RG; rb += 4) {
+            // 4 rows at a time, without branches (rows past NB read row NB - 1, dropped below)
+            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int m = 0; m < nch; ++m) {
+                const int c = t + P * m;
+                if (c < C) {
+                    if (nch > 1) load_x(c);
+                    uint4 qv[4];
+                    float sc[4], bi[4];
 #pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                const int nl = j * (8 * WG_THREADS / 64) + wave * 8 + r8;   // row within the block
-                if (nl < NB) {
-                    const uint4 qv = L.q[nl * C + c];
-                    const float sc = bf2f(L.s[nl * G64 + (c >> 1)]);
-                    const float bi = bf2f(L.b[nl * G64 + (c >> 1)]);
-                    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-                    float part = 0.0f;
+                    for (int ii = 0; ii < 4; ++ii) {
+                        int nl = row_of(rb, ii);
+                        nl = nl < NB ? nl : NB - 1;
+                        qv[ii] = L.q[nl * C + c];
+                        sc[ii] = bf2f(L.s[nl * G64 + (c >> 1)]);
+                        bi[ii] = bf2f(L.b[nl * G64 + (c >> 1)]);
+                    }
+                    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        float qf[8];
-                        nibbles8(qw[q4], qf);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(qf[i], xf[8 * q4 + i], part);
+                        for (int ii = 0; ii < 4; ++ii) {
+                            const uint32_t w = q4 == 0 ? qv[ii].x : q4 == 1 ? qv[ii].y : q4 == 2 ? qv[ii].z : qv[ii].w;
+                            float qf[8];
+                            nibbles8(w, qf);
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) part[ii] = __builtin_fmaf(qf[k], xf[8 * q4 + k], part[ii]);
+                        }
                     }
-                    acc[j] = __builtin_fmaf(sc, part, acc[j]);
-                    acc[j] = __builtin_fmaf(bi, xsum, acc[j]);
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        v[ii] = __builtin_fmaf(sc[ii], part[ii], v[ii]);
+                        v[ii] = __builtin_fmaf(bi[ii], xs, v[ii]);
+                    }
                 }
             }
-        }
-#pragma unroll
-        for (int j = 0; j < RPL; ++j) {
-            float v = acc[j];
-            v = v + __shfl_xor(v, 4, 64);
-            v = v + __shfl_xor(v, 2, 64);
-            v = v + __shfl_xor(v, 1, 64);
-            const int nl = j * (8 * WG_THREADS / 64) + wave * 8 + r8;
-            if (s8 == 0 && nl < NB) {
+            const int rr = RB == 4 ? reduce_rows<4>(v, P, t) : RB == 2 ? reduce_rows<2>(v, P, t) : reduce_rows<1>(v, P, t);
+            // lane t holds row rb + rr; the lowest lane of those holding it stores it
+            const int nl = row_of(rb, rr);
+            if ((t & (P / RB - 1)) == 0 && nl < NB && rb + rr < RG) {
                 const int n = n0 + nl;
-                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(p.act_f16, relu_sq(p.act_f16, rnd(p.act_f16, v)));
-                else if (p.inline_comb) p.eout[(size_t)pr * p.D + n] = f2act(p.act_f16, v);   // read next launch
-                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(p.act_f16, v));   // combined in this one
+                const float acc = v[0];
+                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(F16, relu_sq(F16, rnd(F16, acc)));
+                else if (p.inline_comb) p.eout[(size_t)pr * p.D + n] = f2act(F16, acc);   // read next launch
+                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(F16, acc));   // combined in this one
             }
         }
     }
@@ -856,6 +915,9 @@ constexpr int NW = WG_THREADS / 64;    // waves of a workgroup
 // items inside them); WIDE selects the expert variant for inputs wider than 2048.
 struct NoLds {};
 
+// widest expert input row of a kernel variant
+#define XMAX_OF(wide) ((wide) ? 6144 : 2048)
+
 template <int FIRST, int LAST, bool WIDE>
 struct StageLds {
     static constexpr bool has(int s) { return FIRST <= s && s <= LAST; }
@@ -864,7 +926,7 @@ struct StageLds {
         typename std::conditional<dense, DenseLds<NW>, NoLds>::type dense;
         typename std::conditional<has(ST_GATE) || has(ST_ROUTE), RouteLds<WG_THREADS>, NoLds>::type route;
         typename std::conditional<has(ST_ROUTE), SchedLds, NoLds>::type sched;
-        typename std::conditional<has(ST_UP) || has(ST_DOWN), ExpertLds<WIDE ? 6144 : 2048>, NoLds>::type ex;
+        typename std::conditional<has(ST_UP) || has(ST_DOWN), ExpertLds<XMAX_OF(WIDE)>, NoLds>::type ex;
     };
 };
 
@@ -896,10 +958,12 @@ __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT 
                                  lds.dense, s_flag);
     } else if constexpr (S == ST_UP) {
         const int slot = local / p.up_blocks, blk = local % p.up_blocks;
-        expert_item<true>(p, slot, blk, lds.ex);
+        if (p.act_f16) expert_item<true, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex);
+        else expert_item<true, XMAX_OF(WIDE), false>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_DOWN) {
         const int slot = local / p.dn_blocks, blk = local % p.dn_blocks;
-        const int U = expert_item<false>(p, slot, blk, lds.ex);
+        const int U = p.act_f16 ? expert_item<false, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex)
+                                : expert_item<false, XMAX_OF(WIDE), false>(p, slot, blk, lds.ex);
         if (slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, s_flag))
             combine_block(p, blk * p.dn_nb, p.dn_nb);
     } else if constexpr (S == ST_FC2) {
@@ -920,11 +984,17 @@ __device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds
     }
 }
 
+// Waves per SIMD the register allocation aims for: what the kernel's LDS allows (expert
+// stages: 3), and 2 for fc2 (one item per compute unit).
+constexpr int waves_target(int first, int last, bool wide) {
+    return first == ST_FC2 ? 2 : (first <= ST_DOWN && last >= ST_UP) ? 3 : 4;
+}
+
 // Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST]; with rev
 // set, workgroup 0 takes the last item (the hardware dispatches workgroups in index order, so
 // the later stage's items start first).
 template <int FIRST, int LAST, bool WIDE>
-__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(FIRST == ST_FC2 ? 2 : 4, 8)))
+__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_target(FIRST, LAST, WIDE), 8)))
 moe_stage_kernel(LayerParams p, int lo, int hi, int rev) {
     __shared__ typename StageLds<FIRST, LAST, WIDE>::U lds;
     __shared__ int s_flag;
