@@ -250,7 +250,9 @@ static int setup_workspace(moe_latent *h) {
     LayerParams &p = h->base;
     p.ks_fc1 = dense_splits_host((int)H);
     p.ks_shup = dense_splits_host((int)H);
-    p.ks_shdn = dense_splits_host(SI ? (int)SI : 1);
+    // the shared down projection fills the expert launches, where whole 128 KB tiles (no
+    // partial sums) measured faster
+    p.ks_shdn = SI > 4096 && SI % 4096 == 0 ? (int)(SI / 4096) : 1;
     p.ks_fc2 = dense_splits_host(L ? (int)L : 1);
     // dense tile counters after the fixed ones
     p.ctr_fc1 = CTR_DENSE;
