@@ -390,49 +390,63 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
     return MOE_OK;
 }
 
-// Launch the items of stages [first, last] on stream st with the kernel covering them; rev:
-// the last stage's items are dispatched first.
-template <int KF, int KL, bool WIDE>
-static void launch_range(const LayerParams &p, int first, int last, hipStream_t st, int rev = 0) {
-    const int lo = p.item_base[first], hi = p.item_base[last + 1];
-    if (hi > lo)
-        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, rev);
-}
+// One launch of a forward: the items of stages [first, last], run by the kernel instance
+// `kernel` (its template range covers them); rev: the last stage's items are dispatched
+// first.
+enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2 };
+struct Launch {
+    int first, last, kernel, rev;
+};
 
-// The launches of one forward, in order (see layer_kernels.hip): all of them (g == -1),
-// launch g only (g >= 0), or none (g == -2, to count them). Returns the number of launches.
-static int launch_plan(const LayerParams &p, hipStream_t st, int g) {
-    const bool wide = p.D > 2048 || p.I > 2048;
+// The launches of one forward, in order (see layer_kernels.hip). Returns their number.
+static int plan_launches(const LayerParams &p, Launch *out) {
     int n = 0;
-    auto go = [&](auto fn) { if (g == -1 || g == n) fn(); ++n; };
-    go([&] { launch_range<ST_GATE, ST_SHUP, false>(p, ST_GATE, ST_SHUP, st); });
+    auto add = [&](int f, int l, int k, int rev = 0) { out[n++] = Launch{f, l, k, rev}; };
     if (p.single_row) {
         // the routed expert items (on the critical path) are dispatched before the shared
         // expert's down items that fill the rest of the machine
-        go([&] {
-            if (wide) launch_range<ST_ROUTE, ST_UP, true>(p, ST_ROUTE, ST_UP, st, 1);
-            else launch_range<ST_ROUTE, ST_UP, false>(p, ST_ROUTE, ST_UP, st, 1);
-        });
-        go([&] {
-            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_SHDN_B, ST_DOWN, st, 1);
-            else launch_range<ST_UP, ST_DOWN, false>(p, ST_SHDN_B, ST_DOWN, st, 1);
-        });
+        add(ST_GATE, ST_SHUP, K_GATE_SHUP);
+        add(ST_ROUTE, ST_UP, K_ROUTE_UP, 1);
+        add(ST_SHDN_B, ST_DOWN, K_UP_DOWN, 1);
     } else {
-        go([&] {
-            if (wide) launch_range<ST_ROUTE, ST_UP, true>(p, ST_ROUTE, ST_SHDN_A, st);
-            else launch_range<ST_ROUTE, ST_UP, false>(p, ST_ROUTE, ST_SHDN_A, st);
-        });
-        go([&] {
-            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_UP, ST_SHDN_B, st);
-            else launch_range<ST_UP, ST_DOWN, false>(p, ST_UP, ST_SHDN_B, st);
-        });
-        go([&] {
-            if (wide) launch_range<ST_UP, ST_DOWN, true>(p, ST_DOWN, ST_DOWN, st);
-            else launch_range<ST_UP, ST_DOWN, false>(p, ST_DOWN, ST_DOWN, st);
-        });
+        add(ST_GATE, ST_SHUP, K_GATE_SHUP);
+        add(ST_ROUTE, ST_SHDN_A, K_ROUTE_UP);
+        add(ST_UP, ST_SHDN_B, K_UP_DOWN);
+        add(ST_DOWN, ST_DOWN, K_UP_DOWN);
     }
-    go([&] { launch_range<ST_FC2, ST_FC2, false>(p, ST_FC2, ST_FC2, st); });
+    add(ST_FC2, ST_FC2, K_FC2);
     return n;
+}
+
+template <int KF, int KL, bool WIDE>
+static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st) {
+    const int lo = p.item_base[l.first], hi = p.item_base[l.last + 1];
+    if (hi > lo)
+        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, l.rev);
+}
+
+static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st) {
+    const bool wide = p.D > 2048 || p.I > 2048;
+    switch (l.kernel) {
+        case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st); break;
+        case K_ROUTE_UP:
+            if (wide) launch_kernel<ST_ROUTE, ST_UP, true>(p, l, st);
+            else launch_kernel<ST_ROUTE, ST_UP, false>(p, l, st);
+            break;
+        case K_UP_DOWN:
+            if (wide) launch_kernel<ST_UP, ST_DOWN, true>(p, l, st);
+            else launch_kernel<ST_UP, ST_DOWN, false>(p, l, st);
+            break;
+        default: launch_kernel<ST_FC2, ST_FC2, false>(p, l, st); break;
+    }
+}
+
+// Enqueue a whole forward (g == -1), or launch g alone.
+static void enqueue(const moe_latent *h, const LayerParams &p, int g) {
+    Launch ls[8];
+    const int n = plan_launches(p, ls);
+    for (int i = 0; i < n; ++i)
+        if (g == -1 || g == i) launch_one(p, ls[i], h->stream);
 }
 
 extern "C" int moe_latent_set_variant(moe_latent_t *h, int32_t variant) {
@@ -491,7 +505,7 @@ extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hid
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    launch_plan(p, h->stream, -1);
+    enqueue(h, p, -1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     h->last_rows = rows;
@@ -505,9 +519,10 @@ extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    const int n = launch_plan(p, nullptr, -2);   // counts the launches, launches nothing
+    Launch ls[8];
+    const int n = plan_launches(p, ls);
     if (group < 0 || group >= n) return fail(MOE_ERR_INVALID_ARG, "group %d outside 0..%d", group, n - 1);
-    launch_plan(p, h->stream, group);
+    enqueue(h, p, group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     return MOE_OK;
@@ -517,14 +532,10 @@ extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t gro
     if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
     LayerParams p = h->base;
     plan_items(p, rows);
-    const int n = launch_plan(p, nullptr, -2);
+    Launch ls[8];
+    const int n = plan_launches(p, ls);
     if (group < 0 || group >= n) return 0;
-    // items of the launch: the stage ranges of launch_plan
-    static const int one[4][2] = {{ST_GATE, ST_SHUP}, {ST_ROUTE, ST_UP}, {ST_SHDN_B, ST_DOWN}, {ST_FC2, ST_FC2}};
-    static const int many[5][2] = {{ST_GATE, ST_SHUP}, {ST_ROUTE, ST_SHDN_A}, {ST_UP, ST_SHDN_B}, {ST_DOWN, ST_DOWN},
-                                   {ST_FC2, ST_FC2}};
-    const int *r = p.single_row ? one[group] : many[group];
-    return p.item_base[r[1] + 1] - p.item_base[r[0]];
+    return p.item_base[ls[group].last + 1] - p.item_base[ls[group].first];
 }
 
 extern "C" int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev) {
