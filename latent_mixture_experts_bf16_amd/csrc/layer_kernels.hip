@@ -743,30 +743,51 @@ __device__ __forceinline__ void stage_lds(const uint4 *src, uint4 *dst, int unit
     }
 }
 
+// v of the lane t ^ m(b), where m(b) = 2^(b+1) - 1 for bit b <= 3 (within quads and rows of
+// 16 lanes: data-parallel-primitive moves) and m(b) = 2^b for b = 4, 5 (a swizzle, a
+// permute). m(b) has bit b as its highest bit, so the masks of distinct bits are linearly
+// independent and pair up every lane group of size 2^k exactly.
+__device__ __forceinline__ float lane_mirror(float v, int b) {
+    const int i = __float_as_int(v);
+    int r;
+    switch (b) {
+        case 0: r = __builtin_amdgcn_update_dpp(i, i, 0xB1, 0xF, 0xF, false); break;    // quad_perm 1,0,3,2
+        case 1: r = __builtin_amdgcn_update_dpp(i, i, 0x1B, 0xF, 0xF, false); break;    // quad_perm 3,2,1,0
+        case 2: r = __builtin_amdgcn_update_dpp(i, i, 0x141, 0xF, 0xF, false); break;   // row_half_mirror
+        case 3: r = __builtin_amdgcn_update_dpp(i, i, 0x140, 0xF, 0xF, false); break;   // row_mirror
+        case 4: r = __builtin_amdgcn_ds_swizzle(i, 0x401F); break;                       // xor 16
+        default: r = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), i); break;   // xor 32
+    }
+    return __int_as_float(r);
+}
+
+__device__ __forceinline__ int mirror_mask(int b) { return b >= 4 ? 1 << b : (2 << b) - 1; }
+
 // Sum each of the R values of v over the P lanes of a lane group (P, R powers of two,
-// R <= P <= 64; t = lane index in the group). Halving steps first: at distance d the lanes
-// with bit d set keep the upper half of their values and add their partner's, the others
-// the lower half; then plain butterflies. Afterwards v[0] of lane t holds the full sum of
-// value row(t) = the bits of t at P/2, P/4, ..., P/R read high to low. Fixed order.
+// R <= P <= 64; t = lane index in the group, groups aligned to P lanes). Halving steps
+// first, over the top bits of t: the lane whose bit is set keeps the upper half of its
+// values and adds its partner's (lane t ^ m(bit)), the other the lower half; then plain
+// exchanges over the remaining bits. Afterwards v[0] of lane t holds the full sum of value
+// row(t) = the top log2(R) bits of t read high to low. Fixed order.
 template <int R>
 __device__ __forceinline__ int reduce_rows(float *v, int P, int t) {
-    int n = R, d = P >> 1, row = 0;
+    int n = R, bit = 31 - __builtin_clz(P) - 1, row = 0;
 #pragma unroll
     for (int step = 0; (1 << step) < R; ++step) {
         n >>= 1;
-        const bool upper = (t & d) != 0;
+        const bool upper = (t >> bit) & 1;
         row = 2 * row + (upper ? 1 : 0);
 #pragma unroll
         for (int i = 0; i < R / 2; ++i) {
             if (i < n) {
                 const float send = upper ? v[i] : v[i + n];
                 const float keep = upper ? v[i + n] : v[i];
-                v[i] = keep + __shfl_xor(send, d, 64);
+                v[i] = keep + lane_mirror(send, bit);
             }
         }
-        d >>= 1;
+        --bit;
     }
-    for (; d >= 1; d >>= 1) v[0] = v[0] + __shfl_xor(v[0], d, 64);
+    for (; bit >= 0; --bit) v[0] = v[0] + lane_mirror(v[0], bit);
     return row;
 }
 
