@@ -554,8 +554,22 @@ enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
 template <int NW>
 struct DenseLds {
     f32x4 part[NW][2][64];   // [wave][row tile][lane]
-    uint16_t xc[4096];       // fc2 of a one-row pass: the item's slice of the combine
+    // the item's slice of the input rows, [row][kpart], when it fits (the combine itself in
+    // fc2 of a one-row pass)
+    uint16_t xs[DENSE_XLDS];
 };
+
+// 16-byte loads through a pointer of a known address space (p must point into LDS, resp.
+// global memory), so that a wait for one kind of access never counts the other.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_ld16(const void *p) {
+    const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 glb_ld16(const void *p) {
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Inputs of the fc2 epilogue (shared expert output and residual) of 4 outputs.
 struct EpiIn {
@@ -622,6 +636,8 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
     float *mypart = part + ((size_t)(tile * ks + split) * p.rows) * DENSE_TILE;
     constexpr int RT = 2;   // row tiles (16 rows each) per pass over the weights
     const bool inl = EPI == EPI_FC2 && p.inline_comb;
+    // the input slice staged in LDS when it fits (always for a one-row fc2 pass that combines)
+    const bool xl = inl || p.rows * kpart <= DENSE_XLDS;
     const uint16_t *wrow = W + (size_t)(n0 + nr) * K + kbase + wave * kw + 32 * grp;
     const size_t xoff = (size_t)kbase + wave * kw + 32 * grp;
 
@@ -635,7 +651,6 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
             }
         }
     };
-    if (wave < nsplit) load_w(0);
     // the fc2 epilogue's inputs, when one pass finishes every row here
     const bool epi_pre = EPI == EPI_FC2 && ks == 1 && nrt <= RT;
     EpiIn pre = {};
@@ -643,13 +658,26 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
         const int row = wave * 16 + nr;
         if (row < p.rows) pre = epi_load(p, row, n0 + 4 * grp);
     }
-    if (inl) {
-        for (int i = 4 * threadIdx.x; i < kpart; i += 4 * NW * 64) {
-            float c4[4];
-            combine4(p, 0, kbase + i, c4);
-            const uint2 c = {pack2(f2bf(c4[0]), f2bf(c4[1])), pack2(f2bf(c4[2]), f2bf(c4[3]))};
-            *(uint2 *)(L.xc + i) = c;
-            if (tile == 0) *(uint2 *)(p.comb + kbase + i) = c;
+    // the passes over the weights, compiled once per input source (LDS or global memory); the
+    // first weights are loaded inside, so that no weight register is live across the choice
+    auto passes = [&](auto xl_c) {
+    if (wave < nsplit) load_w(0);
+    if constexpr (decltype(xl_c)::value) {
+        if (inl) {
+            for (int i = 4 * threadIdx.x; i < kpart; i += 4 * NW * 64) {
+                float c4[4];
+                combine4(p, 0, kbase + i, c4);
+                const uint2 c = {pack2(f2bf(c4[0]), f2bf(c4[1])), pack2(f2bf(c4[2]), f2bf(c4[3]))};
+                *(uint2 *)(L.xs + i) = c;
+                if (tile == 0) *(uint2 *)(p.comb + kbase + i) = c;
+            }
+        } else {
+            const int cpr = kpart >> 3;   // 16-byte chunks per row
+#pragma unroll 4
+            for (int c = threadIdx.x; c < p.rows * cpr; c += NW * 64) {
+                const int r = c / cpr, o = (c - r * cpr) << 3;
+                *(uint4 *)(L.xs + r * kpart + o) = glb_ld16(X + (size_t)r * K + kbase + o);
+            }
         }
         __syncthreads();
     }
@@ -670,9 +698,15 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
                             if (rt0 + t < nrt) {
                                 uint4 b0 = {0, 0, 0, 0}, b1 = b0, b2 = b0, b3 = b0;
                                 if (row < p.rows) {
-                                    const uint4 *xp = inl ? (const uint4 *)(L.xc + wave * kw + 32 * grp + kb)
-                                                          : (const uint4 *)(X + (size_t)row * K + xoff + kb);
-                                    b0 = xp[0]; b1 = xp[1]; b2 = xp[2]; b3 = xp[3];
+                                    if constexpr (decltype(xl_c)::value) {
+                                        const uint16_t *xp = L.xs + row * kpart + wave * kw + 32 * grp + kb;
+                                        b0 = lds_ld16(xp); b1 = lds_ld16(xp + 8);
+                                        b2 = lds_ld16(xp + 16); b3 = lds_ld16(xp + 24);
+                                    } else {
+                                        const uint16_t *xp = X + (size_t)row * K + xoff + kb;
+                                        b0 = glb_ld16(xp); b1 = glb_ld16(xp + 8);
+                                        b2 = glb_ld16(xp + 16); b3 = glb_ld16(xp + 24);
+                                    }
                                 }
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                     __builtin_bit_cast(bf16x8, a[q][0]), __builtin_bit_cast(bf16x8, b0), acc[t], 0, 0, 0);
@@ -685,6 +719,9 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
                             }
                         }
                     }
+                    // one step's inputs live at a time (keeps the scheduler from hoisting
+                    // the input reads of every step ahead of the first multiply)
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -708,6 +745,9 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
         }
         __syncthreads();
     }
+    };
+    if (xl) passes(std::true_type{});
+    else passes(std::false_type{});
     if (ks > 1 && last_arriver(ctr + tile, (uint32_t)ks, s_flag)) {
         for (int i = threadIdx.x; i < p.rows * DENSE_TILE; i += NW * 64) {
             const int row = i / DENSE_TILE, nn = i % DENSE_TILE;

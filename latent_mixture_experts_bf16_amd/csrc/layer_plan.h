@@ -55,6 +55,7 @@ constexpr int EXPERT_LDS_CODES = 32768;   // LDS bytes for one expert item's cod
 constexpr int EXPERT_LDS_SCALES = 2048;   // ... and for its scales (and again its biases)
 constexpr int EXPERT_MAX_BLOCK = 64;      // output rows of one expert item at most
 constexpr int DENSE_TILE = 16;    // outputs per dense item
+constexpr int DENSE_XLDS = 8192;  // input elements a dense item stages in LDS at most
 
 struct LayerParams {
     // sizes

@@ -462,7 +462,7 @@ static void plan_items(LayerParams &p, int rows) {
     int n[NSTAGE];
     p.rows = rows;
     p.single_row = rows == 1;
-    p.inline_comb = rows == 1 && p.L && p.L / p.ks_fc2 <= 4096;
+    p.inline_comb = rows == 1 && p.L && p.L / p.ks_fc2 <= DENSE_XLDS;
     p.umax = p.E < rows * p.K ? p.E : rows * p.K;
     p.up_nb = expert_block(p.I, p.D);
     p.dn_nb = expert_block(p.D, p.I);
