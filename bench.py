@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--pmc-out")
     ap.add_argument("--stats-out")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--no-rows-sweep", action="store_true",
+                    help="skip the 16-row and 64-row passes reported beside the one-row line")
     return ap.parse_args()
 
 
@@ -370,10 +372,75 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
     }
-    print(json.dumps(line), flush=True)
     for lay in layers:
         lay.close()
+    del layers, xs, outs
+    torch.cuda.empty_cache()
+    if not args.no_rows_sweep and rows == 1:
+        line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
+    print(json.dumps(line), flush=True)
     return 0
+
+
+def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):
+    """Multi-row passes: the 16-row pass (distinct weight instances rotated through HBM) or the
+    8-layer 64-row stack (each layer with its own input), timed as graph replays of one sweep
+    over all layers and instances; algorithmic bytes as for the one-row line."""
+    import numpy as np
+    import torch
+    wl = synth.WORKLOADS[cfg]
+    rows = wl.rows
+    t0 = time.time()
+    layers, xs, outs, nbytes = [], [], [], 0.0
+    for i in range(instances):
+        for d, arrays in synth.workload_layers(cfg, instance=i):
+            lay = LY.DeviceLayer(d, arrays, max_rows=rows)
+            layers.append(lay)
+            xs.append(LY.to_device(arrays["x"]))
+            outs.append(torch.empty_like(xs[-1]))
+            del arrays
+    s = torch.cuda.Stream()
+    for lay in layers:
+        B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+    with torch.cuda.stream(s):
+        for lay, x, o in zip(layers, xs, outs):
+            lay.forward(x, o, rows)
+    s.synchronize()
+    for lay in layers:
+        lay.status()
+        idx, _ = lay.routing(rows)
+        nbytes += sum(stage_bytes(lay.dims, rows, len(np.unique(idx))).values())
+    print(f"[bench] rows sweep {wl.name}: {len(layers)} layers ready in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for lay, x, o in zip(layers, xs, outs):
+                lay.forward(x, o, rows)
+        for _ in range(warmup):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(sweeps):
+            g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    for lay in layers:
+        lay.status()
+    us_sweep = a.elapsed_time(b) * 1e3 / sweeps
+    n_layers = len(layers)
+    gbps = nbytes / (us_sweep * 1e-6) / 1e9
+    out = {"workload": wl.name, "rows": rows, "layers_per_sweep": n_layers,
+           "us_per_layer_pass": round(us_sweep / n_layers, 2),
+           "layer_tokens_per_s": round(rows * n_layers / (us_sweep * 1e-6), 1),
+           "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "bytes_per_sweep": int(nbytes)}
+    print(f"[bench] rows sweep: {json.dumps(out)}", file=sys.stderr, flush=True)
+    for lay in layers:
+        lay.close()
+    del layers, xs, outs, g
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
