@@ -158,22 +158,71 @@ __device__ __forceinline__ bool last_arriver(uint32_t *c, uint32_t target, int *
 
 // ------------------------------------------------------------------ gate
 
-// Item: NW experts (one per wave), all rows. Fixed summation order described above. The
-// loads of a row are issued before its arithmetic; bf16 gate rows of up to 4096 inputs stay
-// in registers across the rows of the pass.
+// Input rows of a multi-row gate item, staged in LDS (16-bit values).
+constexpr int GATE_LDS_ELEMS = 16384;
+struct GateLds {
+    uint4 x[GATE_LDS_ELEMS / 8];
+};
+
+// Item: NW experts (one per wave) for the rows [r0, r1) of chunk item / groups (all rows when
+// gate_rc >= rows). Fixed summation order described above. bf16 gate rows of up to 4096
+// inputs stay in registers across the rows; a one-row pass loads its input row into registers
+// with them, a multi-row item first copies its chunk of input rows into LDS (all rows' loads
+// in flight at once) and reads each row from there.
 template <int NW>
-__device__ __forceinline__ void gate_item(const LayerParams &p, int item) {
+__device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLds &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = item * NW + wave;
-    if (e >= p.E) return;
+    const int groups = (p.E + NW - 1) / NW;
+    const int e = (item % groups) * NW + wave;
+    const int r0 = (item / groups) * p.gate_rc;
+    const int r1 = r0 + p.gate_rc < p.rows ? r0 + p.gate_rc : p.rows;
     const int nj = p.H / 512;
+    if (!p.router_f32 && nj <= 8 && p.rows > 1) {
+        // the chunk's rows: direct global -> LDS copies, 1 KB per wave instruction
+        const int units = (r1 - r0) * (p.H >> 3);
+        const uint4 *src = (const uint4 *)(p.x + (size_t)r0 * p.H);
+        for (int u0 = wave * 64; u0 < units; u0 += NW * 64) {
+            if (u0 + lane < units)
+                __builtin_amdgcn_global_load_lds((const void *)(src + u0 + lane),
+                                                 (__attribute__((address_space(3))) void *)(L.x + u0), 16, 0, 0);
+        }
+        uint4 wv[8];
+        if (e < p.E) {
+            const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < nj) wv[j] = *(const uint4 *)(wr + 512 * j);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (e >= p.E) return;
+        for (int r = r0; r < r1; ++r) {
+            const uint4 *xr = L.x + (size_t)(r - r0) * (p.H >> 3) + lane;
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < nj) {
+                    float xf[8], wf[8];
+                    unpack8(p.act_f16, xr[64 * j], xf);
+                    unpack8(0, wv[j], wf);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
+            if (lane == 0) st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
+        }
+        return;
+    }
+    if (e >= p.E) return;
     if (!p.router_f32 && nj <= 8) {
         const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
         uint4 wv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             if (j < nj) wv[j] = *(const uint4 *)(wr + 512 * j);
-        for (int r = 0; r < p.rows; ++r) {
+        for (int r = r0; r < r1; ++r) {
             const uint16_t *xr = p.x + (size_t)r * p.H + 8 * lane;
             uint4 xv[8];
 #pragma unroll
@@ -196,7 +245,7 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item) {
         }
         return;
     }
-    for (int r = 0; r < p.rows; ++r) {
+    for (int r = r0; r < r1; ++r) {
         const uint16_t *xr = p.x + (size_t)r * p.H;
         float acc = 0.0f;
         for (int j0 = 0; j0 < nj; j0 += 4) {
@@ -986,6 +1035,7 @@ struct StageLds {
     union U {
         typename std::conditional<dense, DenseLds<NW>, NoLds>::type dense;
         typename std::conditional<has(ST_GATE) || has(ST_ROUTE), RouteLds<WG_THREADS>, NoLds>::type route;
+        typename std::conditional<has(ST_GATE), GateLds, NoLds>::type gate;
         typename std::conditional<has(ST_ROUTE), SchedLds, NoLds>::type sched;
         typename std::conditional<has(ST_UP) || has(ST_DOWN), ExpertLds<XMAX_OF(WIDE)>, NoLds>::type ex;
     };
@@ -994,7 +1044,7 @@ struct StageLds {
 template <int S, bool WIDE, class LdsT>
 __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
-        gate_item<NW>(p, local);
+        gate_item<NW>(p, local, lds.gate);
         if (p.single_row &&
             last_arriver(p.ctr + CTR_GATE, (uint32_t)(p.item_base[ST_GATE + 1] - p.item_base[ST_GATE]), s_flag))
             route_item<WG_THREADS>(p, 0, lds.route);

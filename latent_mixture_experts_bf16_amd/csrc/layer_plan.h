@@ -98,6 +98,7 @@ struct LayerParams {
     int up_nb, dn_nb;      // output rows of one routed up / down item
     int up_blocks, dn_blocks;
     int single_row;        // rows == 1: the last gate item routes and writes the schedule
+    int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)
     int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
 };
 

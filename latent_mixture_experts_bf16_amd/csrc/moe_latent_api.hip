@@ -471,7 +471,11 @@ static void plan_items(LayerParams &p, int rows) {
     // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's
     // tiles are cut in two halves for two launches
     const int shdn = p.SI ? p.H / DENSE_TILE : 0, ks_sd = p.ks_shdn;
-    n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64);
+    // gate: groups of 4 experts; a multi-row pass of bf16 rows up to 4096 wide splits its rows
+    // in chunks that fit the item's 32 KB of LDS
+    p.gate_rc = rows > 1 && !p.router_f32 && p.H <= 4096 ? 16384 / p.H : rows;
+    if (p.gate_rc > 16) p.gate_rc = 16;
+    n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64) * ((rows + p.gate_rc - 1) / p.gate_rc);
     n[ST_FC1] = p.L ? p.L / DENSE_TILE * p.ks_fc1 : 0;
     n[ST_SHUP] = p.SI / DENSE_TILE * p.ks_shup;
     n[ST_ROUTE] = p.single_row ? 0 : rows;
