@@ -69,7 +69,8 @@ typedef struct {
  * latent % 128 == 0; expert_inter % 64 == 0; shared_inter == 0 or % 128 == 0; expert input
  * and inter widths <= 6144; group_size == 64; n_experts <= 1024; n_group <= 256; top_k <= 16;
  * 1 <= max_rows <= 256. latent == 0 selects the non-latent layer; shared_inter == 0 drops
- * the shared expert. */
+ * the shared expert. A shared expert needs a latent layer (MOE_ERR_SHAPE otherwise): its
+ * output is added in the fc2 epilogue. */
 typedef struct {
     int32_t hidden;         /* H */
     int32_t latent;         /* L, or 0 (non-latent) */

@@ -131,6 +131,9 @@ static int check_config(const moe_latent_config &c) {
         return fail(MOE_ERR_DTYPE, "config: act_dtype %s (bf16 or f16)", dt_name(c.act_dtype));
     if (c.act_dtype == MOE_DT_F16 && (c.latent || c.shared_inter))
         return fail(MOE_ERR_DTYPE, "config: f16 activations only for the non-latent layer without a shared expert");
+    if (!c.latent && c.shared_inter)
+        return fail(MOE_ERR_SHAPE, "config: a shared expert needs a latent layer (its output is added in the fc2 "
+                    "epilogue)");
     if (c.router_dtype != MOE_DT_BF16 && c.router_dtype != MOE_DT_F32)
         return fail(MOE_ERR_DTYPE, "config: router_dtype %s (bf16 or f32)", dt_name(c.router_dtype));
     if (c.activation != MOE_ACT_RELU2) return fail(MOE_ERR_INVALID_ARG, "config: activation %d", c.activation);

@@ -99,6 +99,13 @@ def test_config_refusals(over, code, word):
     assert word in msg
 
 
+def test_non_latent_shared_expert_refused():
+    # a non-latent layer has no fc2 epilogue, where the shared output is added
+    rc, h, msg = _create(NONLAT, cfg_over={"shared_inter": 512, "act_dtype": B.MOE_DT_BF16})
+    assert rc == "MOE_ERR_SHAPE" and h is None
+    assert "latent layer" in msg
+
+
 @pytest.mark.parametrize("name,over,code,word", [
     ("fc1_w", {"ptr": 0}, "MOE_ERR_MISSING_TENSOR", "fc1_latent_proj"),
     ("fc2_w", {"ptr": 0}, "MOE_ERR_MISSING_TENSOR", "fc2_latent_proj"),
