@@ -158,6 +158,27 @@ __device__ __forceinline__ bool last_arriver(uint32_t *c, uint32_t target, int *
 
 // ------------------------------------------------------------------ gate
 
+// The handoff word of expert e of a one-row pass (see LayerParams::ctr_hand).
+__device__ __forceinline__ uint64_t *hand_word(const LayerParams &p, int e) {
+    return (uint64_t *)(p.ctr + p.ctr_hand) + e;
+}
+
+// Store logit (r, e) (raw bits: bf16, or fp32 for the fp32 router). A multi-row pass writes it
+// through for the route items of the next launch; a one-row pass hands it to the route item
+// of this launch in one 64-bit store (value and presence bit together, so the route item
+// never sees one without the other) and keeps a plain copy for the stage readback.
+__device__ __forceinline__ void put_logit(const LayerParams &p, int r, int e, uint32_t bits) {
+    if (p.single_row) {
+        __hip_atomic_store(hand_word(p, e), (1ull << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.router_f32) ((uint32_t *)p.logits)[e] = bits;
+        else ((uint16_t *)p.logits)[e] = (uint16_t)bits;
+    } else if (p.router_f32) {
+        st_shared32((int32_t *)p.logits + (size_t)r * p.E + e, (int32_t)bits);
+    } else {
+        st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, (uint16_t)bits);
+    }
+}
+
 // Input rows of a multi-row gate item, staged in LDS (16-bit values).
 constexpr int GATE_LDS_ELEMS = 16384;
 struct GateLds {
@@ -211,7 +232,7 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLd
             }
 #pragma unroll
             for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-            if (lane == 0) st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
+            if (lane == 0) put_logit(p, r, e, f2bf(acc));
         }
         return;
     }
@@ -241,7 +262,7 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLd
             }
 #pragma unroll
             for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-            if (lane == 0) st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
+            if (lane == 0) put_logit(p, r, e, f2bf(acc));
         }
         return;
     }
@@ -283,10 +304,7 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLd
         }
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-        if (lane == 0) {
-            if (p.router_f32) st_shared32((int32_t *)p.logits + (size_t)r * p.E + e, __float_as_int(acc));
-            else st_shared16((uint16_t *)p.logits + (size_t)r * p.E + e, f2bf(acc));
-        }
+        if (lane == 0) put_logit(p, r, e, p.router_f32 ? __float_as_uint(acc) : (uint32_t)f2bf(acc));
     }
 }
 
@@ -366,8 +384,29 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     for (int e = tid; e < E; e += NT) {
         // both loads are issued before either value is used
         const float bias = p.has_bias ? p.bias[e] : 0.0f;
-        const uint32_t raw = p.router_f32 ? (uint32_t)ld_shared32((const int32_t *)p.logits + (size_t)r * E + e)
-                                          : (uint32_t)ld_shared16((const uint16_t *)p.logits + (size_t)r * E + e);
+        uint32_t raw;
+        if (p.single_row) {
+            // the gate items of this launch hand the logits over: poll the expert's word
+            // (read around the caches) until it is present, for at most wait_ticks (then
+            // error bit 8), and clear it for the next forward
+            uint64_t v = __hip_atomic_load(hand_word(p, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!(v >> 32)) {
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                do {
+                    __builtin_amdgcn_s_sleep(1);
+                    v = __hip_atomic_load(hand_word(p, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (!(v >> 32) && __builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)p.wait_ticks) {
+                        atomicOr(p.err, 8u);
+                        break;
+                    }
+                } while (!(v >> 32));
+            }
+            __hip_atomic_store(hand_word(p, e), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            raw = (uint32_t)v;
+        } else {
+            raw = p.router_f32 ? (uint32_t)ld_shared32((const int32_t *)p.logits + (size_t)r * E + e)
+                               : (uint32_t)ld_shared16((const uint16_t *)p.logits + (size_t)r * E + e);
+        }
         const float z = p.router_f32 ? __uint_as_float(raw) : __uint_as_float(raw << 16);
         const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
         const float b = p.has_bias ? s + bias : s;
@@ -1044,10 +1083,10 @@ struct StageLds {
 template <int S, bool WIDE, class LdsT>
 __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
-        gate_item<NW>(p, local, lds.gate);
-        if (p.single_row &&
-            last_arriver(p.ctr + CTR_GATE, (uint32_t)(p.item_base[ST_GATE + 1] - p.item_base[ST_GATE]), s_flag))
-            route_item<WG_THREADS>(p, 0, lds.route);
+        // a one-row pass: item 0 routes the row with the logits the other gate items hand it
+        if (!p.single_row) gate_item<NW>(p, local, lds.gate);
+        else if (local == 0) route_item<WG_THREADS>(p, 0, lds.route);
+        else gate_item<NW>(p, local - 1, lds.gate);
     } else if constexpr (S == ST_FC1) {
         const int ks = p.ks_fc1;
         dense_item<EPI_FC1, NW>(p, p.fc1, p.x, p.H, local / ks, local % ks, ks, p.part_fc1, p.ctr + p.ctr_fc1,

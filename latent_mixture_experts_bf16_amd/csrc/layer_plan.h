@@ -11,8 +11,8 @@ namespace moe {
 // "last arriver" of the same launch reads after every item it depends on has counted itself
 // done (no item ever waits for another).
 enum Stage : int {
-    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; for a one-row
-                   // pass the last gate item to finish also routes the row
+    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; a one-row pass
+                   // has one more item, first: the route item, which waits for the logits
     ST_FC1,        // u = rnd(W1 . x), 16 outputs per item (MFMA)
     ST_SHUP,       // shared expert up + relu^2, 16 outputs per item
     ST_ROUTE,      // multi-row passes: one row per item; the last route item to finish builds
@@ -32,7 +32,6 @@ enum : int {
     MAX_ROWS = 256,
     // completion counters (uint32) of the last-arriver steps; the dense projections' tile
     // counters follow (offsets in LayerParams)
-    CTR_GATE = 0,
     CTR_ROUTE = 1,
     CTR_BLOCK = 2,         // CTR_BLOCK + b: down items of output block b done
     CTR_DENSE = 2048,
@@ -100,6 +99,11 @@ struct LayerParams {
     int single_row;        // rows == 1: the last gate item routes and writes the schedule
     int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)
     int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
+    // one-row pass: each gate item hands its logits to the route item (the first item of the
+    // launch) through 64-bit words [E] in the counter block at ctr_hand (bit 32: present),
+    // which the route item polls for at most wait_ticks ticks of the 100 MHz real-time counter
+    int ctr_hand;
+    uint32_t wait_ticks;
 };
 
 }  // namespace moe

@@ -262,7 +262,10 @@ static int setup_workspace(moe_latent *h) {
     p.ctr_shup = p.ctr_fc1 + (int)(L / DENSE_TILE);
     p.ctr_shdn = p.ctr_shup + (int)(SI / DENSE_TILE);
     p.ctr_fc2 = p.ctr_shdn + (SI ? (int)(H / DENSE_TILE) : 0);
-    h->n_ctr = p.ctr_fc2 + (L ? (int)(H / DENSE_TILE) : 0);
+    // the one-row logit handoff words (8-byte aligned, zero between forwards)
+    p.ctr_hand = (p.ctr_fc2 + (L ? (int)(H / DENSE_TILE) : 0) + 1) & ~1;
+    h->n_ctr = p.ctr_hand + 2 * (int)E;
+    p.wait_ticks = 10000000u;   // 100 ms: far beyond any forward
     // split-K partials: [tile][split][row][16] floats = N * splits * rows floats
     const size_t part_fc1 = L * p.ks_fc1 * R * 4;
     const size_t part_shup = SI * p.ks_shup * R * 4;
@@ -478,7 +481,8 @@ static void plan_items(LayerParams &p, int rows) {
     // in chunks that fit the item's 32 KB of LDS
     p.gate_rc = rows > 1 && !p.router_f32 && p.H <= 4096 ? 16384 / p.H : rows;
     if (p.gate_rc > 16) p.gate_rc = 16;
-    n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64) * ((rows + p.gate_rc - 1) / p.gate_rc);
+    n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64) * ((rows + p.gate_rc - 1) / p.gate_rc) +
+                 (p.single_row ? 1 : 0);
     n[ST_FC1] = p.L ? p.L / DENSE_TILE * p.ks_fc1 : 0;
     n[ST_SHUP] = p.SI / DENSE_TILE * p.ks_shup;
     n[ST_ROUTE] = p.single_row ? 0 : rows;
