@@ -919,14 +919,41 @@ __device__ __forceinline__ int reduce_rows(float *v, int P, int t) {
     return row;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c in fp32, a and b packed bf16 (F16: fp16) pairs
+template <bool F16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Codes i and i + 4 of the word w (inputs 8j+i and 8j+i+4 of its 8) as a packed pair of
+// 16-bit values, with one mask-and-insert: nibble bits placed under the exponent of 128 (bf16:
+// 0x4300 | q is 128 + q exactly) or of 1024 (fp16: 0x6400 | q is 1024 + q, less 1024 exactly
+// gives q).
+template <bool F16>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, int i) {
+    const uint32_t m = ((w >> (4 * i)) & 0x000F000Fu) | (F16 ? 0x64006400u : 0x43004300u);
+    if constexpr (F16) {
+        const f16x2 h = __builtin_bit_cast(f16x2, m) - (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+        return __builtin_bit_cast(uint32_t, h);
+    } else {
+        return m;
+    }
+}
+
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
 // pair (row, pick) of that slot. The block's 4-bit codes, scales and biases and the first
 // pair's input row are staged in LDS (all in flight at once; every weight byte is read from
 // HBM once, whatever the number of rows). Each output row's inputs are cut in chunks of 32
-// (16 bytes of codes). A group of P lanes (P = chunks rounded up to a power of two, at most
-// 64) covers the chunks of R output rows, lane t taking chunks t, t + P, ...: it keeps its
-// chunk's inputs in registers and adds, per row and chunk, scale * sum(q * x) + bias *
-// sum(x); reduce_rows then joins the P lanes of each row.
+// (16 bytes of codes). A group of P lanes covers the chunks of its output rows, lane t taking
+// chunks t, t + P, ... (at most 4): it keeps their inputs in registers as packed pairs and
+// adds, per row and chunk, scale * sum(q * x) + bias * sum(x), the products summed by
+// 2-element dot products in fp32; reduce_rows then joins the P lanes of each row.
 template <bool UP, int XMAX, bool F16>
 __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -951,23 +978,41 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G64;
     const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
     auto xrow = [&](int q) { return xin + (UP ? (size_t)(q / p.K) * Kin : (size_t)q * Kin); };
-    int P = 1;
-    while (P < C && P < 64) P <<= 1;
+    // P lanes per row, each keeping up to XCH chunks (32 inputs each) of the input row, so that
+    // a row is joined over few lanes (within a row of 16 lanes: data-parallel moves only)
+    constexpr int XCH = 4;
+    int P = 2;
+    while (P * XCH < C && P < 64) P <<= 1;
+    const int nch = (C + P - 1) / P;          // chunks per lane, <= XCH (inputs <= 6144)
     const int gpw = 64 / P, t = lane % P, grp = lane / P;
     const int NG = (WG_THREADS / 64) * gpw;   // lane groups of the item
-    int RG = NB / NG;                          // rows per lane group
+    int RG = NB / NG;                          // rows per lane group (1 or 2: NB * C <= 2048)
     if (RG < 1) RG = 1;
-    const int nch = (C + P - 1) / P;
-    const int RB = RG < 4 ? RG : 4;            // rows per batch
-    // batch b of group g covers rows b * 4 * NG + 4 g + (0..3)
+    const int g = wave * gpw + grp;
+    // The codes go to LDS in the order the lanes read them when the lanes tile the block
+    // exactly: unit ((m * RG + row in group) * NG + group) * P + t holds chunk t + P m of that
+    // row, so each read instruction of a wave takes 1 KB of consecutive LDS (no bank
+    // conflicts); otherwise row-major (row * C + chunk).
+    const bool tiled = nch * P == C && RG * NG == NB;
     stage_lds((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
     stage_lds((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
     stage_lds((const uint4 *)xrow(pr), L.x, Kin >> 3);
-    stage_lds((const uint4 *)Q, L.q, NB * C);
+    if (tiled) {
+        const uint4 *src = (const uint4 *)Q;
+        const int lp = __builtin_ctz(P), lg = __builtin_ctz(NG), lr = __builtin_ctz(RG);   // powers of two
+        for (int u0 = wave * 64; u0 < NB * C; u0 += WG_THREADS) {
+            const int u = u0 + lane;
+            const int ut = u & (P - 1), ug = (u >> lp) & (NG - 1), ur = (u >> (lp + lg)) & (RG - 1);
+            const int um = u >> (lp + lg + lr);
+            if (u < NB * C)
+                __builtin_amdgcn_global_load_lds((const void *)(src + (ug * RG + ur) * C + ut + P * um),
+                                                 (__attribute__((address_space(3))) void *)(L.q + u0), 16, 0, 0);
+        }
+    } else {
+        stage_lds((const uint4 *)Q, L.q, NB * C);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    auto row_of = [&](int rb, int ii) { return RB == 4 ? (rb / 4) * 4 * NG + 4 * (wave * gpw + grp) + ii
-                                                       : (wave * gpw + grp) * RG + rb + ii; };
     for (int r = 0; r < R; ++r) {
         if (r > 0) {
             pr = p.sched[SCH_PAIRS + off + r];
@@ -977,56 +1022,72 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
-        // the lane's input chunk (one chunk per lane unless the rows are wider than 2048)
-        float xf[32], xs = 0.0f;
-        auto load_x = [&](int c) {
+        // the lane's chunks of the input row: packed 16-bit pairs (x[8j+i], x[8j+i+4]), i < 4,
+        // matching the code pairs decoded below, and each chunk's sum
+        uint32_t xq[XCH][16];
+        float xs[XCH];
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) unpack8(F16, L.x[4 * c + q4], &xf[8 * q4]);
-            xs = 0.0f;
+        for (int m = 0; m < XCH; ++m) {
+            const int c = t + P * m;
+            xs[m] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) xs = xs + xf[i];
-        };
-        if (nch == 1 && t < C) load_x(t);
-        for (int rb = 0; rb < RG; rb += 4) {
-            // 4 rows at a time, without branches (rows past NB read row NB - 1, dropped below)
-            float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int m = 0; m < nch; ++m) {
+            for (int k = 0; k < 16; ++k) xq[m][k] = 0u;
+            if (m < nch && c < C) {
+                uint32_t xw[16];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const uint4 v4 = lds_ld16(&L.x[4 * c + q4]);
+                    xw[4 * q4] = v4.x; xw[4 * q4 + 1] = v4.y; xw[4 * q4 + 2] = v4.z; xw[4 * q4 + 3] = v4.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xq[m][4 * j] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x05040100u);
+                    xq[m][4 * j + 1] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x07060302u);
+                    xq[m][4 * j + 2] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x05040100u);
+                    xq[m][4 * j + 3] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x07060302u);
+                }
+                float sx = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) sx = dot2<F16>(F16 ? 0x3C003C00u : 0x3F803F80u, xw[k], sx);
+                xs[m] = sx;
+            }
+        }
+        for (int rb = 0; rb < RG; rb += 2) {
+            // 2 rows at a time, without branches (rows past NB read row NB - 1, dropped below)
+            float v[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < XCH; ++m) {
                 const int c = t + P * m;
-                if (c < C) {
-                    if (nch > 1) load_x(c);
-                    uint4 qv[4];
-                    float sc[4], bi[4];
+                if (m < nch && c < C) {
+                    uint4 qv[2];
+                    float sc[2], bi[2];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        int nl = row_of(rb, ii);
+                    for (int ii = 0; ii < 2; ++ii) {
+                        int nl = g * RG + rb + ii;
                         nl = nl < NB ? nl : NB - 1;
-                        qv[ii] = L.q[nl * C + c];
+                        qv[ii] = lds_ld16(&L.q[tiled ? ((m * RG + rb + ii) * NG + g) * P + t : nl * C + c]);
                         sc[ii] = bf2f(L.s[nl * G64 + (c >> 1)]);
                         bi[ii] = bf2f(L.b[nl * G64 + (c >> 1)]);
                     }
-                    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
+                    for (int ii = 0; ii < 2; ++ii) {
+                        float a = 0.0f;
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
-                            const uint32_t w = q4 == 0 ? qv[ii].x : q4 == 1 ? qv[ii].y : q4 == 2 ? qv[ii].z : qv[ii].w;
-                            float qf[8];
-                            nibbles8(w, qf);
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t w = j == 0 ? qv[ii].x : j == 1 ? qv[ii].y : j == 2 ? qv[ii].z : qv[ii].w;
 #pragma unroll
-                            for (int k = 0; k < 8; ++k) part[ii] = __builtin_fmaf(qf[k], xf[8 * q4 + k], part[ii]);
+                            for (int i = 0; i < 4; ++i) a = dot2<F16>(code_pair<F16>(w, i), xq[m][4 * j + i], a);
                         }
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        v[ii] = __builtin_fmaf(sc[ii], part[ii], v[ii]);
-                        v[ii] = __builtin_fmaf(bi[ii], xs, v[ii]);
+                        // bf16 pairs carry 128 + q: scale * sum(q x) = scale * a - 128 scale * sum(x)
+                        v[ii] = __builtin_fmaf(sc[ii], a, v[ii]);
+                        v[ii] = __builtin_fmaf(F16 ? bi[ii] : __builtin_fmaf(-128.0f, sc[ii], bi[ii]), xs[m], v[ii]);
                     }
                 }
             }
-            const int rr = RB == 4 ? reduce_rows<4>(v, P, t) : RB == 2 ? reduce_rows<2>(v, P, t) : reduce_rows<1>(v, P, t);
+            const int rr = reduce_rows<2>(v, P, t);
             // lane t holds row rb + rr; the lowest lane of those holding it stores it
-            const int nl = row_of(rb, rr);
-            if ((t & (P / RB - 1)) == 0 && nl < NB && rb + rr < RG) {
+            const int nl = g * RG + rb + rr;
+            if ((t & (P / 2 - 1)) == 0 && nl < NB && rb + rr < RG) {
                 const int n = n0 + nl;
                 const float acc = v[0];
                 if (UP) p.eact[(size_t)pr * p.I + n] = f2act(F16, relu_sq(F16, rnd(F16, acc)));
