@@ -10,8 +10,11 @@ layer are 0.86 GB. The steps are replayed from a captured HIP graph.
 
 Prints one JSON line: layer-tokens/s (rows x steps / seconds), the whole layer's achieved
 HBM bandwidth from its algorithmic bytes, the dominant kernel's roofline (algorithmic
-bytes of one launch / its average duration, both measured here with HIP events on the
-launch stream), and the CPU oracle timed on this host.
+bytes of one launch / its average duration inside full forwards, the duration taken from
+HIP events that the launch's own kernel dispatch records on the launch stream), and the
+CPU oracle timed on this host. Each launch group is also timed alone (graph replays of that
+launch over all instances, "us_alone"): a launch runs 0.2-1.7 us faster after itself than
+after the previous launch of a forward.
 """
 import argparse
 import glob
@@ -138,6 +141,20 @@ def summarize_stats(args):
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"{r['Name'][:70]:70s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:9.3f} "
                      f"{float(r['MinNs']) / 1e3:9.3f} {float(r['MaxNs']) / 1e3:9.3f} {float(r['Percentage']):6.2f}")
+    # the same dispatches split by what ran just before: another kernel (inside a forward) or
+    # the same one (the replays of one launch group alone)
+    trace = _csv_rows(args.summarize_stats, "kernel_trace.csv")
+    disp = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in trace)
+    split = {}
+    for i in range(1, len(disp)):
+        st, en, name = disp[i]
+        if "moe_stage_kernel" not in name:
+            continue
+        key = (name, "inside forwards" if disp[i - 1][2] != name else "after itself")
+        split.setdefault(key, []).append((en - st) / 1e3)
+    lines += ["", "by the dispatch before (moe_stage_kernel only)", f"{'kernel':70s} {'context':>16s} {'calls':>7s} {'avg_us':>9s}"]
+    for (name, ctx), v in sorted(split.items()):
+        lines.append(f"{name[:70]:70s} {ctx:>16s} {len(v):7d} {sum(v) / len(v):9.3f}")
     txt = "\n".join(lines) + "\n"
     with open(args.stats_out, "w") as fh:
         fh.write(txt)
@@ -299,6 +316,15 @@ def main():
         del gg
     for lay in layers:
         lay.status()
+    # each launch inside full forwards, as the roofline's duration: its kernel's start and end
+    # recorded by the kernel's own dispatch (no marker packets between the launches)
+    inside = in_forward_launches(B, layers, xs, outs, rows, s, len(launches))
+    for gid, v in group_stats.items():
+        v["us_alone"] = v["us"]
+        v["us"] = round(float(inside[gid]), 3)
+        v["gbps"] = round(v["bytes"] / (v["us"] * 1e-6) / 1e9, 1)
+    for lay in layers:
+        lay.status()
     dom = max(group_stats, key=lambda k: group_stats[k]["us"])
     d = group_stats[dom]
     traffic, traffic_note = None, "no counter summary for this workload"
@@ -367,7 +393,7 @@ def main():
                      "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_note": traffic_note,
                      "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]},
-        "launches": {v["name"]: {"us": v["us"], "bytes": v["bytes"], "gbps": v["gbps"]}
+        "launches": {v["name"]: {"us": v["us"], "us_alone": v["us_alone"], "bytes": v["bytes"], "gbps": v["gbps"]}
                      for v in group_stats.values()},
         "cpu_baseline": cpu,
         "parity": parity,
@@ -380,6 +406,37 @@ def main():
         line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
     print(json.dumps(line), flush=True)
     return 0
+
+
+def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):
+    """Mean duration (us) of each launch group inside full forwards: forwards enqueued eagerly,
+    `sweeps` sweeps over the instances between synchronizations, each launch's kernel start and
+    end recorded by its own dispatch; the first forward after each synchronization and the
+    first two rounds are left out."""
+    import numpy as np
+    import torch
+    nf = sweeps * len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ng)] for _ in range(nf)]
+    with torch.cuda.stream(s):
+        for lst in evs:
+            for e in lst:
+                e.record(s)
+    s.synchronize()
+    handles = [[e.cuda_event for e in lst] for lst in evs]
+    acc, n = np.zeros(ng), 0
+    with torch.cuda.stream(s):
+        for r in range(rounds + 2):
+            for f in range(nf):
+                i = f % len(layers)
+                B.moe_latent_forward_timed(layers[i].handle, rows, xs[i].data_ptr(), outs[i].data_ptr(), handles[f])
+            s.synchronize()
+            if r < 2:
+                continue
+            for f in range(1, nf):
+                for g in range(ng):
+                    acc[g] += evs[f][2 * g].elapsed_time(evs[f][2 * g + 1]) * 1e3
+                n += 1
+    return acc / n
 
 
 def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):

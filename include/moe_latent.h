@@ -161,6 +161,16 @@ int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in
  * launch, or no such group), or -1 for an invalid handle or rows. */
 int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
 
+/* A forward like moe_latent_forward, whose launch i also records the start and the end of
+ * its own kernel into events[2 i] and events[2 i + 1] (hipEvent_t handles the caller created
+ * with timing enabled; the timestamps come from the kernel's dispatch itself, no extra
+ * packets), so that hipEventElapsedTime gives each launch's duration inside the forward. For
+ * per-launch timing; it cannot be captured in a graph. n_events must be at least twice the
+ * number of launch groups of the pass (MOE_ERR_INVALID_ARG otherwise); a launch with no work
+ * leaves its two events untouched. */
+int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
+                             void *const *events, int32_t n_events);
+
 /* Change the stream later forwards are enqueued on (e.g. a graph-capture stream). */
 int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
 

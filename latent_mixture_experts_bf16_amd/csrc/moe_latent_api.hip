@@ -7,6 +7,7 @@
 // failed load created are released). Here: configuration, then tensor descriptors, then the
 // device, then allocation; every failure frees what was allocated and returns a named code.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <atomic>
 #include <cstdarg>
@@ -424,26 +425,32 @@ static int plan_launches(const LayerParams &p, Launch *out) {
     return n;
 }
 
+// ev0, ev1: when set, the kernel's start and end are recorded into them by its own dispatch
 template <int KF, int KL, bool WIDE>
-static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st) {
+static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const int lo = p.item_base[l.first], hi = p.item_base[l.last + 1];
-    if (hi > lo)
+    if (hi <= lo) return;
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1, 0,
+                              p, lo, hi, l.rev);
+    else
         hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, l.rev);
 }
 
-static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st) {
+static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr) {
     const bool wide = p.D > 2048 || p.I > 2048;
     switch (l.kernel) {
-        case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st); break;
+        case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st, ev0, ev1); break;
         case K_ROUTE_UP:
-            if (wide) launch_kernel<ST_ROUTE, ST_UP, true>(p, l, st);
-            else launch_kernel<ST_ROUTE, ST_UP, false>(p, l, st);
+            if (wide) launch_kernel<ST_ROUTE, ST_UP, true>(p, l, st, ev0, ev1);
+            else launch_kernel<ST_ROUTE, ST_UP, false>(p, l, st, ev0, ev1);
             break;
         case K_UP_DOWN:
-            if (wide) launch_kernel<ST_UP, ST_DOWN, true>(p, l, st);
-            else launch_kernel<ST_UP, ST_DOWN, false>(p, l, st);
+            if (wide) launch_kernel<ST_UP, ST_DOWN, true>(p, l, st, ev0, ev1);
+            else launch_kernel<ST_UP, ST_DOWN, false>(p, l, st, ev0, ev1);
             break;
-        default: launch_kernel<ST_FC2, ST_FC2, false>(p, l, st); break;
+        default: launch_kernel<ST_FC2, ST_FC2, false>(p, l, st, ev0, ev1); break;
     }
 }
 
@@ -536,6 +543,26 @@ extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void
     enqueue(h, p, group);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
+                                        void *const *events, int32_t n_events) {
+    if (int rc = check_io(h, rows, hidden_in, out)) return rc;
+    LayerParams p = h->base;
+    p.x = (const uint16_t *)hidden_in;
+    p.out = (uint16_t *)out;
+    plan_items(p, rows);
+    Launch ls[8];
+    const int n = plan_launches(p, ls);
+    if (!events || n_events < 2 * n)
+        return fail(MOE_ERR_INVALID_ARG, "events: %d given, 2 per launch group (%d groups) needed", n_events, n);
+    for (int i = 0; i < 2 * n; ++i)
+        if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
+    for (int i = 0; i < n; ++i) launch_one(p, ls[i], h->stream, (hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    h->last_rows = rows;
     return MOE_OK;
 }
 

@@ -141,5 +141,6 @@ def test_valid_descriptors_reach_the_device_check():
 def test_null_arguments():
     assert B.lib().moe_latent_create(None, None, None, None) == 1
     assert B.lib().moe_latent_forward(None, 1, None, None) == 1
+    assert B.lib().moe_latent_forward_timed(None, 1, None, None, None, 0) == 1
     B.moe_latent_destroy(None)   # NULL-safe
     assert B.lib().moe_latent_status(None) == 1

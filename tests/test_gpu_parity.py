@@ -323,6 +323,35 @@ def test_repeated_forwards_are_deterministic():
     lay.close()
 
 
+def test_timed_forward_equals_forward_and_records_each_launch():
+    """The per-launch timed forward writes the same output as a plain forward, its events
+    hold a positive duration for every launch group, and too few events are refused."""
+    from latent_mixture_experts_bf16_amd import binding as B
+    dims, arrays = workload(1)
+    lay = _LY().DeviceLayer(dims, arrays, 1)
+    xd = _x_dev(dims, arrays["x"])
+    ref = torch.empty_like(xd)
+    lay.forward(xd, ref)
+    torch.cuda.synchronize()
+    ng = sum(1 for g in range(8) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
+    assert ng == 4
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ng)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    handles = [e.cuda_event for e in evs]
+    out = torch.empty_like(xd)
+    B.moe_latent_forward_timed(lay.handle, 1, xd.data_ptr(), out.data_ptr(), handles)
+    torch.cuda.synchronize()
+    lay.status()
+    assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy())
+    for g in range(ng):
+        assert evs[2 * g].elapsed_time(evs[2 * g + 1]) > 0.0, g
+    with pytest.raises(B.MoeError):
+        B.moe_latent_forward_timed(lay.handle, 1, xd.data_ptr(), out.data_ptr(), handles[:-1])
+    lay.close()
+
+
 def test_sixteen_rows_equal_sixteen_single_row_passes():
     """The 16-row E=496 workload (prompt rows pushed through the decode kernels 16 at a time,
     TensorFold pull request 1038, «Not yet / next»): each row equals its own 1-row pass bit
