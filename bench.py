@@ -66,6 +66,11 @@ def parse():
     ap.add_argument("--summarize-stats", metavar="DIR",
                     help="turn a rocprofv3 --kernel-trace --stats output folder into a text summary "
                          "written to --stats-out")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="turn a rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 output folder into "
+                         "the MFMA summary --mfma-out")
+    ap.add_argument("--mfma-out")
+    ap.add_argument("--mfma-workload", default="")
     ap.add_argument("--pmc-out")
     ap.add_argument("--stats-out")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
@@ -190,6 +195,8 @@ def main():
         return summarize_pmc(args)
     if args.summarize_stats:
         return summarize_stats(args)
+    if args.summarize_mfma:
+        return summarize_mfma(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the layer's sharding "
@@ -204,8 +211,11 @@ def main():
     from latent_mixture_experts_bf16_amd import synth
 
     wl = synth.WORKLOADS[args.config]
+    if len(wl.layers) != 1 and args.profile_steps:
+        return profile_stack(args, B, LY, synth)
     if len(wl.layers) != 1:
-        print("bench.py times single-layer workloads (configs 0-3)", file=sys.stderr)
+        print("bench.py times single-layer workloads (configs 0-3); the stack is timed by the rows "
+              "sweep", file=sys.stderr)
         return 2
     dims = wl.layers[0]
     rows = wl.rows
@@ -278,14 +288,20 @@ def main():
     with torch.cuda.stream(s):
         run_steps(args.warmup)
     s.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps in NBLOCK blocks, each bracketed by events: the whole span gives the
+    # value, the blocks its spread
+    nblock = 5 if args.steps >= 5 else 1
+    bsteps = [args.steps // nblock + (1 if b < args.steps % nblock else 0) for b in range(nblock)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nblock + 1)]
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
-        e0.record(s)
-        run_steps(args.steps)
-        e1.record(s)
+        evs[0].record(s)
+        for b in range(nblock):
+            run_steps(bsteps[b])
+            evs[b + 1].record(s)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
+    ms_total = evs[0].elapsed_time(evs[nblock])
+    block_us = sorted(evs[b].elapsed_time(evs[b + 1]) * 1e3 / bsteps[b] for b in range(nblock))
     for lay in layers:
         lay.status()
     ms_step = ms_total / args.steps
@@ -344,8 +360,30 @@ def main():
                 traffic_note = f"{kname} missing from the counter summary"
     print(f"[bench] groups: {json.dumps(group_stats)}", file=sys.stderr, flush=True)
 
+    # a plain read-only stream over 1 GiB on the same box: the measured reference beside the
+    # 8 TB/s peak (never instead of it)
+    stream_ref = None
+    if rows == 1:
+        buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        nb = buf.numel() * 4
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                B.moe_latent_stream_read(buf.data_ptr(), nb, sink.data_ptr(), s.cuda_stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(20):
+                B.moe_latent_stream_read(buf.data_ptr(), nb, sink.data_ptr(), s.cuda_stream)
+            b.record(s)
+        torch.cuda.synchronize()
+        gbps_ref = nb * 20 / (a.elapsed_time(b) * 1e-3) / 1e9
+        stream_ref = {"gbps": round(gbps_ref, 1), "frac_of_peak": round(gbps_ref / HBM_PEAK_GBPS, 4),
+                      "bytes": nb, "kernel": "moe_stream_read_kernel (read-only, 16-byte loads, 2048 workgroups)"}
+        del buf, sink
+
     # parity of instance 0 against the oracle, and the oracle timed on this host
     cpu = None
+    cpu_single = None
     parity = None
     if not args.no_cpu_baseline:
         from oracle import oracle as O
@@ -367,8 +405,10 @@ def main():
         parity = {"routing_bitwise": bool(np.array_equal(idx0, ref["idx"]) and
                                           np.array_equal(w0.view(np.uint32), ref["w"].view(np.uint32))),
                   "rel_rms": rel_rms, "rel_max": rel_max}
-        cpu = {"value": round(rows * n / el, 3), "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} forwards of instance 0 ({rows} row(s) each), single-threaded plain C, {el:.1f} s"}
+        cpu_single = {"value": round(rows * n / el, 3), "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
+                      "sample": f"{n} forwards of instance 0 ({rows} row(s) each), single-threaded plain C, "
+                                f"{el:.1f} s"}
+        cpu = cpu_parallel(args.config, args.cpu_seconds) or cpu_single
 
     line = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (% of roofline) at 1/16/64 rows",
@@ -396,6 +436,11 @@ def main():
         "launches": {v["name"]: {"us": v["us"], "us_alone": v["us_alone"], "bytes": v["bytes"], "gbps": v["gbps"]}
                      for v in group_stats.values()},
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu_single,
+        "host_cpu": host_cpu(),
+        "blocks": {"n": nblock, "us_per_step_median": round(float(np.median(block_us)), 3),
+                   "us_per_step_min": round(block_us[0], 3), "us_per_step_max": round(block_us[-1], 3)},
+        "stream_read_reference": stream_ref,
         "parity": parity,
     }
     for lay in layers:
@@ -406,6 +451,113 @@ def main():
         line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
     print(json.dumps(line), flush=True)
     return 0
+
+
+def profile_stack(args, B, LY, synth):
+    """The counter runs' workload for a multi-layer configuration: every layer of the stack
+    forwarded --profile-steps times, eagerly."""
+    import torch
+    wl = synth.WORKLOADS[args.config]
+    layers, xs, outs = [], [], []
+    for d, arrays in synth.workload_layers(args.config):
+        layers.append(LY.DeviceLayer(d, arrays, max_rows=wl.rows))
+        xs.append(LY.to_device(arrays["x"]))
+        outs.append(torch.empty_like(xs[-1]))
+        del arrays
+    for _ in range(args.profile_steps):
+        for lay, x, o in zip(layers, xs, outs):
+            lay.forward(x, o, wl.rows)
+    torch.cuda.synchronize()
+    for lay in layers:
+        lay.status()
+        lay.close()
+    print(f"[bench] profile workload done: {args.profile_steps} passes over {len(layers)} layers",
+          file=sys.stderr, flush=True)
+    return 0
+
+
+def summarize_mfma(args):
+    """MFMA utilisation (percent of SIMD cycles with the matrix core busy) and bf16 MFMA flops
+    of each layer kernel, from one rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 run."""
+    import numpy as np
+    rows = _csv_rows(args.summarize_mfma, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        if "moe_stage_kernel" not in name:
+            continue
+        k = "moe_stage_kernel<" + name.split("moe_stage_kernel<")[1].split(">")[0] + ">"
+        per.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    out = {}
+    for (k, c), v in sorted(per.items()):
+        out.setdefault(k, {"dispatches": len(v)})[c + "_mean"] = float(np.mean(v))
+    for k, v in out.items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16_mean" in v:
+            v["mfma_bf16_flops_per_dispatch"] = v["SQ_INSTS_VALU_MFMA_MOPS_BF16_mean"] * 512
+    summary = {"workload": args.mfma_workload, "kernel_source_sha256": source_hash(), "command": args.command,
+               "kernels": out}
+    with open(args.mfma_out, "w") as fh:
+        json.dump(summary, fh, indent=1)
+    print(json.dumps(summary, indent=1))
+    return 0
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
+_CPU_WORKER = r"""
+import sys, time
+sys.path.insert(0, sys.argv[1])
+from latent_mixture_experts_bf16_amd import synth
+from oracle import oracle as O
+d, arrays = next(synth.workload_layers(int(sys.argv[2])))
+seconds = float(sys.argv[3])
+n, t0 = 0, time.time()
+while True:
+    O.forward(d, arrays)
+    n += 1
+    if time.time() - t0 >= seconds:
+        break
+print(n, time.time() - t0, flush=True)
+"""
+
+
+def cpu_parallel(cfg, seconds, max_workers=16):
+    """The oracle as it stands, one copy per host core (at most 16): each child process draws
+    instance 0 and runs whole forwards for `seconds`; the children are separate programs
+    (nothing in them touches the GPU)."""
+    import subprocess
+    nw = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, "-c", _CPU_WORKER, ROOT, str(cfg), str(seconds)],
+                              stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, env=env)
+             for _ in range(nw)]
+    tok_s, n_tot = 0.0, 0
+    rows = None
+    for p in procs:
+        try:
+            out, _ = p.communicate(timeout=seconds * 4 + 120)
+            n, el = out.split()
+            tok_s += int(n) / float(el)
+            n_tot += int(n)
+        except Exception:   # a worker that failed or timed out leaves the parallel figure out
+            p.kill()
+            return None
+    from latent_mixture_experts_bf16_amd import synth
+    rows = synth.WORKLOADS[cfg].rows
+    return {"value": round(rows * tok_s, 3), "unit": "layer-tokens/s", "cores": nw, "kind": "oracle",
+            "sample": f"{nw} processes, each whole forwards of instance 0 ({rows} row(s)) for {seconds:.0f} s: "
+                      f"{n_tot} forwards in all, plain C, one thread each"}
 
 
 def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):

@@ -209,6 +209,17 @@ const char *moe_latent_last_error(void);
 /* Number of device allocations the library currently holds (all handles). */
 int32_t moe_latent_live_allocations(void);
 
+/* A plain read-only stream over device memory, the reference beside the published HBM peak
+ * that the measured bandwidth of the layer is judged against (mlx-bun 0.3.0
+ * decode-speed program, the bandwidth-wall model and its measurement discipline: what a
+ * pure read of the same bytes achieves on the same machine). Enqueues on hip_stream (NULL:
+ * the null stream) one launch that reads `bytes` bytes at src (device, 16-byte aligned,
+ * bytes a multiple of 16, at most 2^40) with 16-byte loads spread over the whole chip, and
+ * folds the data into *sink_dev (one device uint32, XOR-accumulated, so the reads are not
+ * elided). No allocation. MOE_ERR_INVALID_ARG for a NULL pointer, a misaligned src or a bad
+ * size. */
+int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *sink_dev, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

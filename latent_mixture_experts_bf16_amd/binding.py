@@ -82,6 +82,7 @@ def _load():
         "moe_latent_launch_group": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.c_int32]),
         "moe_latent_group_items": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32]),
         "moe_latent_forward_timed": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.POINTER(P), ctypes.c_int32]),
+        "moe_latent_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -94,7 +95,8 @@ _lib = _load()
 EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "moe_latent_set_stream",
             "moe_latent_set_variant", "moe_latent_get_routing", "moe_latent_read_stage",
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
-            "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed")
+            "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
+            "moe_latent_stream_read")
 
 
 def lib():
@@ -189,3 +191,7 @@ def moe_latent_forward_timed(h: int, rows: int, hidden_in: int, out: int, events
     """events: hipEvent_t handles (integers), two per launch group (start, end)."""
     arr = (ctypes.c_void_p * len(events))(*events)
     _check(_lib.moe_latent_forward_timed(h, rows, hidden_in, out, arr, len(events)))
+
+
+def moe_latent_stream_read(src: int, nbytes: int, sink_dev: int, stream: int = 0) -> None:
+    _check(_lib.moe_latent_stream_read(src, nbytes, sink_dev, stream))

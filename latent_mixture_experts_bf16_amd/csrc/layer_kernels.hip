@@ -1221,6 +1221,34 @@ template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, in
 template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int);
 template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int);
 
+// Read-only stream: n 16-byte units, 8 loads in flight per thread per round, grid-stride;
+// the data is folded into one XOR per workgroup so that the loads are kept.
+__global__ void __launch_bounds__(256) moe_stream_read_kernel(const uint4 *__restrict__ src, size_t n, uint32_t *sink) {
+    __shared__ uint32_t red[256];
+    const size_t stride = (size_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 7 * stride < n; i += 8 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = src[i + q * stride];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+    }
+    for (; i < n; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        uint32_t r = red[threadIdx.x] ^ red[threadIdx.x + 64] ^ red[threadIdx.x + 128] ^ red[threadIdx.x + 192];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) r ^= __shfl_xor(r, d, 64);
+        if (threadIdx.x == 0) atomicXor(sink, r);
+    }
+}
+
 // zero a small device buffer (the error flag) without a memset node in captured graphs
 __global__ void moe_clear_kernel(uint32_t *ctr, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;

@@ -22,6 +22,7 @@
 namespace moe {
 template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int rev);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
+__global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 }  // namespace moe
 
 using namespace moe;
@@ -563,6 +564,19 @@ extern "C" int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     h->last_rows = rows;
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *sink_dev, void *hip_stream) {
+    if (!src || !sink_dev) return fail(MOE_ERR_INVALID_ARG, "stream_read: src or sink is NULL");
+    if (((uintptr_t)src & 15) || (bytes & 15) || bytes == 0 || bytes > ((size_t)1 << 40))
+        return fail(MOE_ERR_INVALID_ARG, "stream_read: src must be 16-byte aligned and bytes a nonzero multiple of 16 "
+                    "up to 2^40 (%zu)", bytes);
+    // 8 workgroups of 256 threads per compute unit of the 256, each with 8 loads in flight
+    hipLaunchKernelGGL(moe_stream_read_kernel, dim3(2048), dim3(256), 0, (hipStream_t)hip_stream,
+                       (const uint4 *)src, bytes / 16, sink_dev);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream_read launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 

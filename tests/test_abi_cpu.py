@@ -142,5 +142,9 @@ def test_null_arguments():
     assert B.lib().moe_latent_create(None, None, None, None) == 1
     assert B.lib().moe_latent_forward(None, 1, None, None) == 1
     assert B.lib().moe_latent_forward_timed(None, 1, None, None, None, 0) == 1
+    # the stream reference refuses NULL, misaligned and odd sizes before touching a device
+    assert B.lib().moe_latent_stream_read(None, 16, None, None) == 1
+    assert B.lib().moe_latent_stream_read(8, 16, 64, None) == 1
+    assert B.lib().moe_latent_stream_read(16, 24, 64, None) == 1
     B.moe_latent_destroy(None)   # NULL-safe
     assert B.lib().moe_latent_status(None) == 1

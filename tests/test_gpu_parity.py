@@ -352,6 +352,19 @@ def test_timed_forward_equals_forward_and_records_each_launch():
     lay.close()
 
 
+def test_stream_read_reads_every_word_once():
+    """The read-only stream reference folds every 32-bit word of the buffer exactly once."""
+    from latent_mixture_experts_bf16_amd import binding as B
+    for nbytes in (16, 4096 + 48, (64 << 20) + 16 * 77):
+        rng = np.random.default_rng(nbytes)
+        host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+        src = torch.from_numpy(host.view(np.int32)).cuda()
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        B.moe_latent_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), 0)
+        torch.cuda.synchronize()
+        assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host)), nbytes
+
+
 def test_sixteen_rows_equal_sixteen_single_row_passes():
     """The 16-row E=496 workload (prompt rows pushed through the decode kernels 16 at a time,
     TensorFold pull request 1038, «Not yet / next»): each row equals its own 1-row pass bit
