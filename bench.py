@@ -378,7 +378,8 @@ def main():
         torch.cuda.synchronize()
         gbps_ref = nb * 20 / (a.elapsed_time(b) * 1e-3) / 1e9
         stream_ref = {"gbps": round(gbps_ref, 1), "frac_of_peak": round(gbps_ref / HBM_PEAK_GBPS, 4),
-                      "bytes": nb, "kernel": "moe_stream_read_kernel (read-only, 16-byte loads, 2048 workgroups)"}
+                      "bytes": nb, "kernel": "moe_stream_read_kernel (read-only, 16-byte nontemporal loads, one workgroup "
+                                "per compute unit, 8 loads in flight per thread)"}
         del buf, sink
 
     # parity of instance 0 against the oracle, and the oracle timed on this host

@@ -214,7 +214,8 @@ int32_t moe_latent_live_allocations(void);
  * decode-speed program, the bandwidth-wall model and its measurement discipline: what a
  * pure read of the same bytes achieves on the same machine). Enqueues on hip_stream (NULL:
  * the null stream) one launch that reads `bytes` bytes at src (device, 16-byte aligned,
- * bytes a multiple of 16, at most 2^40) with 16-byte loads spread over the whole chip, and
+ * bytes a multiple of 16, at most 2^40) with 16-byte nontemporal loads, one workgroup per
+ * compute unit, and
  * folds the data into *sink_dev (one device uint32, XOR-accumulated, so the reads are not
  * elided). No allocation. MOE_ERR_INVALID_ARG for a NULL pointer, a misaligned src or a bad
  * size. */

@@ -1233,7 +1233,8 @@ template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, in
 template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int);
 template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int);
 
-// Read-only stream: n 16-byte units, 8 loads in flight per thread per round, grid-stride;
+// Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
+// grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);
 // the data is folded into one XOR per workgroup so that the loads are kept.
 __global__ void __launch_bounds__(256) moe_stream_read_kernel(const uint4 *__restrict__ src, size_t n, uint32_t *sink) {
     __shared__ uint32_t red[256];
@@ -1243,7 +1244,7 @@ __global__ void __launch_bounds__(256) moe_stream_read_kernel(const uint4 *__res
     for (; i + 7 * stride < n; i += 8 * stride) {
         uint4 v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = src[i + q * stride];
+        for (int q = 0; q < 8; ++q) v[q] = ld_weight16(src + i + q * stride);
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
     }

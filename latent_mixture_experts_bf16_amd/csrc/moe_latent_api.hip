@@ -572,8 +572,12 @@ extern "C" int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *s
     if (((uintptr_t)src & 15) || (bytes & 15) || bytes == 0 || bytes > ((size_t)1 << 40))
         return fail(MOE_ERR_INVALID_ARG, "stream_read: src must be 16-byte aligned and bytes a nonzero multiple of 16 "
                     "up to 2^40 (%zu)", bytes);
-    // 8 workgroups of 256 threads per compute unit of the 256, each with 8 loads in flight
-    hipLaunchKernelGGL(moe_stream_read_kernel, dim3(2048), dim3(256), 0, (hipStream_t)hip_stream,
+    // one workgroup of 256 threads per compute unit, each thread with 8 loads in flight
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    hipLaunchKernelGGL(moe_stream_read_kernel, dim3(cus), dim3(256), 0, (hipStream_t)hip_stream,
                        (const uint4 *)src, bytes / 16, sink_dev);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream_read launch: %s", hipGetErrorString(e));
