@@ -140,8 +140,10 @@ int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, voi
 /* Release the workspace and the handle (NULL-safe). Synchronises the handle's stream. */
 void moe_latent_destroy(moe_latent_t *h);
 
-/* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (the last
- * gate workgroup routes the row); 1 routed expert up + shared down (first half); 2 routed
+/* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (its first
+ * workgroup routes the row once the gate workgroups have handed it their logits; that wait
+ * is bounded, and a timeout sets bit 8 of the device error flag, reported by
+ * moe_latent_status); 1 routed expert up + shared down (first half); 2 routed
  * expert down + shared down (second half); 3 combine + fc2 + shared + residual (each fc2
  * workgroup combines the slice of the expert outputs it reads; a non-latent layer combines
  * in group 2 instead). Multi-row pass: 0 as above without the route; 1 route (the

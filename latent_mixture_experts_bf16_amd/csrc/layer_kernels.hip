@@ -2,9 +2,11 @@
 //
 // A forward is a table of work items (tiles of each stage, see layer_plan.h) run as a short
 // chain of launches on one stream; stages that do not depend on each other share a launch,
-// and steps that need every item of a stage (route after the gate, schedule after the
-// route, combine after the experts of a block) are run by the last item to finish:
-//   one row:   [gate, fc1, shared up; route] -> [expert up, shared down A] ->
+// and steps that need every item of a stage (schedule after the route, the adding of a
+// split tile's parts, combine after the experts of a block) are run by the last item to
+// finish. The one exception: in a one-row pass the route item (the first item of the first
+// launch) waits, bounded, for the logits the gate items hand it.
+//   one row:   [route, gate, fc1, shared up] -> [expert up, shared down A] ->
 //              [expert down, shared down B] -> [combine + fc2 + shared + residual]
 //   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
 //              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]

@@ -9,7 +9,8 @@ namespace moe {
 // it»: gate gemv -> route -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj
 // -> + shared -> + residual). A stage only reads what earlier launches wrote, or what a
 // "last arriver" of the same launch reads after every item it depends on has counted itself
-// done (no item ever waits for another).
+// done. One item waits: the route item of a one-row pass, for the logits of the gate items
+// dispatched after it (bounded; see ctr_hand).
 enum Stage : int {
     ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; a one-row pass
                    // has one more item, first: the route item, which waits for the logits
@@ -96,7 +97,7 @@ struct LayerParams {
     int umax;              // slots enumerated by ST_UP / ST_DOWN items
     int up_nb, dn_nb;      // output rows of one routed up / down item
     int up_blocks, dn_blocks;
-    int single_row;        // rows == 1: the last gate item routes and writes the schedule
+    int single_row;        // rows == 1: the route item (first gate item) routes and writes the schedule
     int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)
     int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
     // one-row pass: each gate item hands its logits to the route item (the first item of the
