@@ -11,8 +11,9 @@
 //   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
 //              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]
 // One workgroup of 4 waves runs one item; a launch's items are sized (about 32-64 KB of
-// weights each) so that all of them are resident at once (up to four per compute unit,
-// three in the expert launches, whose LDS holds a 32 KB block of codes).
+// weights each) so that all of them are resident at once (three per compute unit: the
+// expert launches' LDS holds a 32 KB block of codes, and the dense tiles' registers hold four
+// steps of weights and their way into MFMA fragments).
 //
 // Arithmetic of each stage (TensorFold pull request 1038, «What's in it»: gate gemv ->
 // route top-k -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj -> +
@@ -654,7 +655,13 @@ enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
 
 template <int NW>
 struct DenseLds {
-    f32x4 part[NW][2][64];   // [wave][row tile][lane]
+    // per wave: one step's weights (16 rows x 128 inputs, rows 272 bytes apart) on their way
+    // from row runs to MFMA fragments; after the wave's last step, its partial sums
+    // [row tile][lane]
+    union WaveBuf {
+        uint4 wt[16 * 17];
+        f32x4 part[2][64];
+    } w[NW];
     // the item's slice of the input rows, [row][kpart], when it fits (the combine itself in
     // fc2 of a one-row pass)
     uint16_t xs[DENSE_XLDS];
@@ -666,6 +673,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 lds_ld16(const void *p) {
     const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void lds_st16(void *p, uint4 v) {
+    *(__attribute__((address_space(3))) u32x4 *)p = (u32x4){v.x, v.y, v.z, v.w};
 }
 __device__ __forceinline__ uint4 glb_ld16(const void *p) {
     const u32x4 v = *(const __attribute__((address_space(1))) u32x4 *)p;
@@ -715,10 +725,12 @@ __device__ __forceinline__ void dense_epilogue(const LayerParams &p, int epi, in
 
 // Item: part `split` (of `ks`) of K for outputs n0..n0+15 of W [N][K] (bf16, row-major)
 // against X [rows][K] (bf16), all rows. Inside the item K is split again over up to NW waves
-// in contiguous slices (each a multiple of 128); per 128 inputs each lane holds 4 pieces of
-// 8 consecutive k of one weight row and of one input row (k = 32 j + 8 grp for MFMA j), fed to
-// 4 MFMAs of 32. A wave
-// issues the loads of up to 4 such steps of its weight slice, then multiplies. The waves'
+// in contiguous slices (each a multiple of 128). A step of 128 inputs is 4 MFMAs of 32: lane
+// L holds 8 consecutive k of weight row L % 16 and of one input row (k = 32 j + 8 (L / 16) for
+// MFMA j). The weights are loaded in 256-byte row runs (load instruction i of a step: rows
+// 4i..4i+3, 16 lanes per row, streamed nontemporal) and rearranged into those fragments
+// through the wave's LDS buffer. A wave issues the loads of up to 4 steps of its weight
+// slice, then multiplies. The waves'
 // partial sums are joined in wave order; with ks > 1 the item's partial goes to the
 // workspace and the last of the ks items to finish adds them in split order and applies the
 // epilogue. For the fc2 of a one-row pass (p.inline_comb) the item first computes its slice
@@ -740,11 +752,13 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
     const bool inl = EPI == EPI_FC2 && p.inline_comb;
     // the input slice staged in LDS when it fits (always for a one-row fc2 pass that combines)
     const bool xl = inl || p.rows * kpart <= DENSE_XLDS;
-    // MFMA j of a step of 128 inputs takes inputs 32 j .. 32 j + 31: lane group grp holds
-    // 32 j + 8 grp .. + 7, so a load instruction reads 64 contiguous bytes of each of the 16
-    // rows (measured about 6 % faster than four scattered 16-byte pieces per row)
-    const uint16_t *wrow = W + (size_t)(n0 + nr) * K + kbase + wave * kw + 8 * grp;
+    // weight loads: lane (16 r + c) reads inputs 8c..8c+7 of the step from row 4i + r in
+    // instruction i (whole 256-byte runs of a row: measured about 10 % faster than 64 bytes
+    // of each of 16 rows, the LDS round trip included)
+    const int rr = lane >> 4, kk = lane & 15;
+    const uint16_t *wrow = W + (size_t)(n0 + rr) * K + kbase + wave * kw + 8 * kk;
     const size_t xoff = (size_t)kbase + wave * kw + 8 * grp;
+    uint4 *wt = L.w[wave].wt;
 
     uint4 a[4][4];
     auto load_w = [&](int i0) {
@@ -752,8 +766,8 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
         for (int q = 0; q < 4; ++q) {
             if (i0 + q < nit) {
                 const uint16_t *wp = wrow + 128 * (i0 + q);
-                a[q][0] = *(const uint4 *)wp; a[q][1] = *(const uint4 *)(wp + 32);
-                a[q][2] = *(const uint4 *)(wp + 64); a[q][3] = *(const uint4 *)(wp + 96);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[q][i] = ld_weight16(wp + (size_t)(4 * i) * K);
             }
         }
     };
@@ -798,6 +812,14 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
                 for (int q = 0; q < 4; ++q) {
                     if (i0 + q < nit) {
                         const int kb = 128 * (i0 + q);
+                        // the step's weights through the wave's buffer: written as loaded,
+                        // read as fragments (MFMA j: row nr, inputs 32 j + 8 grp ..); LDS
+                        // accesses of a wave are carried out in order
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) lds_st16(&wt[(4 * i + rr) * 17 + kk], a[q][i]);
+                        uint4 f[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) f[j] = lds_ld16(&wt[nr * 17 + 4 * j + grp]);
 #pragma unroll
                         for (int t = 0; t < RT; ++t) {
                             const int row = (rt0 + t) * 16 + nr;
@@ -815,13 +837,13 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
                                     }
                                 }
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, a[q][0]), __builtin_bit_cast(bf16x8, b0), acc[t], 0, 0, 0);
+                                    __builtin_bit_cast(bf16x8, f[0]), __builtin_bit_cast(bf16x8, b0), acc[t], 0, 0, 0);
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, a[q][1]), __builtin_bit_cast(bf16x8, b1), acc[t], 0, 0, 0);
+                                    __builtin_bit_cast(bf16x8, f[1]), __builtin_bit_cast(bf16x8, b1), acc[t], 0, 0, 0);
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, a[q][2]), __builtin_bit_cast(bf16x8, b2), acc[t], 0, 0, 0);
+                                    __builtin_bit_cast(bf16x8, f[2]), __builtin_bit_cast(bf16x8, b2), acc[t], 0, 0, 0);
                                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    __builtin_bit_cast(bf16x8, a[q][3]), __builtin_bit_cast(bf16x8, b3), acc[t], 0, 0, 0);
+                                    __builtin_bit_cast(bf16x8, f[3]), __builtin_bit_cast(bf16x8, b3), acc[t], 0, 0, 0);
                             }
                         }
                     }
@@ -832,13 +854,13 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
             }
         }
 #pragma unroll
-        for (int t = 0; t < RT; ++t) L.part[wave][t][lane] = acc[t];
+        for (int t = 0; t < RT; ++t) L.w[wave].part[t][lane] = acc[t];
         __syncthreads();
         // wave t finishes row tile rt0 + t: partials joined in wave order
         if (wave < RT && rt0 + wave < nrt) {
             const int t = wave;
-            f32x4 v = L.part[0][t][lane];
-            for (int q = 1; q < nsplit; ++q) v = v + L.part[q][t][lane];
+            f32x4 v = L.w[0].part[t][lane];
+            for (int q = 1; q < nsplit; ++q) v = v + L.w[q].part[t][lane];
             const int row = (rt0 + t) * 16 + nr;
             if (row < p.rows) {
 #pragma unroll
@@ -1214,10 +1236,13 @@ __device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds
     }
 }
 
-// Waves per SIMD the register allocation aims for: what the kernel's LDS allows (expert
-// stages: 3), and 2 for fc2 (one item per compute unit).
+// Waves per SIMD the register allocation aims for: 3 (three items per compute unit: what
+// the expert stages' LDS allows, and enough for every item of the first launch at once), and
+// 2 for fc2 (one item per compute unit).
 constexpr int waves_target(int first, int last, bool wide) {
-    return first == ST_FC2 ? 2 : (first <= ST_DOWN && last >= ST_UP) ? 3 : 4;
+    (void)last;
+    (void)wide;
+    return first == ST_FC2 ? 2 : 3;
 }
 
 // Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST]; with rev

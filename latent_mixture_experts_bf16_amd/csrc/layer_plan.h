@@ -50,7 +50,7 @@ enum : int {
     SCH_COUNT = SCH_PAIRS + MAX_ROWS * MAX_TOPK,
 };
 
-constexpr int WG_THREADS = 256;   // 4 waves of 64 in every item (four items per CU at once)
+constexpr int WG_THREADS = 256;   // 4 waves of 64 in every item (three items per CU at once)
 constexpr int EXPERT_LDS_CODES = 32768;   // LDS bytes for one expert item's codes
 constexpr int EXPERT_LDS_SCALES = 2048;   // ... and for its scales (and again its biases)
 constexpr int EXPERT_MAX_BLOCK = 64;      // output rows of one expert item at most
