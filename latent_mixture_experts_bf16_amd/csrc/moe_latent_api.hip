@@ -20,7 +20,7 @@
 #include "layer_plan.h"
 
 namespace moe {
-template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int rev);
+template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 }  // namespace moe
@@ -399,23 +399,22 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 }
 
 // One launch of a forward: the items of stages [first, last], run by the kernel instance
-// `kernel` (its template range covers them); rev: the last stage's items are dispatched
-// first.
+// `kernel` (its template range covers them), dispatched in table order.
 enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2 };
 struct Launch {
-    int first, last, kernel, rev;
+    int first, last, kernel;
 };
 
 // The launches of one forward, in order (see layer_kernels.hip). Returns their number.
 static int plan_launches(const LayerParams &p, Launch *out) {
     int n = 0;
-    auto add = [&](int f, int l, int k, int rev = 0) { out[n++] = Launch{f, l, k, rev}; };
+    auto add = [&](int f, int l, int k) { out[n++] = Launch{f, l, k}; };
     if (p.single_row) {
-        // the routed expert items (on the critical path) are dispatched before the shared
-        // expert's down items that fill the rest of the machine
+        // the shared expert's 128 KB down items are dispatched before the routed expert items
+        // (measured 0.4 us faster per forward than the other order)
         add(ST_GATE, ST_SHUP, K_GATE_SHUP);
-        add(ST_ROUTE, ST_UP, K_ROUTE_UP, 1);
-        add(ST_SHDN_B, ST_DOWN, K_UP_DOWN, 1);
+        add(ST_ROUTE, ST_UP, K_ROUTE_UP);
+        add(ST_SHDN_B, ST_DOWN, K_UP_DOWN);
     } else {
         add(ST_GATE, ST_SHUP, K_GATE_SHUP);
         add(ST_ROUTE, ST_SHDN_A, K_ROUTE_UP);
@@ -433,9 +432,9 @@ static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st,
     if (hi <= lo) return;
     if (ev0 || ev1)
         hipExtLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1, 0,
-                              p, lo, hi, l.rev);
+                              p, lo, hi);
     else
-        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, l.rev);
+        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi);
 }
 
 static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0 = nullptr,
