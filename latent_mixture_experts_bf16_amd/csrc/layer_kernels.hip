@@ -444,23 +444,47 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     }
     __syncthreads();
     if (grouped) {
-        for (int g = tid; g < G; g += NT) {
-            const float gam = per > 1 ? L.b[L.top[g][0]] + L.b[L.top[g][1]] : L.b[L.top[g][0]];
-            L.gkey[g] = rank_key(gam, g);
-        }
-        __syncthreads();
-        // kept groups: rank < TG
-        for (int g = tid; g < G; g += NT) L.keep[g] = count_greater(L.gkey, G, L.gkey[g]) < p.TG;
-        __syncthreads();
         // candidates: a pick is among the top_k of its own group, so only those members of the
         // kept groups enter; candidate slot = (kept groups before g) * KK + rank in the group
         const int KK = p.K < per ? p.K : per;
-        for (int e = tid; e < E; e += NT) {
-            const int g = e / per, rank = L.inr[e];
-            if (L.keep[g] && rank < KK) {
-                int before = 0;
-                for (int h = 0; h < g; ++h) before += L.keep[h];
-                L.ckey[before * KK + rank] = L.key[e];
+        if (G <= 64) {
+            // up to 64 groups: every wave scores the groups itself, lane g taking group g, and
+            // ranks them with lane reads, so the kept groups are a mask in every wave and no
+            // barrier is needed before the candidates
+            const int lane = tid & 63;
+            uint64_t gk = 0;
+            if (lane < G) {
+                const float gam = per > 1 ? L.b[L.top[lane][0]] + L.b[L.top[lane][1]] : L.b[L.top[lane][0]];
+                gk = rank_key(gam, lane);
+            }
+            int c = 0;
+            for (int h = 0; h < G; ++h) {
+                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gk >> 32), h) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gk, h);
+                c += o > gk;
+            }
+            const uint64_t keepm = __ballot(lane < G && c < p.TG);
+            for (int e = tid; e < E; e += NT) {
+                const int g = e / per, rank = L.inr[e];
+                if (((keepm >> g) & 1ull) && rank < KK)
+                    L.ckey[__popcll(keepm & ((1ull << g) - 1ull)) * KK + rank] = L.key[e];
+            }
+        } else {
+            for (int g = tid; g < G; g += NT) {
+                const float gam = per > 1 ? L.b[L.top[g][0]] + L.b[L.top[g][1]] : L.b[L.top[g][0]];
+                L.gkey[g] = rank_key(gam, g);
+            }
+            __syncthreads();
+            // kept groups: rank < TG
+            for (int g = tid; g < G; g += NT) L.keep[g] = count_greater(L.gkey, G, L.gkey[g]) < p.TG;
+            __syncthreads();
+            for (int e = tid; e < E; e += NT) {
+                const int g = e / per, rank = L.inr[e];
+                if (L.keep[g] && rank < KK) {
+                    int before = 0;
+                    for (int h = 0; h < g; ++h) before += L.keep[h];
+                    L.ckey[before * KK + rank] = L.key[e];
+                }
             }
         }
         __syncthreads();
