@@ -389,8 +389,9 @@ struct RouteLds {
 // Item: one row (TensorFold pull request 1038, «Per operator and row invariance»:
 // group_expert_select at k = 9; pull request 1295, «What this changes»: sigmoid top-8 with
 // per-expert norm and sum). Every selection is by rank: an element's rank is the number of
-// elements whose 64-bit key is larger, counted by the element's own thread from LDS (keys
-// are unique, so ranks are a permutation and no thread waits on another's choice).
+// elements whose 64-bit key is larger, counted by the element's own thread from LDS (group
+// keys, up to 64 groups: by the group's lane of every wave, from the other lanes) -- keys
+// are unique, so ranks are a permutation and no thread waits on another's choice.
 template <int NT>
 __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds<NT> &L) {
     const int tid = threadIdx.x;
