@@ -652,11 +652,16 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (ui
 __device__ __forceinline__ void combine4(const LayerParams &p, int r, int d, float *out) {
     float w[MAX_TOPK];
     uint2 v[MAX_TOPK];
+    // picks past K load nothing (the branches are uniform; the loads still go out together)
 #pragma unroll
     for (int j = 0; j < MAX_TOPK; ++j) {
-        const size_t pr = (size_t)r * p.K + (j < p.K ? j : p.K - 1);
-        w[j] = p.wts[pr];
-        v[j] = *(const uint2 *)(p.eout + pr * p.D + d);
+        w[j] = 0.0f;
+        v[j] = make_uint2(0u, 0u);
+        if (j < p.K) {
+            const size_t pr = (size_t)r * p.K + j;
+            w[j] = p.wts[pr];
+            v[j] = *(const uint2 *)(p.eout + pr * p.D + d);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
