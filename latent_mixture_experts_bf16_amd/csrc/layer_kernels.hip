@@ -1275,25 +1275,27 @@ constexpr int waves_target(int first, int last, bool wide) {
     return first == ST_FC2 ? 2 : 3;
 }
 
-// Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST], workgroup b
-// taking item lo + b (the hardware dispatches workgroups in index order, so the earlier
-// stage's items start first).
+// Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST]. The hardware
+// dispatches workgroups in index order: workgroups 0 .. pre - 1 take items mid .. mid + pre
+// - 1, the next ones items lo .. mid - 1, the rest items mid + pre .. hi - 1 (pre = 0: table
+// order).
 template <int FIRST, int LAST, bool WIDE>
 __global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_target(FIRST, LAST, WIDE), 8)))
-moe_stage_kernel(LayerParams p, int lo, int hi) {
+moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre) {
     __shared__ typename StageLds<FIRST, LAST, WIDE>::U lds;
     __shared__ int s_flag;
-    const int it = lo + (int)blockIdx.x;
+    const int b = (int)blockIdx.x;
+    const int it = b < pre ? mid + b : b < pre + (mid - lo) ? lo + b - pre : lo + b;
     if (it >= hi) return;
     dispatch<FIRST, LAST, WIDE, FIRST>(p, it, lds, &s_flag);
 }
 
-template __global__ void moe_stage_kernel<ST_GATE, ST_SHUP, false>(LayerParams, int, int);
-template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, false>(LayerParams, int, int);
-template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true>(LayerParams, int, int);
-template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, int, int);
-template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int);
-template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int);
+template __global__ void moe_stage_kernel<ST_GATE, ST_SHUP, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int, int);
 
 // Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
 // grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);
