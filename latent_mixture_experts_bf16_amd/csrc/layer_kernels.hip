@@ -920,14 +920,16 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
 // ------------------------------------------------------------------ routed experts (4-bit)
 
 // LDS of one expert item: a block of NB output rows' codes, scales and biases (NB chosen on
-// the host so that they fit), and the current pair's input row (16-bit values). XMAX: the
-// widest input row (2048, or 6144 in the wide variant).
+// the host so that they fit), and the input rows (16-bit values) of the pairs in work: two
+// rows of up to 2048 inputs, or one wider row in the wide variant. XMAX: the widest input row
+// (2048, or 6144 in the wide variant).
 template <int XMAX>
 struct ExpertLds {
+    static constexpr int XROWS = XMAX <= 2048 ? 2 : 1;
     uint4 q[EXPERT_LDS_CODES / 16];
     uint16_t s[EXPERT_LDS_SCALES / 2];
     uint16_t b[EXPERT_LDS_SCALES / 2];
-    uint4 x[XMAX / 8];
+    uint4 x[XROWS * XMAX / 8];
 };
 
 // Copy `units` 16-byte units from global src to LDS dst with direct global->LDS loads
@@ -1017,6 +1019,29 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, int i) {
     }
 }
 
+// Chunk c (32 inputs) of an input row in LDS as packed 16-bit pairs (x[8j+i], x[8j+i+4]),
+// i < 4 (the order code_pair decodes the codes in); returns the chunk's sum.
+template <bool F16>
+__device__ __forceinline__ float x_chunk(const uint4 *x, int c, uint32_t *xq) {
+    uint32_t xw[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const uint4 v4 = lds_ld16(&x[4 * c + q4]);
+        xw[4 * q4] = v4.x; xw[4 * q4 + 1] = v4.y; xw[4 * q4 + 2] = v4.z; xw[4 * q4 + 3] = v4.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        xq[4 * j] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x05040100u);
+        xq[4 * j + 1] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x07060302u);
+        xq[4 * j + 2] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x05040100u);
+        xq[4 * j + 3] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x07060302u);
+    }
+    float sx = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sx = dot2<F16>(F16 ? 0x3C003C00u : 0x3F803F80u, xw[k], sx);
+    return sx;
+}
+
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
 // pair (row, pick) of that slot. The block's 4-bit codes, scales and biases and the first
 // pair's input row are staged in LDS (all in flight at once; every weight byte is read from
@@ -1025,6 +1050,9 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w, int i) {
 // chunks t, t + P, ... (at most 4): it keeps their inputs in registers as packed pairs and
 // adds, per row and chunk, scale * sum(q * x) + bias * sum(x), the products summed by
 // 2-element dot products in fp32; reduce_rows then joins the P lanes of each row.
+// Where two pairs remain (and two input rows fit in LDS), they go through the block together:
+// each code word is decoded once for both, and every (row, pair) sum takes the same operations
+// in the same order as it does alone.
 template <bool UP, int XMAX, bool F16>
 __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1065,9 +1093,20 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     // row, so each read instruction of a wave takes 1 KB of consecutive LDS (no bank
     // conflicts); otherwise row-major (row * C + chunk).
     const bool tiled = nch * P == C && RG * NG == NB;
+    const int xu = Kin >> 3;   // 16-byte units of one input row
+    auto pair_at = [&](int j) {
+        const int q = p.sched[SCH_PAIRS + off + j];
+        return q < 0 || q >= NP ? NP - 1 : q;   // never for a valid schedule
+    };
+    auto put = [&](int q, int n, float acc) {
+        if (UP) p.eact[(size_t)q * p.I + n] = f2act(F16, relu_sq(F16, rnd(F16, acc)));
+        else if (p.inline_comb) p.eout[(size_t)q * p.D + n] = f2act(F16, acc);   // read next launch
+        else st_shared16(p.eout + (size_t)q * p.D + n, f2act(F16, acc));   // combined in this one
+    };
+    constexpr bool PAIR2 = ExpertLds<XMAX>::XROWS == 2;
     stage_lds<AUX_NT>((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
     stage_lds<AUX_NT>((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
-    stage_lds((const uint4 *)xrow(pr), L.x, Kin >> 3);
+    stage_lds((const uint4 *)xrow(pr), L.x, xu);
     if (tiled) {
         const uint4 *src = (const uint4 *)Q;
         const int lp = __builtin_ctz(P), lg = __builtin_ctz(NG), lr = __builtin_ctz(RG);   // powers of two
@@ -1082,16 +1121,74 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     } else {
         stage_lds<AUX_NT>((const uint4 *)Q, L.q, NB * C);
     }
+    int pr2 = 0;
+    if (PAIR2 && R >= 2) {   // the second pair's row, its index read while the codes are in flight
+        pr2 = pair_at(1);
+        stage_lds((const uint4 *)xrow(pr2), L.x + xu, xu);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < R;) {
+        const bool two = PAIR2 && R - r >= 2;
         if (r > 0) {
-            pr = p.sched[SCH_PAIRS + off + r];
-            if (pr < 0 || pr >= NP) pr = NP - 1;
-            __syncthreads();   // every lane is done with the previous input row
-            stage_lds((const uint4 *)xrow(pr), L.x, Kin >> 3);
+            pr = pair_at(r);
+            if (two) pr2 = pair_at(r + 1);
+            __syncthreads();   // every lane is done with the previous input rows
+            stage_lds((const uint4 *)xrow(pr), L.x, xu);
+            if (two) stage_lds((const uint4 *)xrow(pr2), L.x + xu, xu);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+        }
+        if (two) {
+            for (int rb = 0; rb < RG; rb += 2) {
+                float va[2] = {0.0f, 0.0f}, vb[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int m = 0; m < XCH; ++m) {
+                    const int c = t + P * m;
+                    if (m < nch && c < C) {
+                        uint32_t qa[16], qb[16];
+                        const float sa = x_chunk<F16>(L.x, c, qa), sb = x_chunk<F16>(L.x + xu, c, qb);
+                        uint4 qv[2];
+                        float sc[2], bi[2];
+#pragma unroll
+                        for (int ii = 0; ii < 2; ++ii) {
+                            int nl = g * RG + rb + ii;
+                            nl = nl < NB ? nl : NB - 1;
+                            qv[ii] = lds_ld16(&L.q[tiled ? ((m * RG + rb + ii) * NG + g) * P + t : nl * C + c]);
+                            sc[ii] = bf2f(L.s[nl * G64 + (c >> 1)]);
+                            bi[ii] = bf2f(L.b[nl * G64 + (c >> 1)]);
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < 2; ++ii) {
+                            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const uint32_t w = j == 0 ? qv[ii].x : j == 1 ? qv[ii].y : j == 2 ? qv[ii].z : qv[ii].w;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const uint32_t cp = code_pair<F16>(w, i);
+                                    a0 = dot2<F16>(cp, qa[4 * j + i], a0);
+                                    a1 = dot2<F16>(cp, qb[4 * j + i], a1);
+                                }
+                            }
+                            const float bb = F16 ? bi[ii] : __builtin_fmaf(-128.0f, sc[ii], bi[ii]);
+                            va[ii] = __builtin_fmaf(sc[ii], a0, va[ii]);
+                            va[ii] = __builtin_fmaf(bb, sa, va[ii]);
+                            vb[ii] = __builtin_fmaf(sc[ii], a1, vb[ii]);
+                            vb[ii] = __builtin_fmaf(bb, sb, vb[ii]);
+                        }
+                    }
+                }
+                const int rr = reduce_rows<2>(va, P, t);
+                reduce_rows<2>(vb, P, t);
+                const int nl = g * RG + rb + rr;
+                if ((t & (P / 2 - 1)) == 0 && nl < NB && rb + rr < RG) {
+                    put(pr, n0 + nl, va[0]);
+                    put(pr2, n0 + nl, vb[0]);
+                }
+            }
+            r += 2;
+            continue;
         }
         // the lane's chunks of the input row: packed 16-bit pairs (x[8j+i], x[8j+i+4]), i < 4,
         // matching the code pairs decoded below, and each chunk's sum
@@ -1158,14 +1255,9 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
             const int rr = reduce_rows<2>(v, P, t);
             // lane t holds row rb + rr; the lowest lane of those holding it stores it
             const int nl = g * RG + rb + rr;
-            if ((t & (P / 2 - 1)) == 0 && nl < NB && rb + rr < RG) {
-                const int n = n0 + nl;
-                const float acc = v[0];
-                if (UP) p.eact[(size_t)pr * p.I + n] = f2act(F16, relu_sq(F16, rnd(F16, acc)));
-                else if (p.inline_comb) p.eout[(size_t)pr * p.D + n] = f2act(F16, acc);   // read next launch
-                else st_shared16(p.eout + (size_t)pr * p.D + n, f2act(F16, acc));   // combined in this one
-            }
+            if ((t & (P / 2 - 1)) == 0 && nl < NB && rb + rr < RG) put(pr, n0 + nl, v[0]);
         }
+        ++r;
     }
     return U;
 }
