@@ -388,6 +388,32 @@ def test_sixteen_rows_equal_sixteen_single_row_passes():
     lay.close()
 
 
+@pytest.mark.parametrize("rows", [2, 7])
+def test_identical_rows_share_every_expert(rows):
+    """Degenerate routing: every row is the same token, so each of the k picked experts is
+    picked by every row and its items take all `rows` pairs (passes of two pairs, and one
+    pair alone for an odd count). Every output row equals the one-row pass of that token bit
+    for bit and matches the oracle on it (Bolt-like layer, TensorFold pull request 1038,
+    «What's in it»)."""
+    dims, arrays = workload(1)
+    x1 = np.ascontiguousarray(arrays["x"][:1])
+    xr = np.ascontiguousarray(np.repeat(x1, rows, axis=0))
+    lay, xd, out = run_gpu(dims, arrays, x=xr)
+    multi = out.cpu().numpy()
+    idx, w = lay.routing(rows)
+    o1 = torch.empty_like(xd[:1])
+    lay.forward(xd[:1].contiguous(), o1, 1)
+    torch.cuda.synchronize()
+    lay.status()
+    single = o1.cpu().numpy()[0]
+    ref = O.forward(dims, arrays)   # the workload's one row is this token
+    for r in range(rows):
+        assert np.array_equal(idx[r], ref["idx"][0]) and np.array_equal(w[r].view(np.uint32), ref["w"][0].view(np.uint32))
+        assert np.array_equal(multi[r], single), r
+    assert_out_close(dims, single.view(np.uint16)[None], ref["out_f32"][:1], f"identical rows {rows}")
+    lay.close()
+
+
 @pytest.mark.parametrize("rows", [1, 2, 9, 16, 17, 64, 256])
 def test_tiny_layer_ragged_and_max_rows(rows):
     """Row counts that span several 16-row tiles with a ragged tail, up to max_rows = 256."""
