@@ -6,6 +6,7 @@ the seeded input generator is the only module both consume.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import ctypes
 import os
 import subprocess
@@ -51,13 +52,20 @@ class _Stages(ctypes.Structure):
 
 _lib = None
 
+# MOE_ORACLE_LIB names another build of moe_oracle.c to load instead of the default one
+# (the planted-control tests point it at deliberately altered copies).
+_OVERRIDE_ENV = "MOE_ORACLE_LIB"
+
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        _lib = ctypes.CDLL(_LIB)
+        path = os.environ.get(_OVERRIDE_ENV)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        _lib = ctypes.CDLL(path)
         f = _lib
         f.oracle_bf16_to_f32.restype = ctypes.c_float
         f.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
@@ -136,10 +144,12 @@ class _Bound:
 
 
 def forward(dims, arrays: Dict[str, np.ndarray], x: Optional[np.ndarray] = None,
-            rows: Optional[list] = None, stages: bool = False) -> Dict[str, np.ndarray]:
+            rows: Optional[list] = None, stages: bool = False, threads: int = 1) -> Dict[str, np.ndarray]:
     """Run the layer on the rows of x (default arrays['x']); `rows` picks a subset of row
     indices (rows are independent). Returns out (bits), out_f32, idx, w and, when
-    `stages`, the per-row intermediates z, s, u, a, y, c, m, sh as float32 arrays."""
+    `stages`, the per-row intermediates z, s, u, a, y, c, m, sh as float32 arrays.
+    threads > 1 runs the rows on that many threads (each row is one call into the C
+    oracle, which holds no shared state; ctypes releases the interpreter lock)."""
     L = lib()
     b = _Bound(dims, arrays)
     x = arrays["x"] if x is None else x
@@ -154,7 +164,7 @@ def forward(dims, arrays: Dict[str, np.ndarray], x: Optional[np.ndarray] = None,
     if stages:
         for k, sz in shapes.items():
             res[k] = np.zeros((n, sz), np.float32)
-    for i, r in enumerate(sel):
+    def one(i, r):
         st = None
         if stages:
             st = _Stages(**{k: _ptr(res[k][i]) for k in shapes})
@@ -164,6 +174,14 @@ def forward(dims, arrays: Dict[str, np.ndarray], x: Optional[np.ndarray] = None,
                                   ctypes.byref(st) if st is not None else None)
         if rc:
             raise ValueError(f"oracle_forward_row failed: {rc}")
+
+    if threads > 1 and n > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(threads, n)) as ex:
+            for f in [ex.submit(one, i, r) for i, r in enumerate(sel)]:
+                f.result()
+    else:
+        for i, r in enumerate(sel):
+            one(i, r)
     if stages:
         res["a"] = res["a"].reshape(n, K, I)
         res["y"] = res["y"].reshape(n, K, D)

@@ -459,3 +459,115 @@ def test_magnitudes_are_finite_on_every_workload_row0():
         dims, arrays = next(synth.workload_layers(cid))
         r = O.forward(dims, arrays, rows=[0])
         assert np.isfinite(r["out_f32"]).all()
+
+
+# ------------------------------------------------------------------ O8 / O9 input / O11 / O12 / O13
+
+def _bf16r64(v):
+    """float64 values rounded to the nearest bf16 value (8 significant bits, ties to even),
+    straight from the format's definition, with no intermediate fp32 rounding."""
+    m, e = np.frexp(np.asarray(v, np.float64))     # v = m * 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def _bracket(exact, bound):
+    """The bf16 values that a correctly rounded fp32 sum within `bound` of `exact` can
+    round to lie between these two (rounding is monotone)."""
+    return _bf16r64(exact - bound), _bf16r64(exact + bound)
+
+
+def _in_bracket(got, exact, bound):
+    lo, hi = _bracket(exact, bound)
+    got = np.asarray(got, np.float64)
+    return bool(((got >= lo) & (got <= hi)).all())
+
+
+def _q4_matrix(Q, S, k_in):
+    """float64 dequantised 4-bit matrix [N][K] with bias = -8 * scale: (q - 8) * scale."""
+    k = np.arange(k_in)
+    q = ((Q[:, k // 8] >> (4 * (k % 8)).astype(np.uint32)) & 15).astype(np.float64)
+    return (q - 8) * O.bf16_to_f32(S).astype(np.float64)[:, k // 64]
+
+
+def test_shared_expert_is_textbook_relu2_mlp():
+    """O12: sh = rnd(Sd . rnd(relu(rnd(Su . x))^2)) on the layer input x, with a shared width
+    (256) other than hidden (512), so that Su [256][512] and Sd [512][256] cannot stand in
+    for each other. The data make every fp32 sum exact: x in {-1, 0, 1}, Su with 16 entries
+    of +-1/4 per row (|Su . x| <= 4, a multiple of 1/4, so the pre-activation is a bf16
+    value and its square is too), Sd entries in {-1/4, 0, 1/4} (every partial sum of Sd . a
+    a multiple of 2^-6 below 2^10). The result is then fixed bit for bit by float64 products
+    and one bf16 rounding of sh. The routed experts have all-zero scales and biases, so every
+    routed weight, y, c and m are exactly 0; fc1 is a random projection, so the latent u is
+    not x. The layer output is rnd(x + sh)."""
+    H, SI = 512, 256
+    dims = _dims(hidden=H, latent=H, n_experts=4, n_group=1, topk_group=1, top_k=2,
+                 expert_inter=128, shared_inter=SI)
+    arrays = synth.make_layer(dims, 4, 2024)
+    rng = np.random.default_rng(2024)
+    for k in ("up_scales", "up_biases", "down_scales", "down_biases"):
+        arrays[k] = np.zeros_like(arrays[k])
+    xv = rng.integers(-1, 2, size=(4, H)).astype(np.float32)
+    su = np.zeros((SI, H), np.float32)
+    for i in range(SI):
+        su[i, rng.choice(H, 16, replace=False)] = rng.choice([-0.25, 0.25], 16)
+    sd = (rng.integers(-1, 2, size=(H, SI)) * 0.25).astype(np.float32)
+    arrays["x"] = synth.f32_to_bf16_bits(xv)
+    arrays["shared_up"] = synth.f32_to_bf16_bits(su)
+    arrays["shared_down"] = synth.f32_to_bf16_bits(sd)
+    r = O.forward(dims, arrays, stages=True)
+    for row in range(4):
+        x = xv[row].astype(np.float64)
+        assert not np.array_equal(r["u"][row], xv[row])
+        assert (r["y"][row] == 0).all() and (r["c"][row] == 0).all() and (r["m"][row] == 0).all()
+        g = su.astype(np.float64) @ x                 # exact, and a bf16 value
+        act = np.maximum(g, 0.0) ** 2                 # exact, and a bf16 value
+        assert (g < 0).any() and (act > 0).any() and np.array_equal(_bf16r64(act), act)
+        sh = _bf16r64(sd.astype(np.float64) @ act)
+        assert np.array_equal(r["sh"][row].astype(np.float64), sh), row
+        assert (sh != sd.astype(np.float64) @ act).any()   # the final rounding is exercised
+        # out = rnd(x + rnd(0 + sh)) = rnd(x + sh): sh is already a bf16 value
+        want = (xv[row] + r["sh"][row]).astype(np.float32)
+        assert np.array_equal(r["out_f32"][row], want), row
+
+
+def test_latent_projections_and_expert_input_are_textbook():
+    """O8, O9's input and O11 with a latent narrower than hidden (128 of 512), no shared
+    expert: u = rnd(W1 . x); each pick's activation a = rnd(relu(rnd(U_e . u))^2) is computed
+    from u (not from x); m = rnd(W2 . c) from the oracle's own combine (pinned on its own);
+    out = rnd(x + m). Each product is compared with a float64 product of the same weights
+    within the fp32 summation bound, the roundings taken at the same points."""
+    dims = _dims(shared_inter=0)
+    H, L, I = dims.hidden, dims.latent, dims.expert_inter
+    arrays = synth.make_layer(dims, 4, 2025)
+    r = O.forward(dims, arrays, stages=True)
+    W1 = O.bf16_to_f32(arrays["fc1_w"]).astype(np.float64)
+    W2 = O.bf16_to_f32(arrays["fc2_w"]).astype(np.float64)
+    for row in range(4):
+        x = O.bf16_to_f32(arrays["x"][row]).astype(np.float64)
+        assert _in_bracket(r["u"][row], W1 @ x, _gamma(H) * (np.abs(W1) @ np.abs(x))), row
+        u = r["u"][row].astype(np.float64)
+        for j in range(dims.top_k):
+            e = int(r["idx"][row, j])
+            U = _q4_matrix(arrays["up_q"][e], arrays["up_scales"][e], L)
+            lo, hi = _bracket(U @ u, _gamma(L) * (np.abs(U) @ np.abs(u)))
+            a = r["a"][row, j].astype(np.float64)
+            assert ((a >= _bf16r64(np.maximum(lo, 0) ** 2)) & (a <= _bf16r64(np.maximum(hi, 0) ** 2))).all(), (row, j)
+        c = r["c"][row].astype(np.float64)
+        assert np.abs(c).max() > 0
+        assert _in_bracket(r["m"][row], W2 @ c, _gamma(L) * (np.abs(W2) @ np.abs(c))), row
+        want = (x.astype(np.float32) + r["m"][row]).astype(np.float32)
+        assert np.array_equal(r["out_f32"][row], want), row
+
+
+def test_final_add_order_constructed_cases():
+    """O13: hand-derived cases (golden/final_add_cases.json) where adding the residual before
+    the shared output, or to it first, rounds to another bf16 value."""
+    dims = _dims(shared_inter=0)
+    arrays = synth.make_layer(dims, 1, 2026)
+    H = dims.hidden
+    for case in _golden("final_add_cases.json")["cases"]:
+        x, m, sh = (np.zeros(H, np.float32) for _ in range(3))
+        x[5], m[5], sh[5] = case["x"], case["m"], case["sh"]
+        out, _ = O.stage(dims, arrays, "final", x, in2=m, in3=sh)
+        assert out[5] == np.float32(case["expect"]), case["why"]
+        assert (out[np.arange(H) != 5] == 0).all()
