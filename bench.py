@@ -268,30 +268,41 @@ def main():
     step_bytes = float(np.mean([sum(g.values()) for g in sb]))
     launches = LAUNCHES_ONE_ROW if rows == 1 else LAUNCHES_MULTI_ROW
 
-    # graphs: one sweep over all instances, and one graph per instance for a remainder
     def capture(fn):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             fn()
         return g
 
-    with torch.cuda.stream(s):
-        sweep = capture(lambda: [lay.forward(x, o, rows) for lay, x, o in zip(layers, xs, outs)])
-        singles = [capture(lambda lay=lay, x=x, o=o: lay.forward(x, o, rows)) for lay, x, o in zip(layers, xs, outs)]
+    # Steps are replayed from graphs of consecutive forwards that rotate through the
+    # instances: chunks of CH forwards, and one graph for a remainder, so that every block of
+    # timed steps is whole graph replays and a step's time does not depend on --steps.
+    CH = inst * max(1, 64 // inst)
+    graphs = {}
+
+    def graph_of(n):
+        if n not in graphs:
+            with torch.cuda.stream(s):
+                graphs[n] = capture(lambda: [layers[i % inst].forward(xs[i % inst], outs[i % inst], rows)
+                                             for i in range(n)])
+        return graphs[n]
 
     def run_steps(n):
-        for _ in range(n // inst):
-            sweep.replay()
-        for j in range(n % inst):
-            singles[j].replay()
+        for _ in range(n // CH):
+            graph_of(CH).replay()
+        if n % CH:
+            graph_of(n % CH).replay()
 
+    # the timed steps in NBLOCK blocks, each bracketed by events: the whole span gives the
+    # value, the blocks its spread (one block unless every block holds whole chunks)
+    nblock = 5 if args.steps >= 5 * CH else 1
+    bsteps = [args.steps // nblock + (1 if b < args.steps % nblock else 0) for b in range(nblock)]
     with torch.cuda.stream(s):
         run_steps(args.warmup)
+        for n in sorted({CH, *(b % CH for b in bsteps)} - {0}):   # every graph the blocks replay, twice
+            for _ in range(2):
+                graph_of(n).replay()
     s.synchronize()
-    # the timed steps in NBLOCK blocks, each bracketed by events: the whole span gives the
-    # value, the blocks its spread
-    nblock = 5 if args.steps >= 5 else 1
-    bsteps = [args.steps // nblock + (1 if b < args.steps % nblock else 0) for b in range(nblock)]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(nblock + 1)]
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
@@ -401,11 +412,21 @@ def main():
         el = time.time() - t_start
         got = O.act_to_f32(dims, out0).astype(np.float64)
         refv = ref["out_f32"].astype(np.float64)
-        rel_rms = float(np.sqrt(((got - refv) ** 2).mean() / (refv ** 2).mean()))
-        rel_max = float(np.abs(got - refv).max() / np.abs(refv).max())
+        rms = float(np.sqrt((refv ** 2).mean()))
+        dd = np.abs(got - refv)
+        rel_rms = float(np.sqrt((dd ** 2).mean())) / rms
+        rel_max = float((dd / np.maximum(rms, np.abs(refv))).max())
+        big = np.abs(refv) >= rms
+        if dims.act_dtype == 1:
+            ulp = np.spacing(np.abs(refv[big]).astype(np.float32)).astype(np.float64) * 65536.0
+        else:
+            ulp = np.spacing(np.abs(refv[big]).astype(np.float16)).astype(np.float64)
         parity = {"routing_bitwise": bool(np.array_equal(idx0, ref["idx"]) and
                                           np.array_equal(w0.view(np.uint32), ref["w"].view(np.uint32))),
-                  "rel_rms": rel_rms, "rel_max": rel_max}
+                  "rel_rms": rel_rms, "max_rel": rel_max, "max_abs_over_rms": float(dd.max()) / rms,
+                  "max_abs": float(dd.max()), "max_ulp_where_abs_ge_rms": float((dd[big] / ulp).max()),
+                  "bar": "rel_rms <= 5e-3 and max |err| / max(RMS(oracle), |oracle|) <= 2e-2",
+                  "ok": bool(rel_rms <= 5e-3 and rel_max <= 2e-2)}
         cpu_single = {"value": round(rows * n / el, 3), "unit": "layer-tokens/s", "cores": 1, "kind": "oracle",
                       "sample": f"{n} forwards of instance 0 ({rows} row(s) each), single-threaded plain C, "
                                 f"{el:.1f} s"}

@@ -137,7 +137,12 @@ int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
  * not reentrant: forwards on one handle must not overlap in time on different streams. */
 int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out);
 
-/* Release the workspace and the handle (NULL-safe). Synchronises the handle's stream. */
+/* Release the workspace and the handle (NULL-safe; a handle already destroyed or never
+ * created is ignored). Synchronises the handle's stream first, so no enqueued forward still
+ * uses what it frees. Every device resource create took is released here, as the loader on
+ * TensorFold pull request 1038 releases what it built (review thread: device resources of a
+ * failed or finished load are freed, checked by counting live allocations; see
+ * moe_latent_live_allocations). */
 void moe_latent_destroy(moe_latent_t *h);
 
 /* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (its first
@@ -183,7 +188,12 @@ int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
 int moe_latent_set_variant(moe_latent_t *h, int32_t variant);
 
 /* Copy the last forward's routing to device buffers, enqueued on the handle's stream:
- * idx_dev [rows][top_k] int32 expert ids in pick order, w_dev [rows][top_k] fp32 weights. */
+ * idx_dev [rows][top_k] int32 expert ids in pick order, w_dev [rows][top_k] fp32 weights
+ * (either may be NULL to skip it); rows is the last forward's row count. The routing is
+ * what TensorFold pull request 1038 checks bit for bit per row («Per operator and row
+ * invariance»: group_expert_select at k = 9; per-row equality of a multi-row pass with its
+ * one-row passes), so the tests read it back here. MOE_ERR_INVALID_ARG before any forward;
+ * MOE_ERR_HIP if a copy cannot be enqueued. */
 int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev);
 
 /* Intermediate values of the last forward, for stage-by-stage checks. */
@@ -205,7 +215,12 @@ int moe_latent_read_stage(moe_latent_t *h, int32_t stage, void *dst_dev, size_t 
  * (MOE_ERR_DEVICE_CHECK) or MOE_ERR_HIP; clears the device error flag. */
 int moe_latent_status(moe_latent_t *h);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none; a successful create clears
+ * it). The message names the refused parameter or tensor and the reason, as the refusals of
+ * TensorFold pull request 1038 do («What's in it»: a layer whose top-k exceeds its expert
+ * count, a missing, quantized or transposed latent projection, experts stored over hidden,
+ * an unsupported chip -- each refused by name before any weight is read). The pointer stays
+ * valid until this thread's next call into the library; the library owns it. */
 const char *moe_latent_last_error(void);
 
 /* Number of device allocations the library currently holds (all handles). */

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "moe_latent.h"
@@ -56,11 +57,20 @@ static int fail(int code, const char *fmt, ...) {
 }
 
 // Device allocation with leak accounting. MOE_LATENT_FAIL_ALLOC_AT=n makes the n-th
-// allocation (counted from 1 over the process) fail, to test the release paths.
-static hipError_t dev_alloc(void **p, size_t bytes) {
-    const int n = ++g_alloc_calls;
+// allocation after the variable was set (or last changed) fail, to test the release paths.
+static std::mutex g_fail_mu;
+static std::string g_fail_seen;
+static bool inject_failure() {
     const char *f = getenv("MOE_LATENT_FAIL_ALLOC_AT");
-    if (f && atoi(f) == n) { *p = nullptr; return hipErrorOutOfMemory; }
+    std::lock_guard<std::mutex> lk(g_fail_mu);
+    const std::string v = f ? f : "";
+    if (v != g_fail_seen) { g_fail_seen = v; g_alloc_calls = 0; }
+    const int n = ++g_alloc_calls;
+    return !v.empty() && atoi(v.c_str()) == n;
+}
+
+static hipError_t dev_alloc(void **p, size_t bytes) {
+    if (inject_failure()) { *p = nullptr; return hipErrorOutOfMemory; }
     hipError_t e = hipMalloc(p, bytes);
     if (e == hipSuccess) ++g_live_allocs;
     return e;
@@ -256,9 +266,9 @@ static int setup_workspace(moe_latent *h) {
     LayerParams &p = h->base;
     p.ks_fc1 = dense_splits_host((int)H);
     p.ks_shup = dense_splits_host((int)H);
-    // the shared down projection fills the expert launches: the most K splits a pass uses
-    // (its partial sums are sized for them; plan_items picks the splits of each pass)
-    p.ks_shdn = SI >= 4096 && SI % 2048 == 0 ? (int)(SI / 2048) : 1;
+    // the shared down projection: whole tiles of up to 4096 inputs (128 KB), parts of 4096
+    // beyond; the same for every row count, so that its sums keep one order
+    p.ks_shdn = SI > 4096 && SI % 4096 == 0 ? (int)(SI / 4096) : 1;
     p.ks_fc2 = dense_splits_host(L ? (int)L : 1);
     // dense tile counters after the fixed ones
     p.ctr_fc1 = CTR_DENSE;
@@ -492,10 +502,6 @@ static void plan_items(LayerParams &p, int rows) {
     p.dn_nb = expert_block(p.D, p.I);
     p.up_blocks = p.I / p.up_nb;
     p.dn_blocks = p.D / p.dn_nb;
-    // the shared down projection: whole tiles of up to 4096 inputs (128 KB) while a pass has
-    // at most 16 rows (measured faster at 1 row, the same at 16), parts of 2048 inputs for
-    // more rows (measured 3.6 % faster per layer at 64 rows)
-    if (rows <= 16) p.ks_shdn = p.SI > 4096 && p.SI % 4096 == 0 ? p.SI / 4096 : 1;
     // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's
     // tiles are cut in two halves for two launches
     const int shdn = p.SI ? p.H / DENSE_TILE : 0, ks_sd = p.ks_shdn;
