@@ -238,6 +238,28 @@ int32_t moe_latent_live_allocations(void);
  * size. */
 int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *sink_dev, void *hip_stream);
 
+/* Size of the static workspace of moe_latent_forward_static, per GPU (16 MiB: a Bolt-like
+ * layer of hidden 4096, latent 1024, 9 picks of 2048-wide experts and a 4096-wide shared
+ * expert fits up to about 100 rows). */
+#define MOE_LATENT_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): one forward like moe_latent_forward, without a
+ * handle and without any allocation. cfg and w are validated as moe_latent_create validates
+ * them (same refusals and codes; nothing is kept after the call), hidden_in / out / rows as
+ * moe_latent_forward checks them (rows <= cfg->max_rows). The workspace for `rows` rows lives
+ * in a library-owned array of MOE_LATENT_STATIC_SCRATCH_BYTES per GPU, held until the process
+ * ends; a forward whose workspace does not fit is refused with MOE_ERR_SHAPE. Enqueued on
+ * hip_stream (NULL: the null stream) as the single-stream launch chain of moe_latent_forward,
+ * preceded by two fill kernels that zero the array's counters and error flag (no memset, no
+ * host synchronisation): it can be captured in a HIP graph. Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents, so calls that overlap in time on one GPU
+ * (on different streams, or replays of graphs on different streams) race and give wrong
+ * results; calls in stream order do not. The output equals moe_latent_forward's bit for bit.
+ * Device-side check flags are cleared by the next call and are not reported. */
+int moe_latent_forward_static(const moe_latent_config *cfg, const moe_latent_weights *w, int32_t rows,
+                              const void *hidden_in, void *out, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

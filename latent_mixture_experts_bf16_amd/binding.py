@@ -83,6 +83,9 @@ def _load():
         "moe_latent_group_items": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32]),
         "moe_latent_forward_timed": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.POINTER(P), ctypes.c_int32]),
         "moe_latent_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
+        "moe_latent_forward_static": (ctypes.c_int, [ctypes.POINTER(moe_latent_config),
+                                                     ctypes.POINTER(moe_latent_weights), ctypes.c_int32,
+                                                     P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -96,7 +99,7 @@ EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "mo
             "moe_latent_set_variant", "moe_latent_get_routing", "moe_latent_read_stage",
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
             "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
-            "moe_latent_stream_read")
+            "moe_latent_stream_read", "moe_latent_forward_static")
 
 
 def lib():
@@ -195,3 +198,15 @@ def moe_latent_forward_timed(h: int, rows: int, hidden_in: int, out: int, events
 
 def moe_latent_stream_read(src: int, nbytes: int, sink_dev: int, stream: int = 0) -> None:
     _check(_lib.moe_latent_stream_read(src, nbytes, sink_dev, stream))
+
+
+def moe_latent_forward_static(cfg: moe_latent_config, weights: moe_latent_weights, rows: int, hidden_in: int,
+                              out: int, stream: int = 0) -> None:
+    _check(_lib.moe_latent_forward_static(ctypes.byref(cfg), ctypes.byref(weights), rows, hidden_in, out,
+                                          stream or None))
+
+
+def moe_latent_forward_static_rc(cfg: moe_latent_config, weights: moe_latent_weights, rows: int, hidden_in: int,
+                                 out: int, stream: int = 0) -> int:
+    return _lib.moe_latent_forward_static(ctypes.byref(cfg), ctypes.byref(weights), rows, hidden_in, out,
+                                          stream or None)

@@ -259,11 +259,12 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // at once), so that a launch's items fit the machine in one round and spread evenly.
 static int dense_splits_host(int K) { return K >= 4096 && K % 2048 == 0 ? K / 2048 : 1; }
 
-static int setup_workspace(moe_latent *h) {
-    const moe_latent_config &c = h->cfg;
-    const size_t R = c.max_rows, E = c.n_experts, K = c.top_k, I = c.expert_inter, H = c.hidden;
+// Lays out the workspace of `R` rows over `base` (nullptr: sizes only) and fills the
+// workspace fields of p (split counts, counter offsets, region pointers). Returns its size in
+// bytes; *n_ctr gets the number of completion counters.
+static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_t R, char *base, int *n_ctr) {
+    const size_t E = c.n_experts, K = c.top_k, I = c.expert_inter, H = c.hidden;
     const size_t D = c.latent ? c.latent : c.hidden, SI = c.shared_inter, L = c.latent;
-    LayerParams &p = h->base;
     p.ks_fc1 = dense_splits_host((int)H);
     p.ks_shup = dense_splits_host((int)H);
     // the shared down projection: whole tiles of up to 4096 inputs (128 KB), parts of 4096
@@ -277,7 +278,7 @@ static int setup_workspace(moe_latent *h) {
     p.ctr_fc2 = p.ctr_shdn + (SI ? (int)(H / DENSE_TILE) : 0);
     // the one-row logit handoff words (8-byte aligned, zero between forwards)
     p.ctr_hand = (p.ctr_fc2 + (L ? (int)(H / DENSE_TILE) : 0) + 1) & ~1;
-    h->n_ctr = p.ctr_hand + 2 * (int)E;
+    *n_ctr = p.ctr_hand + 2 * (int)E;
     p.wait_ticks = 10000000u;   // 100 ms: far beyond any forward
     // split-K partials: [tile][split][row][16] floats = N * splits * rows floats
     const size_t part_fc1 = L * p.ks_fc1 * R * 4;
@@ -285,33 +286,38 @@ static int setup_workspace(moe_latent *h) {
     const size_t part_shdn = SI ? H * p.ks_shdn * R * 4 : 0;
     const size_t part_fc2 = L ? H * p.ks_fc2 * R * 4 : 0;
     enum { NREG = 16 };
-    struct Region { size_t bytes; size_t off; } reg[NREG];
     const size_t sizes[NREG] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
                                 R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
-                                R * H * 2, 256, (size_t)h->n_ctr * 4, part_fc1, part_shup, part_shdn,
+                                R * H * 2, 256, (size_t)*n_ctr * 4, part_fc1, part_shup, part_shdn,
                                 part_fc2};
-    size_t off = 0;
-    for (int i = 0; i < NREG; ++i) { reg[i].bytes = sizes[i]; reg[i].off = off; off += align256(sizes[i]); }
-    h->ws_bytes = off;
-    hipError_t e = dev_alloc(&h->ws, off);
-    if (e != hipSuccess) return fail(MOE_ERR_OOM, "workspace of %zu bytes: %s", off, hipGetErrorString(e));
-    char *b = (char *)h->ws;
-    p.logits = b + reg[0].off;
-    p.idx = (int32_t *)(b + reg[1].off);
-    p.wts = (float *)(b + reg[2].off);
-    p.sched = (int32_t *)(b + reg[3].off);
-    p.u = (uint16_t *)(b + reg[4].off);
-    p.shact = (uint16_t *)(b + reg[5].off);
-    p.eact = (uint16_t *)(b + reg[6].off);
-    p.eout = (uint16_t *)(b + reg[7].off);
-    p.comb = (uint16_t *)(b + reg[8].off);
-    p.shout = (uint16_t *)(b + reg[9].off);
-    p.err = (uint32_t *)(b + reg[10].off);
-    p.ctr = (uint32_t *)(b + reg[11].off);
-    p.part_fc1 = (float *)(b + reg[12].off);
-    p.part_shup = (float *)(b + reg[13].off);
-    p.part_shdn = (float *)(b + reg[14].off);
-    p.part_fc2 = (float *)(b + reg[15].off);
+    size_t off[NREG], total = 0;
+    for (int i = 0; i < NREG; ++i) { off[i] = total; total += align256(sizes[i]); }
+    if (base) {
+        p.logits = base + off[0];
+        p.idx = (int32_t *)(base + off[1]);
+        p.wts = (float *)(base + off[2]);
+        p.sched = (int32_t *)(base + off[3]);
+        p.u = (uint16_t *)(base + off[4]);
+        p.shact = (uint16_t *)(base + off[5]);
+        p.eact = (uint16_t *)(base + off[6]);
+        p.eout = (uint16_t *)(base + off[7]);
+        p.comb = (uint16_t *)(base + off[8]);
+        p.shout = (uint16_t *)(base + off[9]);
+        p.err = (uint32_t *)(base + off[10]);
+        p.ctr = (uint32_t *)(base + off[11]);
+        p.part_fc1 = (float *)(base + off[12]);
+        p.part_shup = (float *)(base + off[13]);
+        p.part_shdn = (float *)(base + off[14]);
+        p.part_fc2 = (float *)(base + off[15]);
+    }
+    return total;
+}
+
+static int setup_workspace(moe_latent *h) {
+    h->ws_bytes = layout_workspace(h->cfg, h->base, (size_t)h->cfg.max_rows, nullptr, &h->n_ctr);
+    hipError_t e = dev_alloc(&h->ws, h->ws_bytes);
+    if (e != hipSuccess) return fail(MOE_ERR_OOM, "workspace of %zu bytes: %s", h->ws_bytes, hipGetErrorString(e));
+    layout_workspace(h->cfg, h->base, (size_t)h->cfg.max_rows, (char *)h->ws, &h->n_ctr);
     return MOE_OK;
 }
 
@@ -337,6 +343,37 @@ extern "C" void moe_latent_destroy(moe_latent_t *h) {
     delete h;
 }
 
+// Sizes, switches and weight pointers of a validated configuration.
+static void fill_params(const moe_latent_config &c, const moe_latent_weights &w, LayerParams &p) {
+    p.H = c.hidden;
+    p.L = c.latent;
+    p.D = c.latent ? c.latent : c.hidden;
+    p.E = c.n_experts;
+    p.G = c.n_group;
+    p.TG = c.topk_group;
+    p.K = c.top_k;
+    p.I = c.expert_inter;
+    p.SI = c.shared_inter;
+    p.act_f16 = c.act_dtype == MOE_DT_F16;
+    p.router_f32 = c.router_dtype == MOE_DT_F32;
+    p.has_bias = c.has_bias != 0;
+    p.norm_topk = c.norm_topk != 0;
+    p.rho = c.routed_scaling;
+    p.gate_w16 = p.router_f32 ? nullptr : (const uint16_t *)w.gate_w.data;
+    p.gate_w32 = p.router_f32 ? (const float *)w.gate_w.data : nullptr;
+    p.bias = c.has_bias ? (const float *)w.corr_bias.data : nullptr;
+    p.fc1 = (const uint16_t *)w.fc1_w.data;
+    p.fc2 = (const uint16_t *)w.fc2_w.data;
+    p.up_q = (const uint32_t *)w.up_q.data;
+    p.up_s = (const uint16_t *)w.up_scales.data;
+    p.up_b = (const uint16_t *)w.up_biases.data;
+    p.dn_q = (const uint32_t *)w.down_q.data;
+    p.dn_s = (const uint16_t *)w.down_scales.data;
+    p.dn_b = (const uint16_t *)w.down_biases.data;
+    p.su = (const uint16_t *)w.shared_up.data;
+    p.sd = (const uint16_t *)w.shared_down.data;
+}
+
 extern "C" int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w, void *hip_stream,
                                  moe_latent_t **out) {
     g_err.clear();
@@ -356,35 +393,7 @@ extern "C" int moe_latent_create(const moe_latent_config *cfg, const moe_latent_
     h->device = dev;
     h->magic = kMagic;
     h->last_rows = 0;
-
-    LayerParams &p = h->base;
-    p.H = cfg->hidden;
-    p.L = cfg->latent;
-    p.D = cfg->latent ? cfg->latent : cfg->hidden;
-    p.E = cfg->n_experts;
-    p.G = cfg->n_group;
-    p.TG = cfg->topk_group;
-    p.K = cfg->top_k;
-    p.I = cfg->expert_inter;
-    p.SI = cfg->shared_inter;
-    p.act_f16 = cfg->act_dtype == MOE_DT_F16;
-    p.router_f32 = cfg->router_dtype == MOE_DT_F32;
-    p.has_bias = cfg->has_bias != 0;
-    p.norm_topk = cfg->norm_topk != 0;
-    p.rho = cfg->routed_scaling;
-    p.gate_w16 = p.router_f32 ? nullptr : (const uint16_t *)w->gate_w.data;
-    p.gate_w32 = p.router_f32 ? (const float *)w->gate_w.data : nullptr;
-    p.bias = cfg->has_bias ? (const float *)w->corr_bias.data : nullptr;
-    p.fc1 = (const uint16_t *)w->fc1_w.data;
-    p.fc2 = (const uint16_t *)w->fc2_w.data;
-    p.up_q = (const uint32_t *)w->up_q.data;
-    p.up_s = (const uint16_t *)w->up_scales.data;
-    p.up_b = (const uint16_t *)w->up_biases.data;
-    p.dn_q = (const uint32_t *)w->down_q.data;
-    p.dn_s = (const uint16_t *)w->down_scales.data;
-    p.dn_b = (const uint16_t *)w->down_biases.data;
-    p.su = (const uint16_t *)w->shared_up.data;
-    p.sd = (const uint16_t *)w->shared_down.data;
+    fill_params(*cfg, *w, h->base);
 
     if ((rc = setup_workspace(h))) {
         delete h;
@@ -668,5 +677,87 @@ extern "C" int moe_latent_status(moe_latent_t *h) {
         return fail(MOE_ERR_DEVICE_CHECK, "device-side error flag %u (2: a route found no candidate, "
                     "4: an invalid schedule)", flag);
     }
+    return MOE_OK;
+}
+
+// ------------------------------------------------------------------ forward without allocation
+
+// The workspace of moe_latent_forward_static: one array per GPU, held until the process ends.
+// Host code never uses its name as an address (that is a host-side stand-in): the device
+// address of each GPU's copy is taken once, with that GPU current, and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[MOE_LATENT_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of scratch on each GPU (nullptr: not taken yet)
+int g_scratch_cus[kMaxDevices];
+}  // namespace
+
+// The current device's scratch address and compute-unit count (taken on its first use).
+static int scratch_of_current_device(void **ptr, int *cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_DEVICE, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        int n = 0;
+        if ((e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess || n < 1)
+            return fail(MOE_ERR_HIP, "compute unit count: %s", hipGetErrorString(e));
+        g_scratch[dev] = p;
+        g_scratch_cus[dev] = n;
+    }
+    *ptr = g_scratch[dev];
+    *cus = g_scratch_cus[dev];
+    return MOE_OK;
+}
+
+extern "C" int moe_latent_forward_static(const moe_latent_config *cfg, const moe_latent_weights *w, int32_t rows,
+                                         const void *hidden_in, void *out, void *hip_stream) {
+    g_err.clear();
+    if (!cfg || !w) return fail(MOE_ERR_INVALID_ARG, "cfg or weights is NULL");
+    int rc;
+    if ((rc = check_config(*cfg))) return rc;
+    if ((rc = check_weights(*cfg, *w))) return rc;
+    int dev = 0, cus = 0;
+    if ((rc = check_device(&dev, &cus))) return rc;
+    if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
+    if (((uintptr_t)hidden_in | (uintptr_t)out) & 15)
+        return fail(MOE_ERR_LAYOUT, "hidden_in and out must be 16-byte aligned");
+    if (rows < 1 || rows > cfg->max_rows)
+        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, cfg->max_rows);
+    const size_t bytes = (size_t)rows * cfg->hidden * 2;
+    const char *a = (const char *)hidden_in, *b = (const char *)out;
+    if (a != b && a < b + bytes && b < a + bytes) return fail(MOE_ERR_ALIAS, "out partially overlaps hidden_in");
+
+    LayerParams p;
+    memset(&p, 0, sizeof p);
+    fill_params(*cfg, *w, p);
+    int n_ctr = 0;
+    const size_t need = layout_workspace(*cfg, p, (size_t)rows, nullptr, &n_ctr);
+    if (need > MOE_LATENT_STATIC_SCRATCH_BYTES)
+        return fail(MOE_ERR_SHAPE, "the workspace of %d rows of this layer needs %zu bytes; the static scratch "
+                    "holds %zu (use moe_latent_create / moe_latent_forward, or fewer rows)",
+                    rows, need, (size_t)MOE_LATENT_STATIC_SCRATCH_BYTES);
+    void *base = nullptr;
+    if ((rc = scratch_of_current_device(&base, &cus))) return rc;
+    layout_workspace(*cfg, p, (size_t)rows, (char *)base, &n_ctr);
+    p.x = (const uint16_t *)hidden_in;
+    p.out = (uint16_t *)out;
+    plan_items(p, rows);
+    hipStream_t st = (hipStream_t)hip_stream;
+    // the counters and the error flag start at zero (the previous call, maybe of another
+    // layer, left its own contents): fill kernels, no memset
+    hipLaunchKernelGGL(moe_clear_kernel, dim3(1), dim3(64), 0, st, p.err, 64);
+    hipLaunchKernelGGL(moe_clear_kernel, dim3((n_ctr + 255) / 256), dim3(256), 0, st, p.ctr, n_ctr);
+    Launch ls[8];
+    const int n = plan_launches(p, cus, ls);
+    for (int i = 0; i < n; ++i) launch_one(p, ls[i], st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }
