@@ -28,24 +28,46 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-# launches of one forward (the library's launch groups) and the stages each one runs
-LAUNCHES_ONE_ROW = [("gate+fc1+shared_up+route", ["gate", "fc1", "shup", "route"]),
-                    ("shared_down_a+expert_up", ["shdn_a", "up"]),
-                    ("shared_down_b+expert_down+combine", ["shdn_b", "down"]),
-                    ("fc2+shared+residual", ["fc2"])]
-# kernel of each one-row launch, as rocprofv3 names it (template arguments: first and last
-# stage of the kernel, wide expert variant)
-KERNELS_ONE_ROW = ["moe_stage_kernel<0, 2, false>", "moe_stage_kernel<3, 5, false>",
-                   "moe_stage_kernel<5, 7, false>", "moe_stage_kernel<8, 8, false>"]
+# stages of the work-item table, in the library's order (include/moe_latent.h,
+# moe_latent_group_stages), and the keys of stage_bytes
+STAGE_KEYS = ["gate", "fc1", "shup", "route", "shdn_a", "up", "shdn_b", "down", "fc2"]
 KERNEL_SOURCES = ["latent_mixture_experts_bf16_amd/csrc/layer_kernels.hip",
                   "latent_mixture_experts_bf16_amd/csrc/layer_plan.h",
                   "latent_mixture_experts_bf16_amd/csrc/moe_latent_api.hip"]
 COPY_MIB = 512   # size of the calibration copy (int32 negation: reads and writes COPY_MIB MiB)
-LAUNCHES_MULTI_ROW = [("gate+fc1+shared_up", ["gate", "fc1", "shup"]),
-                      ("route+schedule+shared_down_a", ["route", "shdn_a"]),
-                      ("expert_up+shared_down_b", ["up", "shdn_b"]),
-                      ("expert_down+combine", ["down"]),
-                      ("fc2+shared+residual", ["fc2"])]
+
+
+def kernel_of(first, last, wide):
+    """The kernel instance (as rocprofv3 names it: first and last stage of its template, wide
+    expert variant) that runs a launch of stages [first, last] (moe_latent_api.hip,
+    launch_one)."""
+    w = "true" if wide else "false"
+    if last <= 2 and first == 0:
+        return "moe_stage_kernel<0, 2, false>"
+    if first == last and first in (2, 4, 6, 8):
+        return f"moe_stage_kernel<{first}, {last}, false>"
+    if 3 <= first and last <= 5:
+        return f"moe_stage_kernel<3, 5, {w}>"
+    return f"moe_stage_kernel<5, 7, {w}>"
+
+
+def plan_groups(B, handle, dims, rows):
+    """The launch groups of a pass, from the library's plan: index, name, stages (stage_bytes
+    keys), side stream, workgroups, kernel name."""
+    D = dims.latent or dims.hidden
+    wide = D > 2048 or dims.expert_inter > 2048
+    out = []
+    for g in range(16):
+        n, f, l, side = B.moe_latent_group_stages(handle, rows, g)
+        if n <= 0:
+            break
+        stages = STAGE_KEYS[f:l + 1]
+        if rows == 1 and f == 0:
+            stages = stages + ["route"]           # the one-row route item rides in the gate launch
+        name = "+".join(stages) + (" [side stream]" if side else "")
+        out.append({"group": g, "name": name, "stages": stages, "side": side, "items": n,
+                    "kernel": kernel_of(f, l, wide)})
+    return out
 
 
 def parse():
@@ -103,9 +125,8 @@ def _csv_rows(folder, name):
 
 
 def _short(kernel_name):
-    for k in KERNELS_ONE_ROW:
-        if k.replace(" ", "") in kernel_name.replace(" ", ""):
-            return k
+    if "moe_stage_kernel<" in kernel_name:
+        return "moe_stage_kernel<" + kernel_name.split("moe_stage_kernel<")[1].split(">")[0] + ">"
     return "copy" if "elementwise" in kernel_name else None
 
 
@@ -266,7 +287,7 @@ def main():
         distinct.append(len(np.unique(idx)))
     sb = [stage_bytes(dims, rows, u) for u in distinct]
     step_bytes = float(np.mean([sum(g.values()) for g in sb]))
-    launches = LAUNCHES_ONE_ROW if rows == 1 else LAUNCHES_MULTI_ROW
+    groups = plan_groups(B, layers[0].handle, dims, rows)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -322,9 +343,8 @@ def main():
     # each launch group on its own: replay graphs of that group over all instances
     group_stats = {}
     reps = max(20, args.steps // (4 * inst))
-    for gid, (gname, stages) in enumerate(launches):
-        if B.moe_latent_group_items(layers[0].handle, rows, gid) <= 0:
-            continue
+    for grp in groups:
+        gid, gname, stages = grp["group"], grp["name"], grp["stages"]
         with torch.cuda.stream(s):
             gg = capture(lambda gid=gid: [B.moe_latent_launch_group(lay.handle, rows, x.data_ptr(), o.data_ptr(), gid)
                                           for lay, x, o in zip(layers, xs, outs)])
@@ -339,13 +359,14 @@ def main():
         us = a.elapsed_time(b) * 1e3 / (reps * inst)
         gbytes = float(np.mean([sum(g[st] for st in stages) for g in sb]))
         group_stats[gid] = {"name": gname, "us": round(us, 3), "bytes": int(gbytes),
-                            "gbps": round(gbytes / (us * 1e-6) / 1e9, 1)}
+                            "gbps": round(gbytes / (us * 1e-6) / 1e9, 1), "kernel": grp["kernel"],
+                            "side_stream": bool(grp["side"]), "workgroups": grp["items"]}
         del gg
     for lay in layers:
         lay.status()
     # each launch inside full forwards, as the roofline's duration: its kernel's start and end
     # recorded by the kernel's own dispatch (no marker packets between the launches)
-    inside = in_forward_launches(B, layers, xs, outs, rows, s, len(launches))
+    inside = in_forward_launches(B, layers, xs, outs, rows, s, len(groups))
     for gid, v in group_stats.items():
         v["us_alone"] = v["us"]
         v["us"] = round(float(inside[gid]), 3)
@@ -362,7 +383,7 @@ def main():
         if pmc.get("kernel_source_sha256") != source_hash():
             traffic_note = "counter summary predates the current kernel source"
         else:
-            kname = KERNELS_ONE_ROW[dom]
+            kname = d["kernel"]
             try:
                 traffic = int(pmc["counters"]["FETCH_SIZE"]["kernels"][kname]["bytes_scaled"] +
                               pmc["counters"]["WRITE_SIZE"]["kernels"][kname]["bytes_scaled"])
@@ -450,12 +471,13 @@ def main():
                    "shared_inter": dims.shared_inter, "weight_instances": inst},
         "layer_hbm": {"bytes_per_step": int(step_bytes), "achieved_gbps": round(layer_gbps, 1),
                       "frac": round(layer_gbps / HBM_PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": f"launch {dom}: moe_stage_kernel ({d['name']})",
+        "roofline": {"bound": "hbm", "kernel": f"launch {dom}: {d['kernel']} ({d['name']})",
                      "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(d["gbps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_note": traffic_note,
                      "bytes_per_launch": d["bytes"], "us_per_launch": d["us"]},
-        "launches": {v["name"]: {"us": v["us"], "us_alone": v["us_alone"], "bytes": v["bytes"], "gbps": v["gbps"]}
+        "launches": {v["name"]: {"us": v["us"], "us_alone": v["us_alone"], "bytes": v["bytes"], "gbps": v["gbps"],
+                                 "kernel": v["kernel"], "workgroups": v["workgroups"]}
                      for v in group_stats.values()},
         "cpu_baseline": cpu,
         "cpu_baseline_single_thread": cpu_single,

@@ -130,9 +130,12 @@ int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
  * layer order; «Per operator and row invariance»: each row of a multi-row pass equals its
  * own one-row pass). hidden_in: [rows][H] activations (act_dtype); out: [rows][H] (same
  * dtype); both 16-byte aligned (MOE_ERR_LAYOUT otherwise). out == hidden_in (in place) is
- * allowed; any other overlap is refused. Enqueued on
- * the handle's stream as four or five launches (no host synchronisation, no allocation, no
- * memset: it can be captured in a HIP graph); returns launch errors only -- device-side
+ * allowed; any other overlap is refused. Enqueued as
+ * a short chain of launches (no host synchronisation, no allocation, no memset: it can be
+ * captured in a HIP graph) that starts and ends on the handle's stream: in a pass of more than
+ * one row (by default) the shared expert runs on the handle's own side stream, forked off the
+ * handle's stream by an event at the start and joined back by an event before the fc2 launch,
+ * so a graph captured on the handle's stream holds both branches; returns launch errors only -- device-side
  * faults surface at the caller's next synchronisation / moe_latent_status(). The handle is
  * not reentrant: forwards on one handle must not overlap in time on different streams. */
 int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out);
@@ -145,17 +148,22 @@ int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, voi
  * moe_latent_live_allocations). */
 void moe_latent_destroy(moe_latent_t *h);
 
-/* Launch groups of a forward, in order. One-row pass: 0 gate + fc1 + shared up (its first
- * workgroup routes the row once the gate workgroups have handed it their logits; that wait
- * is bounded, and a timeout sets bit 8 of the device error flag, reported by
- * moe_latent_status); 1 routed expert up + shared down (first half); 2 routed
- * expert down + shared down (second half); 3 combine + fc2 + shared + residual (each fc2
- * workgroup combines the slice of the expert outputs it reads; a non-latent layer combines
- * in group 2 instead). Multi-row pass: 0 as above without the route; 1 route (the
- * last route workgroup builds the expert schedule) + shared down (first half); 2 routed
- * expert up + shared down (second half); 3 routed expert down + combine; 4 fc2 + shared +
- * residual. A non-latent layer has no fc1 / fc2 / shared launches: its combine adds the
- * residual. */
+/* Launch groups of a forward, in enqueue order.
+ * Variant 2 (two streams; the default for passes of more than one row): 0 gate + fc1 (one-row pass: its first workgroup
+ * routes the row once the gate workgroups have handed it their logits; that wait is bounded,
+ * and a timeout sets bit 8 of the device error flag, reported by moe_latent_status); with a
+ * shared expert, on the side stream: 1 shared up, 2 and 3 the two halves of shared down;
+ * then on the handle's stream: route (multi-row passes only: one workgroup per row, the last
+ * builds the expert schedule); routed expert up; routed expert down (multi-row: the last
+ * workgroup of each output block combines it; a non-latent layer also adds the residual
+ * there); combine + fc2 + shared + residual (latent layers; it waits for the side stream;
+ * one-row pass: each fc2 workgroup combines the slice of the expert outputs it reads).
+ * Variant 1 (one stream; the default for a one-row pass): one-row pass: 0 gate + fc1 + shared up (+ the route as above);
+ * 1 routed expert up + shared down (first half); 2 routed expert down + shared down (second
+ * half); 3 combine + fc2 + shared + residual. Multi-row pass: 0 as above without the route;
+ * 1 route + shared down (first half); 2 routed expert up + shared down (second half); 3 routed
+ * expert down + combine; 4 fc2 + shared + residual. A non-latent layer has no fc1 / fc2 /
+ * shared launches: its combine adds the residual. */
 
 /* Enqueue only launch group `group` of a forward of `rows` rows, for timing one
  * kernel on its own. Its inputs are what the earlier groups of the same forward wrote, so
@@ -168,11 +176,20 @@ int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void *hidden_in
  * launch, or no such group), or -1 for an invalid handle or rows. */
 int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
 
-/* A forward like moe_latent_forward, whose launch i also records the start and the end of
- * its own kernel into events[2 i] and events[2 i + 1] (hipEvent_t handles the caller created
- * with timing enabled; the timestamps come from the kernel's dispatch itself, no extra
- * packets), so that hipEventElapsedTime gives each launch's duration inside the forward. For
- * per-launch timing; it cannot be captured in a graph. n_events must be at least twice the
+/* The same count, and the group's stages (enum values of the work-item table, in layer
+ * order: 0 gate, 1 fc1, 2 shared up, 3 route, 4 shared down first half, 5 routed expert up,
+ * 6 shared down second half, 7 routed expert down, 8 fc2) and stream (0: the handle's
+ * stream, 1: its side stream) into the non-NULL pointers; for labelling per-launch
+ * measurements. */
+int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t group, int32_t *first_stage,
+                            int32_t *last_stage, int32_t *side);
+
+/* A forward like moe_latent_forward, whose launch i (launch group i) also records the start
+ * and the end of its own kernel into events[2 i] and events[2 i + 1] (hipEvent_t handles the
+ * caller created with timing enabled; the timestamps come from the kernel's dispatch itself,
+ * on the stream the launch runs on, no extra packets), so that hipEventElapsedTime gives each
+ * launch's duration inside the forward. For per-launch timing; it cannot be captured in a
+ * graph. n_events must be at least twice the
  * number of launch groups of the pass (MOE_ERR_INVALID_ARG otherwise); a launch with no work
  * leaves its two events untouched. */
 int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out,
@@ -181,10 +198,13 @@ int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const void *hidden_i
 /* Change the stream later forwards are enqueued on (e.g. a graph-capture stream). */
 int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
 
-/* Execution variant. 1 (the default and the only one available): the forward is a chain of
- * launches on the handle's stream (see the launch groups above). 0 (one fused launch per
- * forward, a dependency-ordered work queue) is reserved and refused with
- * MOE_ERR_INVALID_ARG: that variant is disabled until a failure of it is understood. */
+/* Execution variant (see the launch groups above): 2: the routed chain on the handle's stream
+ * and the shared expert on the handle's side stream, in parallel; 1: one chain of launches on
+ * the handle's stream, the shared expert's workgroups filling its launches; 3 (the default):
+ * variant 1 for a one-row pass and variant 2 for more rows (the side stream's fork and join
+ * cost more than they save in a one-row pass). All give the same bits. 0 (one fused launch per forward, a dependency-ordered work queue)
+ * is reserved and refused with MOE_ERR_INVALID_ARG: its first GPU run did not complete, and
+ * it is not built. Synchronises the handle's stream first. */
 int moe_latent_set_variant(moe_latent_t *h, int32_t variant);
 
 /* Copy the last forward's routing to device buffers, enqueued on the handle's stream:
@@ -223,7 +243,8 @@ int moe_latent_status(moe_latent_t *h);
  * valid until this thread's next call into the library; the library owns it. */
 const char *moe_latent_last_error(void);
 
-/* Number of device allocations the library currently holds (all handles). */
+/* Number of device allocations, streams and events the library currently holds (all
+ * handles); a handle holds its workspace, its side stream and two events. */
 int32_t moe_latent_live_allocations(void);
 
 /* A plain read-only stream over device memory, the reference beside the published HBM peak

@@ -81,6 +81,7 @@ def _load():
         "moe_latent_live_allocations": (ctypes.c_int32, []),
         "moe_latent_launch_group": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.c_int32]),
         "moe_latent_group_items": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32]),
+        "moe_latent_group_stages": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
         "moe_latent_forward_timed": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.POINTER(P), ctypes.c_int32]),
         "moe_latent_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
         "moe_latent_forward_static": (ctypes.c_int, [ctypes.POINTER(moe_latent_config),
@@ -99,7 +100,7 @@ EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "mo
             "moe_latent_set_variant", "moe_latent_get_routing", "moe_latent_read_stage",
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
             "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
-            "moe_latent_stream_read", "moe_latent_forward_static")
+            "moe_latent_stream_read", "moe_latent_forward_static", "moe_latent_group_stages")
 
 
 def lib():
@@ -188,6 +189,14 @@ def moe_latent_launch_group(h: int, rows: int, hidden_in: int, out: int, group: 
 
 def moe_latent_group_items(h: int, rows: int, group: int) -> int:
     return _lib.moe_latent_group_items(h, rows, group)
+
+
+def moe_latent_group_stages(h: int, rows: int, group: int):
+    """(workgroups, first stage, last stage, side) of launch group `group`; workgroups <= 0
+    when there is no such group."""
+    f, l, sd = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    n = _lib.moe_latent_group_stages(h, rows, group, ctypes.byref(f), ctypes.byref(l), ctypes.byref(sd))
+    return n, f.value, l.value, sd.value
 
 
 def moe_latent_forward_timed(h: int, rows: int, hidden_in: int, out: int, events) -> None:

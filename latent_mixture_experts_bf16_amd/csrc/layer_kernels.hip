@@ -539,7 +539,8 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
         st_shared32(p.idx + (size_t)r * p.K + j, ej);
         p.wts[(size_t)r * p.K + j] = v * p.rho;
         if (p.single_row) {
-            *(int4 *)(p.sched + SCH_REC + 4 * u) = make_int4(ej, u, 1, j);
+            *(int4 *)(p.sched + SCH_REC + SCH_RECW * u) = make_int4(ej, u, 1, j);
+            *(int4 *)(p.sched + SCH_REC + SCH_RECW * u + 4) = make_int4(-1, 0, 0, 0);
             p.sched[SCH_PAIRS + u] = j;
             if (j == 0) p.sched[SCH_U] = p.K;
         }
@@ -594,7 +595,7 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
     if (tid == WG_THREADS - 1) p.sched[SCH_U] = run_slots;
     // slots past U (up to the slots the item grid enumerates) are marked empty
     const int U = L.scan[WG_THREADS - 1] >> 16, umax = E < NP ? E : NP;
-    for (int u = U + tid; u < umax; u += WG_THREADS) *(int4 *)(p.sched + SCH_REC + 4 * u) = make_int4(-1, 0, 0, 0);
+    for (int u = U + tid; u < umax; u += WG_THREADS) *(int4 *)(p.sched + SCH_REC + SCH_RECW * u) = make_int4(-1, 0, 0, 0);
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) {
         const int e = ld_shared32(p.idx + i);
@@ -610,7 +611,10 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             while (b >= 0 && L.pairs[o + b] > v) { L.pairs[o + b + 1] = L.pairs[o + b]; --b; }
             L.pairs[o + b + 1] = v;
         }
-        if (n > 0) *(int4 *)(p.sched + SCH_REC + 4 * L.slot[e]) = make_int4(e, o, n, L.pairs[o]);
+        if (n > 0) {
+            *(int4 *)(p.sched + SCH_REC + SCH_RECW * L.slot[e]) = make_int4(e, o, n, L.pairs[o]);
+            *(int4 *)(p.sched + SCH_REC + SCH_RECW * L.slot[e] + 4) = make_int4(n > 1 ? L.pairs[o + 1] : -1, 0, 0, 0);
+        }
     }
     __syncthreads();
     for (int i = tid; i < NP; i += WG_THREADS) p.sched[SCH_PAIRS + i] = L.pairs[i];
@@ -1044,7 +1048,7 @@ __device__ __forceinline__ float x_chunk(const uint4 *x, int c, uint32_t *xq) {
 
 // Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
 // pair (row, pick) of that slot. The block's 4-bit codes, scales and biases and the first
-// pair's input row are staged in LDS (all in flight at once; every weight byte is read from
+// pairs' input rows are staged in LDS (all in flight at once; every weight byte is read from
 // HBM once, whatever the number of rows). Each output row's inputs are cut in chunks of 32
 // (16 bytes of codes). A group of P lanes covers the chunks of its output rows, lane t taking
 // chunks t, t + P, ... (at most 4): it keeps their inputs in registers as packed pairs and
@@ -1056,14 +1060,16 @@ __device__ __forceinline__ float x_chunk(const uint4 *x, int c, uint32_t *xq) {
 template <bool UP, int XMAX, bool F16>
 __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // the number of slots and the slot's record: independent loads
+    // the number of slots and the slot's record (expert, pairs, first two pairs): independent loads
     const int U = p.sched[SCH_U];
-    const int4 rec = *(const int4 *)(p.sched + SCH_REC + 4 * slot);
+    const int4 rec = *(const int4 *)(p.sched + SCH_REC + SCH_RECW * slot);
+    const int4 rec2 = *(const int4 *)(p.sched + SCH_REC + SCH_RECW * slot + 4);
     const int e = rec.x, off = rec.y, R = rec.z;
-    int pr = rec.w;
+    int pr = rec.w, pr2 = rec2.x;
     const int NP = p.rows * p.K;
     if (e == -1) return U;   // no expert in this slot for this pass
-    if (e < 0 || e >= p.E || off < 0 || R < 1 || off + R > NP || pr < 0 || pr >= NP) {   // never for a valid schedule
+    if (e < 0 || e >= p.E || off < 0 || R < 1 || off + R > NP || pr < 0 || pr >= NP ||
+        (R >= 2 && (pr2 < 0 || pr2 >= NP))) {   // never for a valid schedule
         if (threadIdx.x == 0) atomicOr(p.err, 4u);
         return 0;
     }
@@ -1104,9 +1110,11 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
         else st_shared16(p.eout + (size_t)q * p.D + n, f2act(F16, acc));   // combined in this one
     };
     constexpr bool PAIR2 = ExpertLds<XMAX>::XROWS == 2;
+    // scales, biases and the first pairs' input rows first, the codes last
     stage_lds<AUX_NT>((const uint4 *)S, (uint4 *)L.s, NB * G64 / 8);
     stage_lds<AUX_NT>((const uint4 *)B, (uint4 *)L.b, NB * G64 / 8);
     stage_lds((const uint4 *)xrow(pr), L.x, xu);
+    if (PAIR2 && R >= 2) stage_lds((const uint4 *)xrow(pr2), L.x + xu, xu);
     if (tiled) {
         const uint4 *src = (const uint4 *)Q;
         const int lp = __builtin_ctz(P), lg = __builtin_ctz(NG), lr = __builtin_ctz(RG);   // powers of two
@@ -1120,11 +1128,6 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
         }
     } else {
         stage_lds<AUX_NT>((const uint4 *)Q, L.q, NB * C);
-    }
-    int pr2 = 0;
-    if (PAIR2 && R >= 2) {   // the second pair's row, its index read while the codes are in flight
-        pr2 = pair_at(1);
-        stage_lds((const uint4 *)xrow(pr2), L.x + xu, xu);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1200,25 +1203,7 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
             xs[m] = 0.0f;
 #pragma unroll
             for (int k = 0; k < 16; ++k) xq[m][k] = 0u;
-            if (m < nch && c < C) {
-                uint32_t xw[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const uint4 v4 = lds_ld16(&L.x[4 * c + q4]);
-                    xw[4 * q4] = v4.x; xw[4 * q4 + 1] = v4.y; xw[4 * q4 + 2] = v4.z; xw[4 * q4 + 3] = v4.w;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    xq[m][4 * j] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x05040100u);
-                    xq[m][4 * j + 1] = __builtin_amdgcn_perm(xw[4 * j + 2], xw[4 * j], 0x07060302u);
-                    xq[m][4 * j + 2] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x05040100u);
-                    xq[m][4 * j + 3] = __builtin_amdgcn_perm(xw[4 * j + 3], xw[4 * j + 1], 0x07060302u);
-                }
-                float sx = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) sx = dot2<F16>(F16 ? 0x3C003C00u : 0x3F803F80u, xw[k], sx);
-                xs[m] = sx;
-            }
+            if (m < nch && c < C) xs[m] = x_chunk<F16>(L.x, c, xq[m]);
         }
         for (int rb = 0; rb < RG; rb += 2) {
             // 2 rows at a time, without branches (rows past NB read row NB - 1, dropped below)
@@ -1388,6 +1373,10 @@ template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true>(LayerParams, in
 template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, int, int, int, int);
 template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int, int);
 template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int, int);
+// the shared expert on its own stream
+template __global__ void moe_stage_kernel<ST_SHUP, ST_SHUP, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_SHDN_A, ST_SHDN_A, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_SHDN_B, ST_SHDN_B, false>(LayerParams, int, int, int, int);
 
 // Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
 // grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);

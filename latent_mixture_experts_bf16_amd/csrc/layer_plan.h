@@ -39,14 +39,16 @@ enum : int {
 };
 
 // schedule block (int32) in the workspace: [SCH_U] = U (distinct experts picked); the
-// record of slot u at [SCH_REC + 4u] = {expert, offset of its pairs, number of pairs, first
-// pair} (slots in increasing expert id; a slot past U holds expert -1), so that an item
-// reads its slot with one 16-byte load; [SCH_PAIRS + i] = pair row * top_k + pick, sorted by
-// (expert, row).
+// record of slot u at [SCH_REC + SCH_RECW u] = {expert, offset of its pairs, number of pairs,
+// first pair, second pair (or -1), 0, 0, 0} (slots in increasing expert id; a slot past U
+// holds expert -1), so that an item reads its slot, and the input rows of its first two
+// pairs, with two adjacent 16-byte loads; [SCH_PAIRS + i] = pair row * top_k + pick, sorted
+// by (expert, row).
 enum : int {
     SCH_U = 0,
-    SCH_REC = 4,
-    SCH_PAIRS = SCH_REC + 4 * MAX_EXPERTS,
+    SCH_RECW = 8,
+    SCH_REC = 8,
+    SCH_PAIRS = SCH_REC + SCH_RECW * MAX_EXPERTS,
     SCH_COUNT = SCH_PAIRS + MAX_ROWS * MAX_TOPK,
 };
 

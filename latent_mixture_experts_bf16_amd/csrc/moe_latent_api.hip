@@ -31,7 +31,11 @@ using namespace moe;
 struct moe_latent {
     moe_latent_config cfg;
     LayerParams base;       // sizes, weights and workspace pointers; per-forward fields set later
-    hipStream_t stream;
+    hipStream_t stream;     // the caller's stream: forwards start and end on it
+    hipStream_t side;       // the handle's own stream (default priority) for the shared expert
+    hipEvent_t ev_fork;     // recorded on `stream` when a forward starts; `side` waits for it
+    hipEvent_t ev_join;     // recorded on `side` after its work; `stream` waits for it
+    int variant;            // 1: one stream; 2: two streams; 3 (default): by row count
     int device;
     int last_rows;
     void *ws;               // one workspace allocation
@@ -78,6 +82,26 @@ static hipError_t dev_alloc(void **p, size_t bytes) {
 
 static void dev_free(void *p) {
     if (p && hipFree(p) == hipSuccess) --g_live_allocs;
+}
+
+// The handle's side stream and events, counted and failure-injected like allocations.
+static hipError_t side_stream_create(hipStream_t *s) {
+    if (inject_failure()) { *s = nullptr; return hipErrorOutOfMemory; }
+    hipError_t e = hipStreamCreateWithFlags(s, hipStreamNonBlocking);   // default priority
+    if (e == hipSuccess) ++g_live_allocs;
+    return e;
+}
+static void side_stream_destroy(hipStream_t s) {
+    if (s && hipStreamDestroy(s) == hipSuccess) --g_live_allocs;
+}
+static hipError_t event_create(hipEvent_t *ev) {
+    if (inject_failure()) { *ev = nullptr; return hipErrorOutOfMemory; }
+    hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e == hipSuccess) ++g_live_allocs;
+    return e;
+}
+static void event_destroy(hipEvent_t ev) {
+    if (ev && hipEventDestroy(ev) == hipSuccess) --g_live_allocs;
 }
 
 // ------------------------------------------------------------------ validation
@@ -335,12 +359,21 @@ extern "C" const char *moe_latent_last_error(void) { return g_err.c_str(); }
 
 extern "C" int32_t moe_latent_live_allocations(void) { return g_live_allocs.load(); }
 
-extern "C" void moe_latent_destroy(moe_latent_t *h) {
-    if (!h || h->magic != kMagic) return;
-    (void)hipStreamSynchronize(h->stream);
+// Release everything a handle holds (each part may be missing after a failed create).
+static void release(moe_latent *h) {
+    if (h->side) (void)hipStreamSynchronize(h->side);
+    event_destroy(h->ev_fork);
+    event_destroy(h->ev_join);
+    side_stream_destroy(h->side);
     dev_free(h->ws);
     h->magic = 0;
     delete h;
+}
+
+extern "C" void moe_latent_destroy(moe_latent_t *h) {
+    if (!h || h->magic != kMagic) return;
+    (void)hipStreamSynchronize(h->stream);
+    release(h);
 }
 
 // Sizes, switches and weight pointers of a validated configuration.
@@ -390,20 +423,29 @@ extern "C" int moe_latent_create(const moe_latent_config *cfg, const moe_latent_
     memset(&h->base, 0, sizeof h->base);
     h->cfg = *cfg;
     h->stream = (hipStream_t)hip_stream;
+    h->side = nullptr;
+    h->ev_fork = h->ev_join = nullptr;
+    h->variant = 3;
+    h->ws = nullptr;
     h->device = dev;
     h->magic = kMagic;
     h->last_rows = 0;
+    h->cus = cus;
     fill_params(*cfg, *w, h->base);
 
     if ((rc = setup_workspace(h))) {
-        delete h;
+        release(h);
         return rc;
     }
-    h->cus = cus;
     hipError_t e;
+    if ((e = side_stream_create(&h->side)) != hipSuccess || (e = event_create(&h->ev_fork)) != hipSuccess ||
+        (e = event_create(&h->ev_join)) != hipSuccess) {
+        release(h);
+        return fail(e == hipErrorOutOfMemory ? MOE_ERR_OOM : MOE_ERR_HIP, "side stream or events: %s",
+                    hipGetErrorString(e));
+    }
     if ((e = clear_flag(h)) != hipSuccess || (e = hipStreamSynchronize(h->stream)) != hipSuccess) {
-        dev_free(h->ws);
-        delete h;
+        release(h);
         return fail(MOE_ERR_HIP, "initialising the workspace: %s", hipGetErrorString(e));
     }
     *out = h;
@@ -421,23 +463,49 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 // One launch of a forward: the items of stages [first, last], run by the kernel instance
 // `kernel` (its template range covers them), dispatched in table order, except that with
 // split >= 0 the first `pre` items of stage `split` on are dispatched first (see
-// moe_stage_kernel).
-enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2 };
+// moe_stage_kernel). side: 0 on the caller's stream, 1 on the handle's side stream; join: the
+// launch first waits for the side stream's work of this forward.
+enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B };
 struct Launch {
-    int first, last, kernel, split, pre;
+    int first, last, kernel, split, pre, side, join;
 };
+constexpr int MAX_LAUNCHES = 10;
 
-// The launches of one forward, in order (see layer_kernels.hip). Returns their number.
-static int plan_launches(const LayerParams &p, int cus, Launch *out) {
+// The launches of one forward, in enqueue order (see layer_kernels.hip). Returns their number.
+//   variant 2 (two streams): the shared expert depends on nothing but the layer input, so it
+//     runs on the side stream (shared up, then the two halves of shared down) while the
+//     caller's stream runs the routed chain; fc2, which adds the shared output, waits for it.
+//   variant 1 (one stream): the shared expert's items fill the chain's launches.
+static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out) {
     int n = 0;
-    auto add = [&](int f, int l, int k, int split = -1, int pre = 0) { out[n++] = Launch{f, l, k, split, pre}; };
+    // variant 3 (the default): one stream for a one-row pass, two streams above. Measured on
+    // the Bolt-like layer: a one-row forward takes 52 us on two streams against 38 us on one
+    // (the side stream's fork and join cost more than the overlap saves in so short a pass);
+    // the 64-row stack 361 us per layer against 394, the 16-row pass 149 against 151.
+    if (variant == 3) variant = p.single_row ? 1 : 2;
+    auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0) {
+        out[n++] = Launch{f, l, k, split, pre, side, join};
+    };
+    if (variant == 2) {
+        add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item first
+        if (p.SI) {
+            add(ST_SHUP, ST_SHUP, K_SHUP, -1, 0, 1);
+            add(ST_SHDN_A, ST_SHDN_A, K_SHDN_A, -1, 0, 1);
+            add(ST_SHDN_B, ST_SHDN_B, K_SHDN_B, -1, 0, 1);
+        }
+        if (!p.single_row) add(ST_ROUTE, ST_ROUTE, K_ROUTE_UP);
+        add(ST_UP, ST_UP, K_ROUTE_UP);
+        add(ST_DOWN, ST_DOWN, K_UP_DOWN);
+        if (p.L) add(ST_FC2, ST_FC2, K_FC2, -1, 0, 0, p.SI ? 1 : 0);
+        return n;
+    }
     if (p.single_row) {
         // Expert launches: the workgroups go to the compute units round-robin in dispatch
         // order, so (cus - shared down items) expert items go first, then the 128 KB shared
         // down items, each on a compute unit of its own, then the other expert items.
         auto pre = [&](int shdn, int ex) {
-            const int s = p.item_base[shdn + 1] - p.item_base[shdn], e = p.item_base[ex + 1] - p.item_base[ex];
-            const int a = cus - s;
+            const int sd = p.item_base[shdn + 1] - p.item_base[shdn], e = p.item_base[ex + 1] - p.item_base[ex];
+            const int a = cus - sd;
             return a <= 0 ? 0 : (a < e ? a : e);
         };
         add(ST_GATE, ST_SHUP, K_GATE_SHUP);
@@ -480,24 +548,56 @@ static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hi
             if (wide) launch_kernel<ST_UP, ST_DOWN, true>(p, l, st, ev0, ev1);
             else launch_kernel<ST_UP, ST_DOWN, false>(p, l, st, ev0, ev1);
             break;
+        case K_SHUP: launch_kernel<ST_SHUP, ST_SHUP, false>(p, l, st, ev0, ev1); break;
+        case K_SHDN_A: launch_kernel<ST_SHDN_A, ST_SHDN_A, false>(p, l, st, ev0, ev1); break;
+        case K_SHDN_B: launch_kernel<ST_SHDN_B, ST_SHDN_B, false>(p, l, st, ev0, ev1); break;
         default: launch_kernel<ST_FC2, ST_FC2, false>(p, l, st, ev0, ev1); break;
     }
 }
 
-// Enqueue a whole forward (g == -1), or launch g alone.
-static void enqueue(const moe_latent *h, const LayerParams &p, int g) {
-    Launch ls[8];
-    const int n = plan_launches(p, h->cus, ls);
-    for (int i = 0; i < n; ++i)
-        if (g == -1 || g == i) launch_one(p, ls[i], h->stream);
+// Enqueue a whole forward (g == -1) on the handle's streams, or launch g alone on the caller's
+// stream. A whole forward forks the side stream off the caller's stream before its first
+// launch and joins it back before the launch marked `join` (or at the end), so that the
+// forward starts and ends on the caller's stream (and a graph captured there holds both
+// branches). evs: per launch i, events to record its kernel's start and end into (or null).
+static void enqueue(const moe_latent *h, const LayerParams &p, int g, void *const *evs = nullptr) {
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
+    bool forked = false, joined = false;
+    for (int i = 0; i < n; ++i) {
+        if (g != -1 && g != i) continue;
+        const Launch &l = ls[i];
+        hipStream_t st = h->stream;
+        if (g == -1 && l.side) {
+            if (!forked) {
+                (void)hipEventRecord(h->ev_fork, h->stream);
+                (void)hipStreamWaitEvent(h->side, h->ev_fork, 0);
+                forked = true;
+            }
+            st = h->side;
+        }
+        if (g == -1 && l.join && forked && !joined) {
+            (void)hipEventRecord(h->ev_join, h->side);
+            (void)hipStreamWaitEvent(h->stream, h->ev_join, 0);
+            joined = true;
+        }
+        launch_one(p, l, st, evs ? (hipEvent_t)evs[2 * i] : nullptr, evs ? (hipEvent_t)evs[2 * i + 1] : nullptr);
+    }
+    if (forked && !joined) {
+        (void)hipEventRecord(h->ev_join, h->side);
+        (void)hipStreamWaitEvent(h->stream, h->ev_join, 0);
+    }
 }
 
 extern "C" int moe_latent_set_variant(moe_latent_t *h, int32_t variant) {
     if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
     if (variant == 0)
         return fail(MOE_ERR_INVALID_ARG, "variant 0 (one fused launch per forward) is disabled: its first "
-                    "GPU run did not complete and the cause is not yet found");
-    if (variant != 1) return fail(MOE_ERR_INVALID_ARG, "variant %d (1: the launch chain)", variant);
+                    "GPU run did not complete (see the description of moe_latent_set_variant)");
+    if (variant < 1 || variant > 3)
+        return fail(MOE_ERR_INVALID_ARG, "variant %d (1: one stream, 2: two streams, 3: by row count)", variant);
+    (void)hipStreamSynchronize(h->stream);
+    h->variant = variant;
     return MOE_OK;
 }
 
@@ -567,8 +667,8 @@ extern "C" int moe_latent_launch_group(moe_latent_t *h, int32_t rows, const void
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    Launch ls[8];
-    const int n = plan_launches(p, h->cus, ls);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
     if (group < 0 || group >= n) return fail(MOE_ERR_INVALID_ARG, "group %d outside 0..%d", group, n - 1);
     enqueue(h, p, group);
     hipError_t e = hipGetLastError();
@@ -583,13 +683,13 @@ extern "C" int moe_latent_forward_timed(moe_latent_t *h, int32_t rows, const voi
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);
-    Launch ls[8];
-    const int n = plan_launches(p, h->cus, ls);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
     if (!events || n_events < 2 * n)
         return fail(MOE_ERR_INVALID_ARG, "events: %d given, 2 per launch group (%d groups) needed", n_events, n);
     for (int i = 0; i < 2 * n; ++i)
         if (!events[i]) return fail(MOE_ERR_INVALID_ARG, "events[%d] is NULL", i);
-    for (int i = 0; i < n; ++i) launch_one(p, ls[i], h->stream, (hipEvent_t)events[2 * i], (hipEvent_t)events[2 * i + 1]);
+    enqueue(h, p, -1, events);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
     h->last_rows = rows;
@@ -617,9 +717,23 @@ extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t gro
     if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
     LayerParams p = h->base;
     plan_items(p, rows);
-    Launch ls[8];
-    const int n = plan_launches(p, h->cus, ls);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
     if (group < 0 || group >= n) return 0;
+    return p.item_base[ls[group].last + 1] - p.item_base[ls[group].first];
+}
+
+extern "C" int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t group, int32_t *first_stage,
+                                       int32_t *last_stage, int32_t *side) {
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
+    LayerParams p = h->base;
+    plan_items(p, rows);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
+    if (group < 0 || group >= n) return 0;
+    if (first_stage) *first_stage = ls[group].first;
+    if (last_stage) *last_stage = ls[group].last;
+    if (side) *side = ls[group].side;
     return p.item_base[ls[group].last + 1] - p.item_base[ls[group].first];
 }
 
@@ -667,6 +781,7 @@ extern "C" int moe_latent_read_stage(moe_latent_t *h, int32_t stage, void *dst_d
 extern "C" int moe_latent_status(moe_latent_t *h) {
     if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
     hipError_t e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->side);
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "stream: %s", hipGetErrorString(e));
     uint32_t flag = 0;
     e = hipMemcpy(&flag, h->base.err, 4, hipMemcpyDeviceToHost);
@@ -754,8 +869,8 @@ extern "C" int moe_latent_forward_static(const moe_latent_config *cfg, const moe
     // layer, left its own contents): fill kernels, no memset
     hipLaunchKernelGGL(moe_clear_kernel, dim3(1), dim3(64), 0, st, p.err, 64);
     hipLaunchKernelGGL(moe_clear_kernel, dim3((n_ctr + 255) / 256), dim3(256), 0, st, p.ctr, n_ctr);
-    Launch ls[8];
-    const int n = plan_launches(p, cus, ls);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, cus, 1, ls);   // one stream: this call owns no side stream
     for (int i = 0; i < n; ++i) launch_one(p, ls[i], st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));

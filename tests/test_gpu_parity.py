@@ -354,8 +354,25 @@ def test_timed_forward_equals_forward_and_records_each_launch():
     ref = torch.empty_like(xd)
     lay.forward(xd, ref)
     torch.cuda.synchronize()
-    ng = sum(1 for g in range(8) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
-    assert ng == 4
+    ng = sum(1 for g in range(10) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
+    assert ng == 4      # one row, one stream: gate + fc1 + shared up, up, down, fc2
+    B.moe_latent_set_variant(lay.handle, 2)
+    ng2 = sum(1 for g in range(10) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
+    assert ng2 == 7     # two streams: gate + fc1, shared up, shared down x 2, expert up, down, fc2
+    sides = [B.moe_latent_group_stages(lay.handle, 1, g)[3] for g in range(ng2)]
+    assert sides == [0, 1, 1, 1, 0, 0, 0]
+    evs2 = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ng2)]
+    for e in evs2:
+        e.record()
+    torch.cuda.synchronize()
+    out2 = torch.empty_like(xd)
+    B.moe_latent_forward_timed(lay.handle, 1, xd.data_ptr(), out2.data_ptr(), [e.cuda_event for e in evs2])
+    torch.cuda.synchronize()
+    lay.status()
+    assert np.array_equal(out2.cpu().numpy(), ref.cpu().numpy())
+    for g in range(ng2):
+        assert evs2[2 * g].elapsed_time(evs2[2 * g + 1]) > 0.0, g
+    B.moe_latent_set_variant(lay.handle, 3)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ng)]
     for e in evs:
         e.record()
@@ -580,22 +597,23 @@ def test_rows_and_alias_refused():
 
 
 def test_injected_allocation_failure_releases_everything():
-    """A create whose first device allocation fails (MOE_LATENT_FAIL_ALLOC_AT=1 counts from
-    the moment the variable is set) returns MOE_ERR_OOM with *out NULL and leaves the live
-    allocation count unchanged; with the variable cleared a create succeeds again (TensorFold
-    pull request 1038, review thread: a failed load releases what it built)."""
+    """A create whose n-th device allocation or runtime object fails (MOE_LATENT_FAIL_ALLOC_AT=n
+    counts from the moment the variable is set: 1 the workspace, 2 the side stream, 3 and 4
+    its events) returns MOE_ERR_OOM with *out NULL and leaves the live count unchanged; with
+    the variable cleared a create succeeds again (TensorFold pull request 1038, review thread:
+    a failed load releases what it built)."""
     from latent_mixture_experts_bf16_amd import binding as B
     dims, arrays = workload(0)
     lay = _LY().DeviceLayer(dims, arrays, 1)      # device copies of the weights
     before = B.moe_latent_live_allocations()
-    for n in (1, 2, 3):
+    for n in (1, 2, 3, 4, 5):      # the workspace, the side stream, the two events, none
         os.environ["MOE_LATENT_FAIL_ALLOC_AT"] = str(n)
         try:
             rc, h = B.moe_latent_create_rc(lay.cfg, lay.w)
         finally:
             del os.environ["MOE_LATENT_FAIL_ALLOC_AT"]
-        if n == 1:
-            assert B.STATUS[rc] == "MOE_ERR_OOM", (rc, B.moe_latent_last_error())
+        if n <= 4:
+            assert B.STATUS[rc] == "MOE_ERR_OOM", (n, rc, B.moe_latent_last_error())
         if rc:
             assert h is None, n
             assert B.moe_latent_live_allocations() == before, n
@@ -626,9 +644,29 @@ def test_variant_zero_is_refused():
     with pytest.raises(B.MoeError):
         B.moe_latent_set_variant(lay.handle, 0)
     with pytest.raises(B.MoeError):
-        B.moe_latent_set_variant(lay.handle, 2)
-    B.moe_latent_set_variant(lay.handle, 1)
+        B.moe_latent_set_variant(lay.handle, 4)
+    for v in (1, 2, 3):
+        B.moe_latent_set_variant(lay.handle, v)
     lay.close()
+
+
+@pytest.mark.parametrize("cid", [0, 1, 2, 3])
+def test_one_stream_and_two_stream_variants_agree_bitwise(cid):
+    """The shared expert on the side stream (variant 2) and inside the chain's launches
+    (variant 1) give the same bits: outputs, routing, and every stage."""
+    dims, arrays = workload(cid)
+    rows = arrays["x"].shape[0]
+    res = []
+    for variant in (1, 2, 3):
+        lay, xd, out = run_gpu(dims, arrays, variant=variant)
+        st = [lay.stage(n, rows) for n in ("logits", "expert_act", "expert_out", "combine")]
+        if dims.shared_inter:
+            st += [lay.stage("shared_act", rows), lay.stage("shared_out", rows)]
+        res.append((out.cpu().numpy(), *lay.routing(rows), *st))
+        lay.close()
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert np.array_equal(a, b)
 
 
 def test_wrong_architecture_and_device_checks_pass_on_gfx950():
