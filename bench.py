@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--no-rows-sweep", action="store_true",
                     help="skip the 16-row and 64-row passes reported beside the one-row line")
+    ap.add_argument("--no-lm-head", action="store_true",
+                    help="skip the lm_head gemv (K 4096, N 131072, 1 and 16 rows) reported beside it")
     return ap.parse_args()
 
 
@@ -493,8 +495,50 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_rows_sweep and rows == 1:
         line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
+    if not args.no_lm_head and rows == 1:
+        line["lm_head"] = lm_head_bench(B, LY, synth)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def lm_head_bench(B, LY, synth, K=4096, N=131072, reps=40):
+    """The bf16 lm_head gemv beside the layer (K = 4096, N = 131072: 1 GiB of weights, four
+    times the 256 MB cache, so every replay streams from HBM), at 1 and 16 rows, bf16 output:
+    graph replays timed with events; algorithmic bytes = weights + input rows + outputs."""
+    import torch
+    d = synth.make_lm_head(K, N, 16, seed=2718)
+    wd = LY.to_device(d["w"])
+    xd = LY.to_device(d["x"])
+    del d
+    desc = B.make_tensor(wd.data_ptr(), B.MOE_DT_BF16, [N, K])
+    s = torch.cuda.Stream()
+    res = {"K": K, "N": N, "weight_bytes": N * K * 2, "kernel": "moe_lm_head_kernel"}
+    for rows in (1, 16):
+        out = torch.empty((rows, N), dtype=torch.int16, device="cuda")
+        with torch.cuda.stream(s):
+            B.moe_lm_head_gemv(desc, rows, xd.data_ptr(), out.data_ptr(), B.MOE_DT_BF16, s.cuda_stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(4):
+                    B.moe_lm_head_gemv(desc, rows, xd.data_ptr(), out.data_ptr(), B.MOE_DT_BF16, s.cuda_stream)
+            for _ in range(3):
+                g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps // 4):
+                g.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = N * K * 2 + rows * K * 2 + rows * N * 2
+        gbps = nbytes / (us * 1e-6) / 1e9
+        res[f"rows{rows}"] = {"us": round(us, 2), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                              "tokens_per_s": round(rows / (us * 1e-6), 1)}
+        del g, out
+    print(f"[bench] lm_head: {json.dumps(res)}", file=sys.stderr, flush=True)
+    del wd, xd
+    torch.cuda.empty_cache()
+    return res
 
 
 def profile_stack(args, B, LY, synth):

@@ -259,6 +259,21 @@ int32_t moe_latent_live_allocations(void);
  * size. */
 int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *sink_dev, void *hip_stream);
 
+/* The bf16 lm_head gemv beside the layer (TensorFold pull request 1038, «Per operator and
+ * row invariance», its lm_head rows: K = 4096 inputs, N = 131072 outputs, at 1 and 16 rows):
+ * out[r][n] = sum_k w[n][k] * x[r][k], products exact in fp32 and summed in fp32, then stored
+ * as fp32 (out_dtype MOE_DT_F32) or rounded to bf16 (MOE_DT_BF16, round to nearest even).
+ *   w    [N][K] bf16, row-major (borrowed; N a multiple of 16, K a multiple of 128)
+ *   x    [rows][K] bf16, 1 <= rows <= 256
+ *   out  [rows][N] fp32 or bf16 (caller's; may not overlap x or w)
+ * All device pointers, 16-byte aligned. Each row's result does not depend on the other rows
+ * of the call (bit for bit). One launch on hip_stream (NULL: the null stream); no allocation,
+ * no synchronisation; it can be captured in a HIP graph. Errors: MOE_ERR_LAYOUT (rank, strides,
+ * alignment), MOE_ERR_DTYPE, MOE_ERR_SHAPE (N or K), MOE_ERR_ROWS, MOE_ERR_ALIAS,
+ * MOE_ERR_DEVICE (not gfx950), MOE_ERR_HIP (launch). */
+int moe_lm_head_gemv(const moe_tensor *w, int32_t rows, const void *x, void *out, int32_t out_dtype,
+                     void *hip_stream);
+
 /* Size of the static workspace of moe_latent_forward_static, per GPU (16 MiB: a Bolt-like
  * layer of hidden 4096, latent 1024, 9 picks of 2048-wide experts and a 4096-wide shared
  * expert fits up to about 100 rows). */

@@ -84,6 +84,7 @@ def _load():
         "moe_latent_group_stages": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
         "moe_latent_forward_timed": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.POINTER(P), ctypes.c_int32]),
         "moe_latent_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
+        "moe_lm_head_gemv": (ctypes.c_int, [ctypes.POINTER(moe_tensor), ctypes.c_int32, P, P, ctypes.c_int32, P]),
         "moe_latent_forward_static": (ctypes.c_int, [ctypes.POINTER(moe_latent_config),
                                                      ctypes.POINTER(moe_latent_weights), ctypes.c_int32,
                                                      P, P, P]),
@@ -100,7 +101,8 @@ EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "mo
             "moe_latent_set_variant", "moe_latent_get_routing", "moe_latent_read_stage",
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
             "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
-            "moe_latent_stream_read", "moe_latent_forward_static", "moe_latent_group_stages")
+            "moe_latent_stream_read", "moe_latent_forward_static", "moe_latent_group_stages",
+            "moe_lm_head_gemv")
 
 
 def lib():
@@ -219,3 +221,12 @@ def moe_latent_forward_static_rc(cfg: moe_latent_config, weights: moe_latent_wei
                                  out: int, stream: int = 0) -> int:
     return _lib.moe_latent_forward_static(ctypes.byref(cfg), ctypes.byref(weights), rows, hidden_in, out,
                                           stream or None)
+
+
+def moe_lm_head_gemv(w: moe_tensor, rows: int, x: int, out: int, out_dtype: int = MOE_DT_F32, stream: int = 0) -> None:
+    _check(_lib.moe_lm_head_gemv(ctypes.byref(w), rows, x, out, out_dtype, stream or None))
+
+
+def moe_lm_head_gemv_rc(w: moe_tensor, rows: int, x: int, out: int, out_dtype: int = MOE_DT_F32,
+                        stream: int = 0) -> int:
+    return _lib.moe_lm_head_gemv(ctypes.byref(w), rows, x, out, out_dtype, stream or None)

@@ -685,7 +685,7 @@ __device__ __forceinline__ void combine4(const LayerParams &p, int r, int d, flo
 
 // ------------------------------------------------------------------ dense bf16 tiles (MFMA)
 
-enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3 };
+enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3, EPI_LMH = 4 };
 
 template <int NW>
 struct DenseLds {
@@ -749,6 +749,9 @@ __device__ __forceinline__ void dense_epilogue(const LayerParams &p, int epi, in
         p.shact[(size_t)row * p.SI + n] = f2bf(relu_sq(0, rnd(0, a)));
     } else if (epi == EPI_SHDN) {
         p.shout[(size_t)row * p.H + n] = f2bf(a);
+    } else if (epi == EPI_LMH) {
+        if (p.lm_f32) ((float *)p.lm_out)[(size_t)row * p.lm_n + n] = a;
+        else ((uint16_t *)p.lm_out)[(size_t)row * p.lm_n + n] = f2bf(a);
     } else {
         // both loads unconditional (the shared output buffer always exists), so they overlap
         const float sh = bf2f(p.shout[(size_t)row * p.H + n]);
@@ -1405,6 +1408,18 @@ __global__ void __launch_bounds__(256) moe_stream_read_kernel(const uint4 *__res
         for (int d = 32; d >= 1; d >>= 1) r ^= __shfl_xor(r, d, 64);
         if (threadIdx.x == 0) atomicXor(sink, r);
     }
+}
+
+// The bf16 lm_head gemv (TensorFold pull request 1038, «Per operator and row invariance»,
+// the lm_head rows: K = 4096 inputs, N = 131072 outputs, at 1 and 16 rows): out = W . x for
+// every row, fp32 sums, with the layer's dense tiles -- 16 outputs over all K per workgroup,
+// each input row its own MFMA column, so a row's result does not depend on the other rows.
+// One workgroup per tile; tiles [lo, hi) of this launch.
+__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(3, 8)))
+moe_lm_head_kernel(LayerParams p, const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, int K, int lo) {
+    __shared__ DenseLds<WG_THREADS / 64> lds;
+    __shared__ int s_flag;
+    dense_item<EPI_LMH, WG_THREADS / 64>(p, W, X, K, lo + (int)blockIdx.x, 0, 1, nullptr, nullptr, lds, &s_flag);
 }
 
 // zero a small device buffer (the error flag) without a memset node in captured graphs

@@ -107,6 +107,10 @@ struct LayerParams {
     // which the route item polls for at most wait_ticks ticks of the 100 MHz real-time counter
     int ctr_hand;
     uint32_t wait_ticks;
+    // the lm_head gemv (a separate entry point sharing the dense tiles): out [rows][lm_n],
+    // fp32 (lm_f32) or bf16
+    void *lm_out;
+    int lm_n, lm_f32;
 };
 
 }  // namespace moe

@@ -24,6 +24,7 @@ namespace moe {
 template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
+__global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint16_t *X, int K, int lo);
 }  // namespace moe
 
 using namespace moe;
@@ -874,5 +875,48 @@ extern "C" int moe_latent_forward_static(const moe_latent_config *cfg, const moe
     for (int i = 0; i < n; ++i) launch_one(p, ls[i], st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    return MOE_OK;
+}
+
+// ------------------------------------------------------------------ lm_head gemv
+
+extern "C" int moe_lm_head_gemv(const moe_tensor *w, int32_t rows, const void *x, void *out, int32_t out_dtype,
+                                void *hip_stream) {
+    g_err.clear();
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "lm_head: weight descriptor is NULL");
+    if (w->ndim != 2) return fail(MOE_ERR_LAYOUT, "lm_head: rank %d, expected 2 ([N][K])", w->ndim);
+    const int64_t N = w->shape[0], K = w->shape[1];
+    {
+        const int64_t shape[2] = {N, K};
+        int rc = check_tensor("lm_head", *w, MOE_DT_BF16, 2, shape);
+        if (rc) return rc;
+    }
+    if (N < 16 || N % 16 || N / 16 > (int64_t)1 << 30)
+        return fail(MOE_ERR_SHAPE, "lm_head: N %lld must be a positive multiple of 16 (tiles of 16 outputs)",
+                    (long long)N);
+    if (K < 128 || K % 128 || K > (int64_t)1 << 20)
+        return fail(MOE_ERR_SHAPE, "lm_head: K %lld must be a multiple of 128, at most 2^20", (long long)K);
+    if (rows < 1 || rows > MAX_ROWS) return fail(MOE_ERR_ROWS, "lm_head: rows %d outside 1..%d", rows, (int)MAX_ROWS);
+    if (out_dtype != MOE_DT_BF16 && out_dtype != MOE_DT_F32)
+        return fail(MOE_ERR_DTYPE, "lm_head: out dtype %s (bf16 or f32)", dt_name(out_dtype));
+    if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "lm_head: x or out is NULL");
+    if (((uintptr_t)x | (uintptr_t)out) & 15) return fail(MOE_ERR_LAYOUT, "lm_head: x and out must be 16-byte aligned");
+    const size_t xb = (size_t)rows * K * 2, ob = (size_t)rows * N * (out_dtype == MOE_DT_F32 ? 4 : 2);
+    const char *xa = (const char *)x, *oa = (const char *)out, *wa = (const char *)w->data;
+    const size_t wb = (size_t)N * K * 2;
+    if ((xa < oa + ob && oa < xa + xb) || (wa < oa + ob && oa < wa + wb))
+        return fail(MOE_ERR_ALIAS, "lm_head: out overlaps x or the weights");
+    int dev = 0, cus = 0, rc;
+    if ((rc = check_device(&dev, &cus))) return rc;
+    LayerParams p;
+    memset(&p, 0, sizeof p);
+    p.rows = rows;
+    p.lm_out = out;
+    p.lm_n = (int)N;
+    p.lm_f32 = out_dtype == MOE_DT_F32;
+    hipLaunchKernelGGL(moe_lm_head_kernel, dim3((unsigned)(N / 16)), dim3(WG_THREADS), 0, (hipStream_t)hip_stream, p,
+                       (const uint16_t *)w->data, (const uint16_t *)x, (int)K, 0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "lm_head launch: %s", hipGetErrorString(e));
     return MOE_OK;
 }

@@ -175,3 +175,17 @@ def workload_layers(cfg_id: int, instance: int = 0, rows: Optional[int] = None,
         if xs is not None:
             xs = xs + 100 * instance
         yield dims, make_layer(dims, r, ws, xs)
+
+
+def make_lm_head(K: int, N: int, rows: int, seed: int) -> Dict[str, np.ndarray]:
+    """A bf16 lm_head and its input rows: W [N][K] N(0, 0.02), x [rows][K] N(0, 1), drawn as
+    float32 normals (in blocks of rows, so that the 1 GiB matrix of K = 4096, N = 131072
+    needs no float64 copy) and rounded to bf16 (nearest even). x is drawn first."""
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits(rng.standard_normal(size=(rows, K), dtype=np.float32))
+    W = np.empty((N, K), np.uint16)
+    step = 4096
+    for n in range(0, N, step):
+        m = min(step, N - n)
+        W[n:n + m] = f32_to_bf16_bits(rng.standard_normal(size=(m, K), dtype=np.float32) * np.float32(0.02))
+    return {"x": x, "w": W}

@@ -18,7 +18,7 @@ FAKE = 0x10000   # a non-NULL address; refused descriptors are never dereference
 def _header_functions():
     with open(os.path.join(ROOT, "include", "moe_latent.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"\b(moe_latent_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_(?:latent|lm)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -148,3 +148,25 @@ def test_null_arguments():
     assert B.lib().moe_latent_stream_read(16, 24, 64, None) == 1
     B.moe_latent_destroy(None)   # NULL-safe
     assert B.lib().moe_latent_status(None) == 1
+
+
+def test_lm_head_refusals_before_the_device():
+    """moe_lm_head_gemv refuses bad descriptors, sizes, rows and dtypes by name before it
+    looks for a device (no GPU here)."""
+    def rc(shape=(64, 256), dtype=B.MOE_DT_BF16, rows=1, out_dtype=B.MOE_DT_F32, strides=None, x=FAKE, out=FAKE * 4):
+        t = B.make_tensor(FAKE, dtype, list(shape), strides)
+        return B.STATUS[B.moe_lm_head_gemv_rc(t, rows, x, out, out_dtype)], B.moe_latent_last_error()
+    assert rc(dtype=B.MOE_DT_F32)[0] == "MOE_ERR_DTYPE"
+    assert rc(dtype=B.MOE_DT_U32)[0] == "MOE_ERR_DTYPE"
+    assert rc(shape=(64, 256), strides=[1, 64])[0] == "MOE_ERR_LAYOUT"
+    assert rc(shape=(40, 256))[0] == "MOE_ERR_SHAPE"
+    assert rc(shape=(64, 200))[0] == "MOE_ERR_SHAPE"
+    assert rc(rows=0)[0] == "MOE_ERR_ROWS"
+    assert rc(rows=257)[0] == "MOE_ERR_ROWS"
+    assert rc(out_dtype=B.MOE_DT_F16)[0] == "MOE_ERR_DTYPE"
+    assert rc(x=0)[0] == "MOE_ERR_INVALID_ARG"
+    assert rc(x=FAKE + 2)[0] == "MOE_ERR_LAYOUT"
+    code, msg = rc(x=FAKE * 4 + 16)
+    assert code == "MOE_ERR_ALIAS", msg
+    code, msg = rc()
+    assert code == "MOE_ERR_DEVICE", msg      # a valid call reaches the device check
