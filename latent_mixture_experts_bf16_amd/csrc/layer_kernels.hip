@@ -4,12 +4,14 @@
 // chain of launches on one stream; stages that do not depend on each other share a launch,
 // and steps that need every item of a stage (schedule after the route, the adding of a
 // split tile's parts, combine after the experts of a block) are run by the last item to
-// finish. The one exception: in a one-row pass the route item (the first item of the first
-// launch) waits, bounded, for the logits the gate items hand it.
-//   one row:   [route, gate, fc1, shared up] -> [expert up, shared down A] ->
+// finish. The one exception: in a one-row pass the route item (the last gate item of the first
+// launch) waits, bounded, for the logits the gate items dispatched before it hand it.
+//   one row:   [gate, route, fc1, shared up] -> [expert up, shared down A] ->
 //              [expert down, shared down B] -> [combine + fc2 + shared + residual]
 //   more rows: [gate, fc1, shared up] -> [route; schedule, shared down A] ->
 //              [expert up, shared down B] -> [expert down; combine] -> [fc2 + ...]
+//   (passes of more rows run the shared expert on a second stream by default: see
+//   moe_latent_api.hip, plan_launches)
 // One workgroup of 4 waves runs one item; a launch's items are sized (about 32-64 KB of
 // weights each) so that all of them are resident at once (three per compute unit: the
 // expert launches' LDS holds a 32 KB block of codes, and the dense tiles' registers hold four
@@ -687,6 +689,25 @@ __device__ __forceinline__ void combine4(const LayerParams &p, int r, int d, flo
 
 enum Epi { EPI_FC1 = 0, EPI_SHUP = 1, EPI_SHDN = 2, EPI_FC2 = 3, EPI_LMH = 4 };
 
+// Weight steps of 128 inputs a wave of a dense tile keeps in flight (1, 2 or 4; build-time
+// knobs). Fewer steps keep the memory queues shorter, and with them the round trips of every
+// other item of the launch -- the gate's loads and the route's logit hand-off in the first
+// launch. Measured on the one-row Bolt-like forward (38.96 us with 4 everywhere): fc1 and
+// shared up at 1 and shared down at 2, 37.17 us; the lm_head at 2, 160 us at one row against
+// 171 (at 16 rows 211 against 224).
+#ifndef MOE_DEP_L0
+#define MOE_DEP_L0 1
+#endif
+#ifndef MOE_DEP_SHDN
+#define MOE_DEP_SHDN 2
+#endif
+#ifndef MOE_DEP_LMH
+#define MOE_DEP_LMH 2
+#endif
+constexpr int dense_depth(int epi) {
+    return epi == EPI_FC1 || epi == EPI_SHUP ? MOE_DEP_L0 : epi == EPI_SHDN ? MOE_DEP_SHDN : epi == EPI_LMH ? MOE_DEP_LMH : 4;
+}
+
 template <int NW>
 struct DenseLds {
     // per wave: one step's weights (16 rows x 128 inputs, rows 272 bytes apart) on their way
@@ -798,10 +819,13 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
     uint4 *wt = L.w[wave].wt;
 
     uint4 a[4][4];
+    // steps in flight per wave: fewer keep the memory queues, and with them every other item's
+    // round trips, shorter
+    constexpr int dep = dense_depth(EPI);
     auto load_w = [&](int i0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (i0 + q < nit) {
+            if (q < dep && i0 + q < nit) {
                 const uint16_t *wp = wrow + 128 * (i0 + q);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a[q][i] = ld_weight16(wp + (size_t)(4 * i) * K);
@@ -843,11 +867,11 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
         if (wave < nsplit) {
-            for (int i0 = 0; i0 < nit; i0 += 4) {
+            for (int i0 = 0; i0 < nit; i0 += dep) {
                 if (rt0 > 0 || i0 > 0) load_w(i0);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    if (i0 + q < nit) {
+                    if (q < dep && i0 + q < nit) {
                         const int kb = 128 * (i0 + q);
                         // the step's weights through the wave's buffer: written as loaded,
                         // read as fragments (MFMA j: row nr, inputs 32 j + 8 grp ..); LDS
@@ -1296,9 +1320,11 @@ template <int S, bool WIDE, class LdsT>
 __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
         // a one-row pass: item 0 routes the row with the logits the other gate items hand it
-        if (!p.single_row) gate_item<NW>(p, local, lds.gate);
-        else if (local == 0) route_item<WG_THREADS>(p, 0, lds.route);
-        else gate_item<NW>(p, local - 1, lds.gate);
+        // a one-row pass: the last item routes the row with the logits the gate items (all
+        // dispatched before it) hand it
+        const int ngate = p.item_base[ST_GATE + 1] - p.item_base[ST_GATE] - (p.single_row ? 1 : 0);
+        if (p.single_row && local == ngate) route_item<WG_THREADS>(p, 0, lds.route);
+        else gate_item<NW>(p, local, lds.gate);
     } else if constexpr (S == ST_FC1) {
         const int ks = p.ks_fc1;
         dense_item<EPI_FC1, NW>(p, p.fc1, p.x, p.H, local / ks, local % ks, ks, p.part_fc1, p.ctr + p.ctr_fc1,

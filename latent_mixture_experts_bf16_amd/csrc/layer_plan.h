@@ -10,10 +10,10 @@ namespace moe {
 // -> + shared -> + residual). A stage only reads what earlier launches wrote, or what a
 // "last arriver" of the same launch reads after every item it depends on has counted itself
 // done. One item waits: the route item of a one-row pass, for the logits of the gate items
-// dispatched after it (bounded; see ctr_hand).
+// dispatched before it (bounded; see ctr_hand).
 enum Stage : int {
     ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; a one-row pass
-                   // has one more item, first: the route item, which waits for the logits
+                   // has one more item, last: the route item, which waits for the logits
     ST_FC1,        // u = rnd(W1 . x), 16 outputs per item (MFMA)
     ST_SHUP,       // shared expert up + relu^2, 16 outputs per item
     ST_ROUTE,      // multi-row passes: one row per item; the last route item to finish builds
@@ -102,8 +102,8 @@ struct LayerParams {
     int single_row;        // rows == 1: the route item (first gate item) routes and writes the schedule
     int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)
     int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
-    // one-row pass: each gate item hands its logits to the route item (the first item of the
-    // launch) through 64-bit words [E] in the counter block at ctr_hand (bit 32: present),
+    // one-row pass: each gate item hands its logits to the route item (the last item of the
+    // gate stage) through 64-bit words [E] in the counter block at ctr_hand (bit 32: present),
     // which the route item polls for at most wait_ticks ticks of the 100 MHz real-time counter
     int ctr_hand;
     uint32_t wait_ticks;

@@ -488,7 +488,7 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
         out[n++] = Launch{f, l, k, split, pre, side, join};
     };
     if (variant == 2) {
-        add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item first
+        add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item last of the gate items
         if (p.SI) {
             add(ST_SHUP, ST_SHUP, K_SHUP, -1, 0, 1);
             add(ST_SHDN_A, ST_SHDN_A, K_SHDN_A, -1, 0, 1);
