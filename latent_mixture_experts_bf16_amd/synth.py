@@ -14,7 +14,9 @@ fp32 router, sigmoid top-8). Value distributions:
 * activations N(0, 1); gate, latent projections and shared expert N(0, 0.02);
   correction bias fp32 N(0, 0.01);
 * routed experts are 4-bit affine with groups of 64 along the input dimension:
-  codes uniform in 0..15, bf16 scale U(0.005, 0.02), bias = -8 * scale.
+  codes uniform in 0..15, bf16 scale U(0.005, 0.02), bias = -8 * scale; the other widths
+  of the affine family (2, 3, 5, 6, 8 bits; groups of 32 or 128) take codes uniform in
+  0 .. 2^b - 1, scale U(0.005, 0.02) * 8 / 2^(b-1) and bias = -2^(b-1) * scale.
 
 Draw order inside one layer (tensor-major, one generator per layer):
 x, Wg, c, W1, W2, up codes, up scales, down codes, down scales, Su, Sd.
@@ -50,6 +52,7 @@ class LayerDims:
     has_bias: bool = True
     norm_topk: bool = True
     routed_scaling: float = 2.5
+    quant_bits: int = 4    # routed expert code width: 2, 3, 4, 5, 6 or 8
 
     @property
     def expert_dim(self) -> int:
@@ -121,8 +124,9 @@ def make_layer(dims: LayerDims, rows: int, weight_seed: int,
       x [rows][H]; gate_w [E][H] (bf16, or fp32 when router_dtype == F32);
       corr_bias [E] fp32 (absent when has_bias is False);
       fc1_w [L][H], fc2_w [H][L] bf16 (absent when non-latent);
-      up_q [E][I][D/8] u32, up_scales/up_biases [E][I][D/64] bf16;
-      down_q [E][D][I/8] u32, down_scales/down_biases [E][D][I/64] bf16;
+      up_q [E][I][D b/32] u32, up_scales/up_biases [E][I][D/gs] bf16;
+      down_q [E][D][I b/32] u32, down_scales/down_biases [E][D][I/gs] bf16
+      (b = quant_bits, gs = group_size);
       shared_up [SI][H], shared_down [H][SI] bf16 (absent when SI == 0).
     """
     H, L, E, I, SI = dims.hidden, dims.latent, dims.n_experts, dims.expert_inter, dims.shared_inter
@@ -143,15 +147,19 @@ def make_layer(dims: LayerDims, rows: int, weight_seed: int,
     if L:
         out["fc1_w"] = _normal_bf16(rng, (L, H), 0.02)
         out["fc2_w"] = _normal_bf16(rng, (H, L), 0.02)
-    out["up_q"] = rng.integers(0, 2**32, size=(E, I, D // 8), dtype=np.uint32)
-    s = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(E, I, D // gs)).astype(np.float32))
+    # b-bit codes as a uniform bit string (every code uniform in 0 .. 2^b - 1); scales drawn
+    # as U(0.005, 0.02) * 8 / 2^(b-1), so that every width spans the weights of the 4-bit layer
+    nb = dims.quant_bits
+    half = 2 ** (nb - 1)
+    out["up_q"] = rng.integers(0, 2**32, size=(E, I, D * nb // 32), dtype=np.uint32)
+    s = f32_to_bf16_bits((rng.uniform(0.005, 0.02, size=(E, I, D // gs)) * (8.0 / half)).astype(np.float32))
     out["up_scales"] = s
-    out["down_q"] = rng.integers(0, 2**32, size=(E, D, I // 8), dtype=np.uint32)
-    s2 = f32_to_bf16_bits(rng.uniform(0.005, 0.02, size=(E, D, I // gs)).astype(np.float32))
+    out["down_q"] = rng.integers(0, 2**32, size=(E, D, I * nb // 32), dtype=np.uint32)
+    s2 = f32_to_bf16_bits((rng.uniform(0.005, 0.02, size=(E, D, I // gs)) * (8.0 / half)).astype(np.float32))
     out["down_scales"] = s2
-    # bias = -8 * scale: exact in bf16 (a power-of-two multiple, then a sign flip)
-    out["up_biases"] = f32_to_bf16_bits(-8.0 * bf16_bits_to_f32(s))
-    out["down_biases"] = f32_to_bf16_bits(-8.0 * bf16_bits_to_f32(s2))
+    # bias = -2^(b-1) * scale: exact in bf16 (a power-of-two multiple, then a sign flip)
+    out["up_biases"] = f32_to_bf16_bits(-float(half) * bf16_bits_to_f32(s))
+    out["down_biases"] = f32_to_bf16_bits(-float(half) * bf16_bits_to_f32(s2))
     if SI:
         out["shared_up"] = _normal_bf16(rng, (SI, H), 0.02)
         out["shared_down"] = _normal_bf16(rng, (H, SI), 0.02)

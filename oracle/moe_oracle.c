@@ -21,7 +21,9 @@
  *   O7  S = sum of s over picks in pick order; w_j = (s_j / S) * rho
  *   O8  u = rnd(W1 . x)                  fc1_latent_proj (u = x when non-latent)
  *   O9  h = rnd(U_e . u), a = rnd(relu(h)^2), y_j = rnd(D_e . a)
- *       with U_e[i][k] = q * scale + bias (4-bit affine, groups of 64 along k)
+ *       with U_e[i][k] = q * scale + bias (b-bit affine codes, b = 4 in the Bolt-like
+ *       layer and 2, 3, 5, 6 or 8 for the other widths of the affine family; groups of
+ *       group_size (64; 32 or 128) along k)
  *   O10 c = rnd(8-lane combine of fp32(w_j * y_j))
  *   O11 m = rnd(W2 . c)                  fc2_latent_proj (m = c when non-latent)
  *   O12 sh = rnd(Sd . rnd(relu(rnd(Su . x))^2)), or +0 without a shared expert
@@ -53,6 +55,7 @@ typedef struct {
     int32_t router_dtype; /* ORC_BF16 (bf16 weights, bf16 logits) or ORC_F32 */
     int32_t has_bias, norm_topk;
     float routed_scaling;
+    int32_t quant_bits;   /* code width of the routed experts: 2, 3, 4, 5, 6 or 8 (0: 4) */
 } orc_cfg;
 
 typedef struct {
@@ -291,14 +294,28 @@ float oracle_dequant(uint32_t q, uint16_t scale_bits, uint16_t bias_bits)
     return (float)q * sc + bi;
 }
 
-/* sum_k U[n][k] * x[k] for one row of a 4-bit expert matrix (codes `qrow` [K/8] words,
+/* Code k of a row of b-bit codes: bits [k b, (k + 1) b) of the row read as one little-endian
+ * bit string over its u32 words (bit j of the string is bit j % 32 of word j / 32), the
+ * lowest bit first. For b = 4 this is nibble k % 8 of word k / 8, the lowest nibble first;
+ * a code of 3, 5 or 6 bits may straddle two words. (The pages fix no packing; this is ours.) */
+uint32_t oracle_code(const uint32_t *qrow, int k, int bits)
+{
+    uint32_t q = 0;
+    for (int i = 0; i < bits; ++i) {
+        long j = (long)k * bits + i;
+        q |= ((qrow[j / 32] >> (j % 32)) & 1u) << i;
+    }
+    return q;
+}
+
+/* sum_k U[n][k] * x[k] for one row of a b-bit expert matrix (codes `qrow` [K b / 32] words,
  * scales and biases [K/gs]), left to right in fp32 from +0 */
-static float dot_q4_row(const uint32_t *qrow, const uint16_t *srow, const uint16_t *brow,
-                        const float *x, int K, int gs)
+static float dot_qb_row(const uint32_t *qrow, const uint16_t *srow, const uint16_t *brow,
+                        const float *x, int K, int gs, int bits)
 {
     float acc = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint32_t q = (qrow[k / 8] >> (4 * (k % 8))) & 0xFu;
+        uint32_t q = oracle_code(qrow, k, bits);
         float wq = oracle_dequant(q, srow[k / gs], brow[k / gs]);
         acc = acc + wq * x[k];
     }
@@ -311,13 +328,22 @@ void oracle_dense(const uint16_t *W, const float *x, int N, int K, float *out)
     for (int n = 0; n < N; ++n) out[n] = dot_bf16_row(W + (size_t)n * K, x, K);
 }
 
-/* fp32 value of U . x for every output n of a 4-bit matrix (exposed for tests) */
+/* fp32 value of U . x for every output n of a b-bit matrix (exposed for tests); rows of
+ * K b / 32 code words */
+void oracle_qb_matvec(const uint32_t *Q, const uint16_t *S, const uint16_t *B,
+                      const float *x, int N, int K, int gs, int bits, float *out)
+{
+    size_t rw = (size_t)K * bits / 32;
+    for (int n = 0; n < N; ++n)
+        out[n] = dot_qb_row(Q + (size_t)n * rw, S + (size_t)n * (K / gs),
+                            B + (size_t)n * (K / gs), x, K, gs, bits);
+}
+
+/* the same for 4-bit codes */
 void oracle_q4_matvec(const uint32_t *Q, const uint16_t *S, const uint16_t *B,
                       const float *x, int N, int K, int gs, float *out)
 {
-    for (int n = 0; n < N; ++n)
-        out[n] = dot_q4_row(Q + (size_t)n * (K / 8), S + (size_t)n * (K / gs),
-                            B + (size_t)n * (K / gs), x, K, gs);
+    oracle_qb_matvec(Q, S, B, x, N, K, gs, 4, out);
 }
 
 static float relu_sq(const orc_cfg *cfg, float h)
@@ -366,7 +392,7 @@ int oracle_stage(const orc_cfg *cfg, const orc_weights *W, int stage, int e, con
                  const float *in2, const float *in3, float *out, float *pre)
 {
     int H = cfg->hidden, L = cfg->latent, I = cfg->expert_inter, SI = cfg->shared_inter;
-    int gs = cfg->group_size, D = L ? L : H;
+    int gs = cfg->group_size, D = L ? L : H, nb = cfg->quant_bits ? cfg->quant_bits : 4;
     int n = 0;
     float *tmp = NULL;
     switch (stage) {
@@ -380,15 +406,15 @@ int oracle_stage(const orc_cfg *cfg, const orc_weights *W, int stage, int e, con
     case ORC_ST_EXPERT_ACT:
         n = I;
         tmp = malloc(sizeof(float) * n);
-        oracle_q4_matvec(W->up_q + (size_t)e * I * (D / 8), W->up_s + (size_t)e * I * (D / gs),
-                         W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, tmp);
+        oracle_qb_matvec(W->up_q + (size_t)e * I * ((size_t)D * nb / 32), W->up_s + (size_t)e * I * (D / gs),
+                         W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, nb, tmp);
         for (int i = 0; i < n; ++i) out[i] = relu_sq(cfg, rnd(cfg, tmp[i]));
         break;
     case ORC_ST_EXPERT_OUT:
         n = D;
         tmp = malloc(sizeof(float) * n);
-        oracle_q4_matvec(W->dn_q + (size_t)e * D * (I / 8), W->dn_s + (size_t)e * D * (I / gs),
-                         W->dn_b + (size_t)e * D * (I / gs), in, D, I, gs, tmp);
+        oracle_qb_matvec(W->dn_q + (size_t)e * D * ((size_t)I * nb / 32), W->dn_s + (size_t)e * D * (I / gs),
+                         W->dn_b + (size_t)e * D * (I / gs), in, D, I, gs, nb, tmp);
         for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);
         break;
     case ORC_ST_SHARED_ACT:
@@ -437,8 +463,9 @@ int oracle_forward_row(const orc_cfg *cfg, const orc_weights *W, const uint16_t 
 {
     int H = cfg->hidden, L = cfg->latent, E = cfg->n_experts, K = cfg->top_k;
     int I = cfg->expert_inter, SI = cfg->shared_inter, gs = cfg->group_size;
-    int D = L ? L : H;
+    int D = L ? L : H, nb = cfg->quant_bits ? cfg->quant_bits : 4;
     if (H <= 0 || H % 512 || D % gs || I % gs || gs % 8 || K > 64) return -1;
+    if (nb < 2 || nb > 8 || nb == 7 || (D * nb) % 32 || (I * nb) % 32) return -1;
     int rc = -2;
     float *x = malloc(sizeof(float) * H), *z = malloc(sizeof(float) * E);
     float *u = malloc(sizeof(float) * D);

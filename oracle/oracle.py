@@ -34,7 +34,7 @@ class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "latent", "n_experts", "n_group", "topk_group", "top_k",
         "expert_inter", "shared_inter", "group_size", "act_dtype", "router_dtype",
-        "has_bias", "norm_topk")] + [("routed_scaling", ctypes.c_float)]
+        "has_bias", "norm_topk")] + [("routed_scaling", ctypes.c_float), ("quant_bits", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -87,6 +87,10 @@ def lib():
         f.oracle_dense.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P]
         f.oracle_q4_matvec.restype = None
         f.oracle_q4_matvec.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
+        f.oracle_qb_matvec.restype = None
+        f.oracle_qb_matvec.argtypes = [_P, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P]
+        f.oracle_code.restype = ctypes.c_uint32
+        f.oracle_code.argtypes = [_P, ctypes.c_int, ctypes.c_int]
         f.oracle_combine.restype = None
         f.oracle_combine.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P]
         f.oracle_forward_row.restype = ctypes.c_int
@@ -112,7 +116,7 @@ def make_cfg(dims) -> _Cfg:
     return _Cfg(dims.hidden, dims.latent, dims.n_experts, dims.n_group, dims.topk_group,
                 dims.top_k, dims.expert_inter, dims.shared_inter, dims.group_size,
                 dims.act_dtype, dims.router_dtype, int(dims.has_bias), int(dims.norm_topk),
-                float(dims.routed_scaling))
+                float(dims.routed_scaling), int(getattr(dims, "quant_bits", 4)))
 
 
 def _c(a, dt):
@@ -264,6 +268,24 @@ def q4_matvec(Q, S, B, x, group_size=64) -> np.ndarray:
     out = np.zeros(N, np.float32)
     lib().oracle_q4_matvec(_ptr(Q), _ptr(S), _ptr(B), _ptr(x), N, K, group_size, _ptr(out))
     return out
+
+
+def qb_matvec(Q, S, B, x, bits, group_size=64) -> np.ndarray:
+    """fp32 U . x for one b-bit affine matrix: Q [N][K b / 32] u32, S, B [N][K/gs] bf16."""
+    Q = np.ascontiguousarray(Q, np.uint32)
+    S = np.ascontiguousarray(S, np.uint16)
+    B = np.ascontiguousarray(B, np.uint16)
+    x = np.ascontiguousarray(x, np.float32)
+    N, K = Q.shape[0], x.shape[0]
+    assert Q.shape[1] * 32 == K * bits
+    out = np.zeros(N, np.float32)
+    lib().oracle_qb_matvec(_ptr(Q), _ptr(S), _ptr(B), _ptr(x), N, K, group_size, bits, _ptr(out))
+    return out
+
+
+def code(qrow, k: int, bits: int) -> int:
+    qrow = np.ascontiguousarray(qrow, np.uint32)
+    return int(lib().oracle_code(_ptr(qrow), k, bits))
 
 
 def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:

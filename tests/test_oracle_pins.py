@@ -571,3 +571,79 @@ def test_final_add_order_constructed_cases():
         out, _ = O.stage(dims, arrays, "final", x, in2=m, in3=sh)
         assert out[5] == np.float32(case["expect"]), case["why"]
         assert (out[np.arange(H) != 5] == 0).all()
+
+
+# ------------------------------------------------------------------ other affine widths (2, 3, 5, 6, 8 bits)
+
+WIDTHS = (2, 3, 5, 6, 8)
+
+
+def _pack_bits(codes, bits):
+    """Codes [N][K] -> u32 words [N][K bits / 32]: one little-endian bit string per row, code k
+    at bits [k bits, (k + 1) bits), built with Python integers (independent of the oracle)."""
+    N, K = codes.shape
+    out = np.zeros((N, K * bits // 32), np.uint32)
+    for n in range(N):
+        v = 0
+        for k in range(K):
+            v |= int(codes[n, k]) << (k * bits)
+        for w in range(out.shape[1]):
+            out[n, w] = (v >> (32 * w)) & 0xFFFFFFFF
+    return out
+
+
+@pytest.mark.parametrize("bits", WIDTHS)
+def test_dequant_closed_form_every_width(bits):
+    """w = q*scale + bias with bias = -2^(b-1)*scale equals (q - 2^(b-1))*scale exactly, for
+    every b-bit code and every 13th positive bf16 scale with 2^b*scale finite (q*scale has at
+    most b + 8 significant bits, the exact sum at most b + 8)."""
+    half = 2 ** (bits - 1)
+    scales = np.arange(1, 0x7F80, 13, dtype=np.uint32).astype(np.uint16)
+    sval = O.bf16_to_f32(scales).astype(np.float64)
+    ok = sval * 2 ** bits <= np.finfo(np.float32).max
+    scales, sval = scales[ok], sval[ok]
+    bias = O.f32_to_bf16((-half * sval).astype(np.float32))
+    assert np.array_equal(O.bf16_to_f32(bias).astype(np.float64), -half * sval)
+    L = O.lib()
+    for q in range(2 ** bits):
+        exact = ((q - half) * sval).astype(np.float32)
+        for i in range(0, len(scales), 37):
+            assert L.oracle_dequant(q, int(scales[i]), int(bias[i])) == exact[i], (bits, q)
+
+
+@pytest.mark.parametrize("bits", WIDTHS + (4,))
+def test_code_layout_every_width(bits):
+    """Code k of a row is bits [k b, (k + 1) b) of the row's little-endian bit string (codes of
+    3, 5 and 6 bits straddle words): every code of random rows read back, and a one-hot input
+    through the matrix product returns exactly the dequantised weight at k."""
+    rng = np.random.default_rng(40 + bits)
+    K = 256
+    codes = rng.integers(0, 2 ** bits, size=(3, K))
+    words = _pack_bits(codes, bits)
+    for n in range(3):
+        assert [O.code(words[n], k, bits) for k in range(K)] == codes[n].tolist()
+    half = 2 ** (bits - 1)
+    s = O.f32_to_bf16(rng.uniform(0.005, 0.02, size=(3, K // 64)).astype(np.float32))
+    b = O.f32_to_bf16(-half * O.bf16_to_f32(s))
+    for k in (0, 1, 10, 31, 32, 33, 100, 255):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        got = O.qb_matvec(words, s, b, x, bits)
+        want = ((codes[:, k] - half) * O.bf16_to_f32(s[:, k // 64]).astype(np.float64)).astype(np.float32)
+        assert np.array_equal(got, want), (bits, k)
+
+
+@pytest.mark.parametrize("bits,gs", [(2, 64), (3, 32), (5, 128), (6, 64), (8, 32), (4, 128)])
+def test_qb_matvec_exact_on_integer_data(bits, gs):
+    """Integer codes and inputs with scale 1/4 and bias -2^(b-1)/4 give partial sums that are
+    all exact in fp32: the oracle must return the integer matrix product exactly, group
+    boundaries of any size included."""
+    rng = np.random.default_rng(bits * 100 + gs)
+    N, K = 24, 512
+    half = 2 ** (bits - 1)
+    codes = rng.integers(0, 2 ** bits, size=(N, K))
+    xi = rng.integers(-16, 16, size=K)
+    S = np.full((N, K // gs), synth.f32_to_bf16_bits(np.float32([0.25]))[0], np.uint16)
+    B = np.full((N, K // gs), synth.f32_to_bf16_bits(np.float32([-0.25 * half]))[0], np.uint16)
+    want = (((codes - half) @ xi) * 0.25).astype(np.float32)
+    assert np.array_equal(O.qb_matvec(_pack_bits(codes, bits), S, B, xi.astype(np.float32), bits, gs), want)

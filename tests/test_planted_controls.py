@@ -41,8 +41,8 @@ CONTROLS = [
      [("oracle_dense(W->fc2_w, in, H, L, tmp);", "oracle_dense(W->fc1_w, in, H, L, tmp);")],
      "test_latent_projections_and_expert_input_are_textbook"),
     ("routed_relu2_dropped",
-     [("W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, tmp);\n        for (int i = 0; i < n; ++i) out[i] = relu_sq(cfg, rnd(cfg, tmp[i]));",
-       "W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, tmp);\n        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);")],
+     [("W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, nb, tmp);\n        for (int i = 0; i < n; ++i) out[i] = relu_sq(cfg, rnd(cfg, tmp[i]));",
+       "W->up_b + (size_t)e * I * (D / gs), in, I, D, gs, nb, tmp);\n        for (int i = 0; i < n; ++i) out[i] = rnd(cfg, tmp[i]);")],
      "test_single_expert_identity_latent_is_textbook_mlp"),
     ("residual_added_before_the_shared_output",
      [("tmp[i] = in[i] + rnd(cfg, in2[i] + (in3 ? in3[i] : 0.0f));",
@@ -79,10 +79,12 @@ CONTROLS = [
     ("dequant_offset_by_one_code",
      [("return (float)q * sc + bi;", "return (float)(q + 1u) * sc + bi;")],
      "test_dequant_closed_form_every_code_and_scale"),
-    ("nibbles_high_first",
-     [("uint32_t q = (qrow[k / 8] >> (4 * (k % 8))) & 0xFu;",
-       "uint32_t q = (qrow[k / 8] >> (4 * (7 - k % 8))) & 0xFu;")],
+    ("code_bits_high_first",
+     [("q |= ((qrow[j / 32] >> (j % 32)) & 1u) << i;", "q |= ((qrow[j / 32] >> (j % 32)) & 1u) << (bits - 1 - i);")],
      "test_nibble_layout_low_nibble_first"),
+    ("codes_on_a_four_bit_stride",
+     [("long j = (long)k * bits + i;", "long j = (long)k * 4 + i;")],
+     "test_code_layout_every_width"),
 ]
 
 
