@@ -67,10 +67,17 @@ typedef struct {
 
 /* Layer configuration. Sizes the kernels take: hidden % 512 == 0; latent == 0 or
  * latent % 128 == 0; expert_inter % 64 == 0; shared_inter == 0 or % 128 == 0; expert input
- * and inter widths <= 6144; group_size == 64; n_experts <= 1024; n_group <= 256; top_k <= 16;
+ * and inter widths <= 6144; n_experts <= 1024; n_group <= 256; top_k <= 16;
  * 1 <= max_rows <= 256. latent == 0 selects the non-latent layer; shared_inter == 0 drops
  * the shared expert. A shared expert needs a latent layer (MOE_ERR_SHAPE otherwise): its
- * output is added in the fc2 epilogue. */
+ * output is added in the fc2 epilogue.
+ * Routed expert format: quant_bits-bit affine codes in groups of group_size inputs (the
+ * affine family whose decode speed the mlx-bun program measures, §7.4 experiment axes:
+ * 2..8 bits, groups of 32, 64 or 128). quant_bits 4 with group_size 64 is the layer's own
+ * format (the fused 4-bit expert path, fp16 activations allowed); any other pair of
+ * quant_bits in {2, 3, 4, 5, 6, 8} and group_size in {32, 64, 128} runs the width-generic
+ * expert kernels, which need bf16 activations and expert input and inter widths that are
+ * multiples of 128 (MOE_ERR_SHAPE / MOE_ERR_DTYPE otherwise). quant_bits 0 reads as 4. */
 typedef struct {
     int32_t hidden;         /* H */
     int32_t latent;         /* L, or 0 (non-latent) */
@@ -88,6 +95,7 @@ typedef struct {
     int32_t norm_topk;      /* 1: weights = scores / (sum over picks), then * routed_scaling */
     int32_t max_rows;       /* largest rows a forward may pass; sizes the workspace */
     float routed_scaling;   /* rho */
+    int32_t quant_bits;     /* routed expert code width: 2, 3, 4, 5, 6 or 8 (0: 4) */
 } moe_latent_config;
 
 /* The layer's weights (borrowed: the caller keeps every buffer alive until destroy; every
@@ -96,13 +104,16 @@ typedef struct {
  *   corr_bias   [E]        fp32 (only read when has_bias)
  *   fc1_w       [L][H]     bf16 (latent layers only)
  *   fc2_w       [H][L]     bf16 (latent layers only)
- *   up_q        [E][I][D/8]   u32: 8 codes per word, code of input k in word k/8 at bits
- *                             4*(k%8) (lowest nibble = lowest k); D = L, or H if non-latent
- *   up_scales   [E][I][D/64]  bf16 scale per group of 64 inputs
- *   up_biases   [E][I][D/64]  bf16 bias per group: weight = code * scale + bias
- *   down_q      [E][D][I/8]   u32, same packing
- *   down_scales [E][D][I/64]  bf16
- *   down_biases [E][D][I/64]  bf16
+ *   up_q        [E][I][D b/32]  u32 (b = quant_bits): each output row's codes as one
+ *                             little-endian bit string, the code of input k in bits
+ *                             [k b, k b + b) (4 bits: 8 codes per word, code of input k in word
+ *                             k/8 at bits 4*(k%8), lowest nibble = lowest k); D = L, or H if
+ *                             non-latent
+ *   up_scales   [E][I][D/gs]  bf16 scale per group of gs = group_size inputs
+ *   up_biases   [E][I][D/gs]  bf16 bias per group: weight = code * scale + bias
+ *   down_q      [E][D][I b/32]  u32, same packing
+ *   down_scales [E][D][I/gs]  bf16
+ *   down_biases [E][D][I/gs]  bf16
  *   shared_up   [SI][H]   bf16 (shared_inter > 0 only)
  *   shared_down [H][SI]   bf16 (shared_inter > 0 only) */
 typedef struct {

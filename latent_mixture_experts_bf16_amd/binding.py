@@ -43,7 +43,7 @@ class moe_latent_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "latent", "n_experts", "n_group", "topk_group", "top_k", "expert_inter",
         "shared_inter", "group_size", "act_dtype", "router_dtype", "activation", "has_bias",
-        "norm_topk", "max_rows")] + [("routed_scaling", ctypes.c_float)]
+        "norm_topk", "max_rows")] + [("routed_scaling", ctypes.c_float), ("quant_bits", ctypes.c_int32)]
 
 
 WEIGHT_FIELDS = ("gate_w", "corr_bias", "fc1_w", "fc2_w", "up_q", "up_scales", "up_biases",

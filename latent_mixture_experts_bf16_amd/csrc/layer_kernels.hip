@@ -1274,6 +1274,151 @@ __device__ __forceinline__ int expert_item(const LayerParams &p, int slot, int b
     return U;
 }
 
+// ------------------------------------------------------------------ routed experts, other widths
+
+// Code k (0..31) of a 32-input chunk whose BITS * 32 bits sit in the words w[0..BITS) as one
+// little-endian bit string (k and BITS known at compile time, so w stays in registers).
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk_code(const uint32_t *w, int k) {
+    const int o = k * BITS, wi = o >> 5, sh = o & 31;
+    const uint32_t mask = (1u << BITS) - 1u;
+    if (sh + BITS <= 32) return (w[wi] >> sh) & mask;
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], (uint32_t)sh) & mask;
+}
+
+// Codes k and k + 4 of a chunk as a packed pair of bf16 values: 128 + q for widths up to 7
+// bits (q under the exponent of 128, exact), q itself for 8 bits (an integer below 256 is a
+// bf16 value: its fp32 image has 16 trailing zero bits).
+template <int BITS>
+__device__ __forceinline__ uint32_t chunk_pair(const uint32_t *w, int k) {
+    const uint32_t a = chunk_code<BITS>(w, k), b = chunk_code<BITS>(w, k + 4);
+    if constexpr (BITS <= 7) {
+        return a | (b << 16) | 0x43004300u;
+    } else {
+        return __builtin_amdgcn_perm(__float_as_uint((float)b), __float_as_uint((float)a), 0x07060302u);
+    }
+}
+
+// Item: outputs [blk*NB, +NB) of the up (UP) or down projection of slot `slot`, for every
+// pair of that slot, with BITS-bit affine codes in groups of p.gs along the input (the
+// affine family of the mlx-bun decode-speed program, §7.4 experiment axes: 2..8-bit, groups
+// of 32/64/128). As expert_item, but the block's codes sit in LDS row by row (a 32-input
+// chunk is BITS words), one pair per pass, bf16 activations; per chunk the lane adds
+// scale * sum(q' x) + (bias - OFF scale) * sum(x) with q' = q + OFF (OFF = 128 for widths up
+// to 7 bits, 0 for 8).
+template <int BITS, bool UP, int XMAX>
+__device__ __forceinline__ int qexpert_item(const LayerParams &p, int slot, int blk, ExpertLds<XMAX> &L) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int U = p.sched[SCH_U];
+    const int4 rec = *(const int4 *)(p.sched + SCH_REC + SCH_RECW * slot);
+    const int e = rec.x, off = rec.y, R = rec.z;
+    int pr = rec.w;
+    const int NP = p.rows * p.K;
+    if (e == -1) return U;
+    if (e < 0 || e >= p.E || off < 0 || R < 1 || off + R > NP || pr < 0 || pr >= NP) {   // never for a valid schedule
+        if (threadIdx.x == 0) atomicOr(p.err, 4u);
+        return 0;
+    }
+    const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
+    const int NB = UP ? p.up_nb : p.dn_nb;
+    const int n0 = blk * NB;
+    const int C = Kin >> 5, G = Kin >> p.gs_log2, RW = (Kin >> 5) * BITS;   // words per row
+    const uint32_t *Q = (UP ? p.up_q : p.dn_q) + ((size_t)e * N + n0) * RW;
+    const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G;
+    const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G;
+    const uint16_t *xin = UP ? (p.L ? p.u : p.x) : p.eact;
+    auto xrow = [&](int q) { return xin + (UP ? (size_t)(q / p.K) * Kin : (size_t)q * Kin); };
+    constexpr int XCH = 4;
+    constexpr float OFF = BITS <= 7 ? 128.0f : 0.0f;
+    int P = 2;
+    while (P * XCH < C && P < 64) P <<= 1;
+    const int nch = (C + P - 1) / P;
+    const int gpw = 64 / P, t = lane % P, grp = lane / P;
+    const int NG = (WG_THREADS / 64) * gpw;
+    int RG = NB / NG;
+    if (RG < 1) RG = 1;
+    const int g = wave * gpw + grp;
+    const int xu = Kin >> 3;
+    auto put = [&](int q, int n, float acc) {
+        if (UP) p.eact[(size_t)q * p.I + n] = f2bf(relu_sq(0, rnd(0, acc)));
+        else if (p.inline_comb) p.eout[(size_t)q * p.D + n] = f2bf(acc);
+        else st_shared16(p.eout + (size_t)q * p.D + n, f2bf(acc));
+    };
+    stage_lds<AUX_NT>((const uint4 *)S, (uint4 *)L.s, NB * G / 8);
+    stage_lds<AUX_NT>((const uint4 *)B, (uint4 *)L.b, NB * G / 8);
+    stage_lds((const uint4 *)xrow(pr), L.x, xu);
+    stage_lds<AUX_NT>((const uint4 *)Q, L.q, NB * RW / 4);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const uint32_t *LQ = (const uint32_t *)L.q;
+    for (int r = 0; r < R; ++r) {
+        if (r > 0) {
+            const int q = p.sched[SCH_PAIRS + off + r];
+            pr = q < 0 || q >= NP ? NP - 1 : q;
+            __syncthreads();
+            stage_lds((const uint4 *)xrow(pr), L.x, xu);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        uint32_t xq[XCH][16];
+        float xs[XCH];
+#pragma unroll
+        for (int m = 0; m < XCH; ++m) {
+            const int c = t + P * m;
+            xs[m] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) xq[m][k] = 0u;
+            if (m < nch && c < C) xs[m] = x_chunk<false>(L.x, c, xq[m]);
+        }
+        for (int rb = 0; rb < RG; rb += 2) {
+            float v[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < XCH; ++m) {
+                const int c = t + P * m;
+                if (m < nch && c < C) {
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        int nl = g * RG + rb + ii;
+                        nl = nl < NB ? nl : NB - 1;
+                        uint32_t w[BITS];
+                        const uint32_t *src = LQ + nl * RW + c * BITS;   // 16-byte aligned for 4 and 8 bits,
+                        if constexpr (BITS % 4 == 0) {                   // 8-byte for 2 and 6
+#pragma unroll
+                            for (int i = 0; i < BITS; i += 4) {
+                                const uint4 v4 = lds_ld16(src + i);
+                                w[i] = v4.x; w[i + 1] = v4.y; w[i + 2] = v4.z; w[i + 3] = v4.w;
+                            }
+                        } else if constexpr (BITS % 2 == 0) {
+#pragma unroll
+                            for (int i = 0; i < BITS; i += 2) {
+                                const uint2 v2 = *(const uint2 *)(src + i);
+                                w[i] = v2.x; w[i + 1] = v2.y;
+                            }
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < BITS; ++i) w[i] = src[i];
+                        }
+                        const int gi = nl * G + ((c << 5) >> p.gs_log2);
+                        const float sc = bf2f(L.s[gi]), bi = bf2f(L.b[gi]);
+                        float a = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) a = dot2<false>(chunk_pair<BITS>(w, 8 * j + i), xq[m][4 * j + i], a);
+                        }
+                        v[ii] = __builtin_fmaf(sc, a, v[ii]);
+                        v[ii] = __builtin_fmaf(__builtin_fmaf(-OFF, sc, bi), xs[m], v[ii]);
+                    }
+                }
+            }
+            const int rr = reduce_rows<2>(v, P, t);
+            const int nl = g * RG + rb + rr;
+            if ((t & (P / 2 - 1)) == 0 && nl < NB && rb + rr < RG) put(pr, n0 + nl, v[0]);
+        }
+    }
+    return U;
+}
+
 // ------------------------------------------------------------------ combine
 
 // Combine of latent outputs [n0, n0 + nb) for every row of the pass (the last down item of
@@ -1406,6 +1551,37 @@ template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, in
 template __global__ void moe_stage_kernel<ST_SHUP, ST_SHUP, false>(LayerParams, int, int, int, int);
 template __global__ void moe_stage_kernel<ST_SHDN_A, ST_SHDN_A, false>(LayerParams, int, int, int, int);
 template __global__ void moe_stage_kernel<ST_SHDN_B, ST_SHDN_B, false>(LayerParams, int, int, int, int);
+
+// The routed expert items of one stage (up or down) with BITS-bit codes: items [lo, hi) of the
+// table, one per workgroup; the last down item of each output block of a multi-row pass
+// combines that block.
+template <int BITS, bool UP, bool WIDE>
+__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(3, 8)))
+moe_qexpert_kernel(LayerParams p, int lo, int hi) {
+    __shared__ ExpertLds<XMAX_OF(WIDE)> lds;
+    __shared__ int s_flag;
+    const int it = lo + (int)blockIdx.x;
+    if (it >= hi) return;
+    const int local = it - p.item_base[UP ? ST_UP : ST_DOWN];
+    const int blocks = UP ? p.up_blocks : p.dn_blocks;
+    const int slot = local / blocks, blk = local % blocks;
+    const int U = qexpert_item<BITS, UP, XMAX_OF(WIDE)>(p, slot, blk, lds);
+    if (!UP && slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, &s_flag))
+        combine_block(p, blk * p.dn_nb, p.dn_nb);
+}
+
+#define MOE_QEXPERT(B)                                                              \
+    template __global__ void moe_qexpert_kernel<B, true, false>(LayerParams, int, int);  \
+    template __global__ void moe_qexpert_kernel<B, false, false>(LayerParams, int, int); \
+    template __global__ void moe_qexpert_kernel<B, true, true>(LayerParams, int, int);   \
+    template __global__ void moe_qexpert_kernel<B, false, true>(LayerParams, int, int);
+MOE_QEXPERT(2)
+MOE_QEXPERT(3)
+MOE_QEXPERT(4)
+MOE_QEXPERT(5)
+MOE_QEXPERT(6)
+MOE_QEXPERT(8)
+#undef MOE_QEXPERT
 
 // Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
 // grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);

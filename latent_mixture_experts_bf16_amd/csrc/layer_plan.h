@@ -98,6 +98,9 @@ struct LayerParams {
     int item_base[NSTAGE + 1];
     int umax;              // slots enumerated by ST_UP / ST_DOWN items
     int up_nb, dn_nb;      // output rows of one routed up / down item
+    int qbits;             // routed expert code width (2, 3, 4, 5, 6, 8)
+    int gs_log2;           // log2 of the quantization group (32, 64, 128 inputs)
+    int generic;           // not 4-bit codes in groups of 64: the width-generic expert kernels
     int up_blocks, dn_blocks;
     int single_row;        // rows == 1: the route item (first gate item) routes and writes the schedule
     int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)

@@ -22,6 +22,7 @@
 
 namespace moe {
 template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre);
+template <int BITS, bool UP, bool WIDE> __global__ void moe_qexpert_kernel(LayerParams p, int lo, int hi);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 __global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint16_t *X, int K, int lo);
@@ -118,16 +119,21 @@ static const char *dt_name(int dt) {
     }
 }
 
-// Output rows of one expert item: the largest power of two <= 64 whose codes, scales and
-// biases fit the item's LDS, that divides N, and whose scales fill whole 16-byte units.
-static int expert_block(int N, int Kin) {
+// Output rows of one expert item: the largest power of two <= 64 that divides N, whose
+// codes, scales and biases fit the item's LDS, and whose codes and scales fill whole 16-byte
+// units. bits: code width; gs: inputs per scale.
+static int expert_block(int N, int Kin, int bits = 4, int gs = 64) {
     for (int nb = EXPERT_MAX_BLOCK; nb > 1; nb >>= 1) {
-        if (N % nb == 0 && (size_t)nb * Kin / 2 <= EXPERT_LDS_CODES &&
-            (size_t)nb * (Kin / 64) * 2 <= EXPERT_LDS_SCALES && ((size_t)nb * Kin) % 512 == 0)
+        const size_t code_bytes = (size_t)nb * Kin * bits / 8, groups = (size_t)nb * (Kin / gs);
+        if (N % nb == 0 && code_bytes <= EXPERT_LDS_CODES && groups * 2 <= EXPERT_LDS_SCALES &&
+            code_bytes % 256 == 0 && groups % 8 == 0)
             return nb;
     }
     return 1;
 }
+
+static int quant_bits_of(const moe_latent_config &c) { return c.quant_bits ? c.quant_bits : 4; }
+static bool generic_format(const moe_latent_config &c) { return quant_bits_of(c) != 4 || c.group_size != 64; }
 
 static int check_config(const moe_latent_config &c) {
     if (c.hidden <= 0 || c.n_experts <= 0 || c.n_group <= 0 || c.topk_group <= 0 || c.top_k <= 0 ||
@@ -150,7 +156,11 @@ static int check_config(const moe_latent_config &c) {
     if (c.topk_group * per < c.top_k)
         return fail(MOE_ERR_GROUPS, "config: %d kept groups of %d experts cannot hold top_k %d",
                     c.topk_group, per, c.top_k);
-    if (c.group_size != 64) return fail(MOE_ERR_SHAPE, "config: group_size %d (only 64)", c.group_size);
+    const int qb = quant_bits_of(c);
+    if (qb != 2 && qb != 3 && qb != 4 && qb != 5 && qb != 6 && qb != 8)
+        return fail(MOE_ERR_SHAPE, "config: quant_bits %d (2, 3, 4, 5, 6 or 8)", c.quant_bits);
+    if (c.group_size != 32 && c.group_size != 64 && c.group_size != 128)
+        return fail(MOE_ERR_SHAPE, "config: group_size %d (32, 64 or 128)", c.group_size);
     if (c.hidden % 512) return fail(MOE_ERR_SHAPE, "config: hidden %d not a multiple of 512", c.hidden);
     if (c.latent % 128) return fail(MOE_ERR_SHAPE, "config: latent %d not a multiple of 128", c.latent);
     if (c.shared_inter % 128)
@@ -159,9 +169,19 @@ static int check_config(const moe_latent_config &c) {
     if (c.expert_inter % 64 || c.expert_inter > 6144 || D > 6144)
         return fail(MOE_ERR_SHAPE, "config: expert dims (in %d, inter %d) must be multiples of 64, <= 6144",
                     D, c.expert_inter);
+    if (generic_format(c)) {
+        if (D % 128 || c.expert_inter % 128)
+            return fail(MOE_ERR_SHAPE, "config: %d-bit codes in groups of %d need expert dims (in %d, inter %d) "
+                        "that are multiples of 128", qb, c.group_size, D, c.expert_inter);
+        if (c.act_dtype != MOE_DT_BF16)
+            return fail(MOE_ERR_DTYPE, "config: %d-bit codes in groups of %d need bf16 activations", qb,
+                        c.group_size);
+    }
     {
-        const int nb_up = expert_block(c.expert_inter, D), nb_dn = expert_block(D, c.expert_inter);
-        if (((size_t)nb_up * D) % 512 || ((size_t)nb_dn * c.expert_inter) % 512)
+        const int nb_up = expert_block(c.expert_inter, D, qb, c.group_size);
+        const int nb_dn = expert_block(D, c.expert_inter, qb, c.group_size);
+        if (((size_t)nb_up * D * qb / 8) % 256 || ((size_t)nb_dn * c.expert_inter * qb / 8) % 256 ||
+            (nb_up * (D / c.group_size)) % 8 || (nb_dn * (c.expert_inter / c.group_size)) % 8)
             return fail(MOE_ERR_SHAPE, "config: no expert block fits the item LDS for in %d, inter %d", D,
                         c.expert_inter);
     }
@@ -230,21 +250,22 @@ static int check_weights(const moe_latent_config &c, const moe_latent_weights &w
         if ((rc = check_tensor("fc1_latent_proj", w.fc1_w, MOE_DT_BF16, 2, s1))) return rc;
         if ((rc = check_tensor("fc2_latent_proj", w.fc2_w, MOE_DT_BF16, 2, s2))) return rc;
         // experts must live in the latent: refuse expert tensors laid out over hidden
-        if (w.up_q.data && w.up_q.ndim == 3 && w.up_q.shape[2] == H / 8 && H != L)
+        if (w.up_q.data && w.up_q.ndim == 3 && w.up_q.shape[2] == H * quant_bits_of(c) / 32 && H != L)
             return fail(MOE_ERR_EXPERTS_OVER_HIDDEN, "up_q: experts stored over hidden (%lld inputs), latent is %lld",
                         (long long)H, (long long)L);
         if (w.down_q.data && w.down_q.ndim == 3 && w.down_q.shape[1] == H && H != L)
             return fail(MOE_ERR_EXPERTS_OVER_HIDDEN, "down_q: experts stored over hidden (%lld outputs), latent is %lld",
                         (long long)H, (long long)L);
     }
+    const int64_t qb = quant_bits_of(c), gs = c.group_size;
     {
-        const int64_t q[3] = {E, I, D / 8}, g[3] = {E, I, D / 64};
+        const int64_t q[3] = {E, I, D * qb / 32}, g[3] = {E, I, D / gs};
         if ((rc = check_tensor("up_q", w.up_q, MOE_DT_U32, 3, q))) return rc;
         if ((rc = check_tensor("up_scales", w.up_scales, MOE_DT_BF16, 3, g))) return rc;
         if ((rc = check_tensor("up_biases", w.up_biases, MOE_DT_BF16, 3, g))) return rc;
     }
     {
-        const int64_t q[3] = {E, D, I / 8}, g[3] = {E, D, I / 64};
+        const int64_t q[3] = {E, D, I * qb / 32}, g[3] = {E, D, I / gs};
         if ((rc = check_tensor("down_q", w.down_q, MOE_DT_U32, 3, q))) return rc;
         if ((rc = check_tensor("down_scales", w.down_scales, MOE_DT_BF16, 3, g))) return rc;
         if ((rc = check_tensor("down_biases", w.down_biases, MOE_DT_BF16, 3, g))) return rc;
@@ -393,6 +414,9 @@ static void fill_params(const moe_latent_config &c, const moe_latent_weights &w,
     p.has_bias = c.has_bias != 0;
     p.norm_topk = c.norm_topk != 0;
     p.rho = c.routed_scaling;
+    p.qbits = quant_bits_of(c);
+    p.gs_log2 = __builtin_ctz((unsigned)c.group_size);
+    p.generic = generic_format(c) ? 1 : 0;
     p.gate_w16 = p.router_f32 ? nullptr : (const uint16_t *)w.gate_w.data;
     p.gate_w32 = p.router_f32 ? (const float *)w.gate_w.data : nullptr;
     p.bias = c.has_bias ? (const float *)w.corr_bias.data : nullptr;
@@ -466,7 +490,7 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 // split >= 0 the first `pre` items of stage `split` on are dispatched first (see
 // moe_stage_kernel). side: 0 on the caller's stream, 1 on the handle's side stream; join: the
 // launch first waits for the side stream's work of this forward.
-enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B };
+enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B, K_QUP, K_QDOWN };
 struct Launch {
     int first, last, kernel, split, pre, side, join;
 };
@@ -487,6 +511,22 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
     auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0) {
         out[n++] = Launch{f, l, k, split, pre, side, join};
     };
+    if (p.generic) {
+        // other code widths: the routed stages in launches of their own (the width-generic
+        // expert kernels), the shared expert on the side stream (variant 2) or in line
+        const int side = variant == 2 ? 1 : 0;
+        add(ST_GATE, ST_FC1, K_GATE_SHUP);
+        if (p.SI) {
+            add(ST_SHUP, ST_SHUP, K_SHUP, -1, 0, side);
+            add(ST_SHDN_A, ST_SHDN_A, K_SHDN_A, -1, 0, side);
+            add(ST_SHDN_B, ST_SHDN_B, K_SHDN_B, -1, 0, side);
+        }
+        if (!p.single_row) add(ST_ROUTE, ST_ROUTE, K_ROUTE_UP);
+        add(ST_UP, ST_UP, K_QUP);
+        add(ST_DOWN, ST_DOWN, K_QDOWN);
+        if (p.L) add(ST_FC2, ST_FC2, K_FC2, -1, 0, 0, p.SI && side ? 1 : 0);
+        return n;
+    }
     if (variant == 2) {
         add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item last of the gate items
         if (p.SI) {
@@ -536,10 +576,41 @@ static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st,
                            pre);
 }
 
+template <int BITS, bool UP, bool WIDE>
+static void launch_q(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const int lo = p.item_base[l.first], hi = p.item_base[l.last + 1];
+    if (hi <= lo) return;
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL((moe_qexpert_kernel<BITS, UP, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1,
+                              0, p, lo, hi);
+    else
+        hipLaunchKernelGGL((moe_qexpert_kernel<BITS, UP, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi);
+}
+
+template <bool UP, bool WIDE>
+static void launch_q_bits(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    switch (p.qbits) {
+        case 2: launch_q<2, UP, WIDE>(p, l, st, ev0, ev1); break;
+        case 3: launch_q<3, UP, WIDE>(p, l, st, ev0, ev1); break;
+        case 4: launch_q<4, UP, WIDE>(p, l, st, ev0, ev1); break;
+        case 5: launch_q<5, UP, WIDE>(p, l, st, ev0, ev1); break;
+        case 6: launch_q<6, UP, WIDE>(p, l, st, ev0, ev1); break;
+        default: launch_q<8, UP, WIDE>(p, l, st, ev0, ev1); break;   // 8: the widths are checked at create
+    }
+}
+
 static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr) {
     const bool wide = p.D > 2048 || p.I > 2048;
     switch (l.kernel) {
+        case K_QUP:
+            if (wide) launch_q_bits<true, true>(p, l, st, ev0, ev1);
+            else launch_q_bits<true, false>(p, l, st, ev0, ev1);
+            break;
+        case K_QDOWN:
+            if (wide) launch_q_bits<false, true>(p, l, st, ev0, ev1);
+            else launch_q_bits<false, false>(p, l, st, ev0, ev1);
+            break;
         case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st, ev0, ev1); break;
         case K_ROUTE_UP:
             if (wide) launch_kernel<ST_ROUTE, ST_UP, true>(p, l, st, ev0, ev1);
@@ -608,8 +679,8 @@ static void plan_items(LayerParams &p, int rows) {
     p.single_row = rows == 1;
     p.inline_comb = rows == 1 && p.L && p.L / p.ks_fc2 <= DENSE_XLDS;
     p.umax = p.E < rows * p.K ? p.E : rows * p.K;
-    p.up_nb = expert_block(p.I, p.D);
-    p.dn_nb = expert_block(p.D, p.I);
+    p.up_nb = expert_block(p.I, p.D, p.qbits, 1 << p.gs_log2);
+    p.dn_nb = expert_block(p.D, p.I, p.qbits, 1 << p.gs_log2);
     p.up_blocks = p.I / p.up_nb;
     p.dn_blocks = p.D / p.dn_nb;
     // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's

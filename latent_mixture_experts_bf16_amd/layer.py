@@ -34,6 +34,7 @@ def config_of(dims, max_rows: int) -> B.moe_latent_config:
     c.norm_topk = int(dims.norm_topk)
     c.max_rows = max_rows
     c.routed_scaling = dims.routed_scaling
+    c.quant_bits = dims.quant_bits
     return c
 
 

@@ -42,9 +42,10 @@ class _Cpu:
     def _shapes(d):
         H, L, E, I, SI = d.hidden, d.latent, d.n_experts, d.expert_inter, d.shared_inter
         D = L or H
-        s = {"gate_w": [E, H], "up_q": [E, I, D // 8], "up_scales": [E, I, D // 64],
-             "up_biases": [E, I, D // 64], "down_q": [E, D, I // 8], "down_scales": [E, D, I // 64],
-             "down_biases": [E, D, I // 64]}
+        b, gs = d.quant_bits, d.group_size
+        s = {"gate_w": [E, H], "up_q": [E, I, D * b // 32], "up_scales": [E, I, D // gs],
+             "up_biases": [E, I, D // gs], "down_q": [E, D, I * b // 32], "down_scales": [E, D, I // gs],
+             "down_biases": [E, D, I // gs]}
         if d.has_bias:
             s["corr_bias"] = [E]
         if L:
@@ -86,7 +87,11 @@ NONLAT = synth.WORKLOADS[3].layers[0]
     ({"n_group": 120, "topk_group": 1}, "MOE_ERR_GROUPS", "kept groups"),
     ({"hidden": 4000}, "MOE_ERR_SHAPE", "hidden"),
     ({"latent": 1000}, "MOE_ERR_SHAPE", "latent"),
-    ({"group_size": 32}, "MOE_ERR_SHAPE", "group_size"),
+    ({"group_size": 16}, "MOE_ERR_SHAPE", "group_size"),
+    ({"group_size": 256}, "MOE_ERR_SHAPE", "group_size"),
+    ({"quant_bits": 7}, "MOE_ERR_SHAPE", "quant_bits"),
+    ({"quant_bits": 1}, "MOE_ERR_SHAPE", "quant_bits"),
+    ({"quant_bits": 3, "expert_inter": 192}, "MOE_ERR_SHAPE", "multiples of 128"),
     ({"max_rows": 0}, "MOE_ERR_ROWS", "max_rows"),
     ({"max_rows": 257}, "MOE_ERR_ROWS", "max_rows"),
     ({"act_dtype": B.MOE_DT_F16}, "MOE_ERR_DTYPE", "f16"),
@@ -97,6 +102,30 @@ def test_config_refusals(over, code, word):
     rc, h, msg = _create(BOLT, cfg_over=over)
     assert rc == code and h is None
     assert word in msg
+
+
+def test_other_widths_refuse_f16_activations():
+    rc, h, msg = _create(NONLAT, cfg_over={"quant_bits": 3})
+    assert rc == "MOE_ERR_DTYPE" and h is None
+    assert "bf16 activations" in msg
+
+
+@pytest.mark.parametrize("bits,gs", [(2, 32), (3, 64), (5, 128), (8, 64), (4, 128)])
+def test_other_widths_check_code_and_group_shapes(bits, gs):
+    """A descriptor laid out for 4-bit codes in groups of 64 is refused by name for another
+    width or group size; the shapes of the width itself pass every check before the device."""
+    import dataclasses
+    dims = dataclasses.replace(BOLT, quant_bits=bits, group_size=gs)
+    if bits != 4:
+        rc, h, msg = _create(dims, up_q={"shape": [BOLT.n_experts, BOLT.expert_inter, BOLT.latent // 8]})
+        assert rc == "MOE_ERR_LAYOUT" and "up_q" in msg, msg
+    if gs != 64:
+        rc, h, msg = _create(dims, down_scales={"shape": [BOLT.n_experts, BOLT.latent, BOLT.expert_inter // 64]})
+        assert rc == "MOE_ERR_LAYOUT" and "down_scales" in msg, msg
+    rc, h, msg = _create(dims)
+    assert rc in ("MOE_ERR_DEVICE", "MOE_OK"), (rc, msg)
+    if h is not None:
+        B.moe_latent_destroy(h)
 
 
 def test_non_latent_shared_expert_refused():
