@@ -37,18 +37,18 @@ KERNEL_SOURCES = ["latent_mixture_experts_bf16_amd/csrc/layer_kernels.hip",
 COPY_MIB = 512   # size of the calibration copy (int32 negation: reads and writes COPY_MIB MiB)
 
 
-def kernel_of(first, last, wide):
+def kernel_of(first, last, wide, qb=0):
     """The kernel instance (as rocprofv3 names it: first and last stage of its template, wide
-    expert variant) that runs a launch of stages [first, last] (moe_latent_api.hip,
-    launch_one)."""
+    expert variant, expert code width or 0 for the fused 4-bit items) that runs a launch of
+    stages [first, last] (moe_latent_api.hip, launch_one)."""
     w = "true" if wide else "false"
     if last <= 2 and first == 0:
-        return "moe_stage_kernel<0, 2, false>"
+        return "moe_stage_kernel<0, 2, false, 0>"
     if first == last and first in (2, 4, 6, 8):
-        return f"moe_stage_kernel<{first}, {last}, false>"
+        return f"moe_stage_kernel<{first}, {last}, false, 0>"
     if 3 <= first and last <= 5:
-        return f"moe_stage_kernel<3, 5, {w}>"
-    return f"moe_stage_kernel<5, 7, {w}>"
+        return f"moe_stage_kernel<3, 5, {w}, {qb}>"
+    return f"moe_stage_kernel<5, 7, {w}, {qb}>"
 
 
 def plan_groups(B, handle, dims, rows):
@@ -56,6 +56,7 @@ def plan_groups(B, handle, dims, rows):
     keys), side stream, workgroups, kernel name."""
     D = dims.latent or dims.hidden
     wide = D > 2048 or dims.expert_inter > 2048
+    qb = 0 if (dims.quant_bits, dims.group_size) == (4, 64) else dims.quant_bits
     out = []
     for g in range(16):
         n, f, l, side = B.moe_latent_group_stages(handle, rows, g)
@@ -66,7 +67,7 @@ def plan_groups(B, handle, dims, rows):
             stages = stages + ["route"]           # the one-row route item rides in the gate launch
         name = "+".join(stages) + (" [side stream]" if side else "")
         out.append({"group": g, "name": name, "stages": stages, "side": side, "items": n,
-                    "kernel": kernel_of(f, l, wide)})
+                    "kernel": kernel_of(f, l, wide, qb)})
     return out
 
 
@@ -98,6 +99,9 @@ def parse():
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--no-rows-sweep", action="store_true",
                     help="skip the 16-row and 64-row passes reported beside the one-row line")
+    ap.add_argument("--formats", default="",
+                    help="also time the Bolt-like layer with routed experts in these affine formats, "
+                         "e.g. 2:64,3:64,4:64,4:128,5:64,6:64,8:64 (bits:group_size)")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip the lm_head gemv (K 4096, N 131072, 1 and 16 rows) reported beside it")
     return ap.parse_args()
@@ -196,7 +200,7 @@ def stage_bytes(dims, rows, n_distinct):
     H, L, E, I, SI, K = dims.hidden, dims.latent, dims.n_experts, dims.expert_inter, dims.shared_inter, dims.top_k
     D = L or H
     a = 2  # activation bytes
-    expert = D * I // 2 + (D * I // 64) * 4            # codes + bf16 scale and bias per 64
+    expert = D * I * dims.quant_bits // 8 + (D * I // dims.group_size) * 4   # codes + bf16 scale, bias per group
     half = (H // 16 // 2) * 16
     return {
         "gate": E * H * (4 if dims.router_dtype == 3 else 2) + rows * H * a + rows * E * 2,
@@ -497,6 +501,9 @@ def main():
         line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
     if not args.no_lm_head and rows == 1:
         line["lm_head"] = lm_head_bench(B, LY, synth)
+    if args.formats and rows == 1:
+        fmts = [tuple(int(v) for v in f.split(":")) for f in args.formats.split(",")]
+        line["formats"] = formats_sweep(B, LY, synth, fmts)
     print(json.dumps(line), flush=True)
     return 0
 
@@ -683,19 +690,47 @@ def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):
     """Multi-row passes: the 16-row pass (distinct weight instances rotated through HBM) or the
     8-layer 64-row stack (each layer with its own input), timed as graph replays of one sweep
     over all layers and instances; algorithmic bytes as for the one-row line."""
+    wl = synth.WORKLOADS[cfg]
+    t0 = time.time()
+    sets = [(d, arrays) for i in range(instances) for d, arrays in synth.workload_layers(cfg, instance=i)]
+    out = time_layer_set(B, LY, sets, wl.rows, sweeps, warmup)
+    out = {"workload": wl.name, **out}
+    print(f"[bench] rows sweep ({time.time() - t0:.1f} s): {json.dumps(out)}", file=sys.stderr, flush=True)
+    return out
+
+
+def formats_sweep(B, LY, synth, formats, rows_list=(1, 16), instances=4, sweeps=200, warmup=20):
+    """The Bolt-like layer (240 experts) with its routed experts in other affine formats
+    (code width, group size), at 1 and 16 rows: weight instances rotated through HBM as for
+    the one-row line; algorithmic bytes count each format's own codes, scales and biases."""
+    import dataclasses
+    base = synth.WORKLOADS[1].layers[0]
+    res = []
+    for bits, gs in formats:
+        dims = dataclasses.replace(base, quant_bits=bits, group_size=gs)
+        for rows in rows_list:
+            t0 = time.time()
+            sets = [(dims, synth.make_layer(dims, rows, weight_seed=8000 + 100 * i + bits, input_seed=8050 + i))
+                    for i in range(instances)]
+            out = {"bits": bits, "group_size": gs, **time_layer_set(B, LY, sets, rows, sweeps, warmup)}
+            del sets
+            print(f"[bench] format {bits}-bit g{gs} rows {rows} ({time.time() - t0:.1f} s): {json.dumps(out)}",
+                  file=sys.stderr, flush=True)
+            res.append(out)
+    return res
+
+
+def time_layer_set(B, LY, sets, rows, sweeps, warmup):
+    """One sweep over the layers of `sets` ((dims, arrays) pairs, each with its own input),
+    captured in a graph and replayed: time per layer pass and achieved algorithmic GB/s."""
     import numpy as np
     import torch
-    wl = synth.WORKLOADS[cfg]
-    rows = wl.rows
-    t0 = time.time()
     layers, xs, outs, nbytes = [], [], [], 0.0
-    for i in range(instances):
-        for d, arrays in synth.workload_layers(cfg, instance=i):
-            lay = LY.DeviceLayer(d, arrays, max_rows=rows)
-            layers.append(lay)
-            xs.append(LY.to_device(arrays["x"]))
-            outs.append(torch.empty_like(xs[-1]))
-            del arrays
+    for d, arrays in sets:
+        lay = LY.DeviceLayer(d, arrays, max_rows=rows)
+        layers.append(lay)
+        xs.append(LY.to_device(arrays["x"]))
+        outs.append(torch.empty_like(xs[-1]))
     s = torch.cuda.Stream()
     for lay in layers:
         B.moe_latent_set_stream(lay.handle, s.cuda_stream)
@@ -707,8 +742,6 @@ def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):
         lay.status()
         idx, _ = lay.routing(rows)
         nbytes += sum(stage_bytes(lay.dims, rows, len(np.unique(idx))).values())
-    print(f"[bench] rows sweep {wl.name}: {len(layers)} layers ready in {time.time() - t0:.1f} s",
-          file=sys.stderr, flush=True)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
@@ -727,12 +760,11 @@ def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):
     us_sweep = a.elapsed_time(b) * 1e3 / sweeps
     n_layers = len(layers)
     gbps = nbytes / (us_sweep * 1e-6) / 1e9
-    out = {"workload": wl.name, "rows": rows, "layers_per_sweep": n_layers,
+    out = {"rows": rows, "layers_per_sweep": n_layers,
            "us_per_layer_pass": round(us_sweep / n_layers, 2),
            "layer_tokens_per_s": round(rows * n_layers / (us_sweep * 1e-6), 1),
            "hbm_gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
            "bytes_per_sweep": int(nbytes)}
-    print(f"[bench] rows sweep: {json.dumps(out)}", file=sys.stderr, flush=True)
     for lay in layers:
         lay.close()
     del layers, xs, outs, g

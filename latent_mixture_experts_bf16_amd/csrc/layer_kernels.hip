@@ -1461,10 +1461,11 @@ struct StageLds {
     };
 };
 
-template <int S, bool WIDE, class LdsT>
+// QB: 0 for the fused 4-bit expert items (codes in groups of 64), else the code width of the
+// width-generic expert items.
+template <int S, bool WIDE, int QB, class LdsT>
 __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
-        // a one-row pass: item 0 routes the row with the logits the other gate items hand it
         // a one-row pass: the last item routes the row with the logits the gate items (all
         // dispatched before it) hand it
         const int ngate = p.item_base[ST_GATE + 1] - p.item_base[ST_GATE] - (p.single_row ? 1 : 0);
@@ -1491,12 +1492,15 @@ __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT 
                                  lds.dense, s_flag);
     } else if constexpr (S == ST_UP) {
         const int slot = local / p.up_blocks, blk = local % p.up_blocks;
-        if (p.act_f16) expert_item<true, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex);
+        if constexpr (QB != 0) qexpert_item<QB, true, XMAX_OF(WIDE)>(p, slot, blk, lds.ex);
+        else if (p.act_f16) expert_item<true, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex);
         else expert_item<true, XMAX_OF(WIDE), false>(p, slot, blk, lds.ex);
     } else if constexpr (S == ST_DOWN) {
         const int slot = local / p.dn_blocks, blk = local % p.dn_blocks;
-        const int U = p.act_f16 ? expert_item<false, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex)
-                                : expert_item<false, XMAX_OF(WIDE), false>(p, slot, blk, lds.ex);
+        int U;
+        if constexpr (QB != 0) U = qexpert_item<QB, false, XMAX_OF(WIDE)>(p, slot, blk, lds.ex);
+        else U = p.act_f16 ? expert_item<false, XMAX_OF(WIDE), true>(p, slot, blk, lds.ex)
+                           : expert_item<false, XMAX_OF(WIDE), false>(p, slot, blk, lds.ex);
         if (slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, s_flag))
             combine_block(p, blk * p.dn_nb, p.dn_nb);
     } else if constexpr (S == ST_FC2) {
@@ -1506,14 +1510,14 @@ __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT 
     }
 }
 
-template <int FIRST, int LAST, bool WIDE, int S, class LdsT>
+template <int FIRST, int LAST, bool WIDE, int QB, int S, class LdsT>
 __device__ __forceinline__ void dispatch(const LayerParams &p, int it, LdsT &lds, int *s_flag) {
     if constexpr (S <= LAST) {
         if (it < p.item_base[S + 1]) {
-            run_stage<S, WIDE>(p, it - p.item_base[S], lds, s_flag);
+            run_stage<S, WIDE, QB>(p, it - p.item_base[S], lds, s_flag);
             return;
         }
-        dispatch<FIRST, LAST, WIDE, S + 1>(p, it, lds, s_flag);
+        dispatch<FIRST, LAST, WIDE, QB, S + 1>(p, it, lds, s_flag);
     }
 }
 
@@ -1529,8 +1533,8 @@ constexpr int waves_target(int first, int last, bool wide) {
 // Runs items [lo, hi) of the table, which must lie in the stages [FIRST, LAST]. The hardware
 // dispatches workgroups in index order: workgroups 0 .. pre - 1 take items mid .. mid + pre
 // - 1, the next ones items lo .. mid - 1, the rest items mid + pre .. hi - 1 (pre = 0: table
-// order).
-template <int FIRST, int LAST, bool WIDE>
+// order). QB: the routed expert items' code width (0: the fused 4-bit items).
+template <int FIRST, int LAST, bool WIDE, int QB>
 __global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(waves_target(FIRST, LAST, WIDE), 8)))
 moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre) {
     __shared__ typename StageLds<FIRST, LAST, WIDE>::U lds;
@@ -1538,50 +1542,29 @@ moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre) {
     const int b = (int)blockIdx.x;
     const int it = b < pre ? mid + b : b < pre + (mid - lo) ? lo + b - pre : lo + b;
     if (it >= hi) return;
-    dispatch<FIRST, LAST, WIDE, FIRST>(p, it, lds, &s_flag);
+    dispatch<FIRST, LAST, WIDE, QB, FIRST>(p, it, lds, &s_flag);
 }
 
-template __global__ void moe_stage_kernel<ST_GATE, ST_SHUP, false>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, false>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_GATE, ST_SHUP, false, 0>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_FC2, ST_FC2, false, 0>(LayerParams, int, int, int, int);
 // the shared expert on its own stream
-template __global__ void moe_stage_kernel<ST_SHUP, ST_SHUP, false>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_SHDN_A, ST_SHDN_A, false>(LayerParams, int, int, int, int);
-template __global__ void moe_stage_kernel<ST_SHDN_B, ST_SHDN_B, false>(LayerParams, int, int, int, int);
-
-// The routed expert items of one stage (up or down) with BITS-bit codes: items [lo, hi) of the
-// table, one per workgroup; the last down item of each output block of a multi-row pass
-// combines that block.
-template <int BITS, bool UP, bool WIDE>
-__global__ void __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(3, 8)))
-moe_qexpert_kernel(LayerParams p, int lo, int hi) {
-    __shared__ ExpertLds<XMAX_OF(WIDE)> lds;
-    __shared__ int s_flag;
-    const int it = lo + (int)blockIdx.x;
-    if (it >= hi) return;
-    const int local = it - p.item_base[UP ? ST_UP : ST_DOWN];
-    const int blocks = UP ? p.up_blocks : p.dn_blocks;
-    const int slot = local / blocks, blk = local % blocks;
-    const int U = qexpert_item<BITS, UP, XMAX_OF(WIDE)>(p, slot, blk, lds);
-    if (!UP && slot < U && !p.inline_comb && last_arriver(p.ctr + CTR_BLOCK + blk, (uint32_t)U, &s_flag))
-        combine_block(p, blk * p.dn_nb, p.dn_nb);
-}
-
-#define MOE_QEXPERT(B)                                                              \
-    template __global__ void moe_qexpert_kernel<B, true, false>(LayerParams, int, int);  \
-    template __global__ void moe_qexpert_kernel<B, false, false>(LayerParams, int, int); \
-    template __global__ void moe_qexpert_kernel<B, true, true>(LayerParams, int, int);   \
-    template __global__ void moe_qexpert_kernel<B, false, true>(LayerParams, int, int);
-MOE_QEXPERT(2)
-MOE_QEXPERT(3)
-MOE_QEXPERT(4)
-MOE_QEXPERT(5)
-MOE_QEXPERT(6)
-MOE_QEXPERT(8)
-#undef MOE_QEXPERT
+template __global__ void moe_stage_kernel<ST_SHUP, ST_SHUP, false, 0>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_SHDN_A, ST_SHDN_A, false, 0>(LayerParams, int, int, int, int);
+template __global__ void moe_stage_kernel<ST_SHDN_B, ST_SHDN_B, false, 0>(LayerParams, int, int, int, int);
+// the launches holding routed expert items, for each expert format
+#define MOE_EXPERT_KERNELS(QB)                                                                        \
+    template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, false, QB>(LayerParams, int, int, int, int); \
+    template __global__ void moe_stage_kernel<ST_ROUTE, ST_UP, true, QB>(LayerParams, int, int, int, int);  \
+    template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, false, QB>(LayerParams, int, int, int, int);  \
+    template __global__ void moe_stage_kernel<ST_UP, ST_DOWN, true, QB>(LayerParams, int, int, int, int);
+MOE_EXPERT_KERNELS(0)
+MOE_EXPERT_KERNELS(2)
+MOE_EXPERT_KERNELS(3)
+MOE_EXPERT_KERNELS(4)
+MOE_EXPERT_KERNELS(5)
+MOE_EXPERT_KERNELS(6)
+MOE_EXPERT_KERNELS(8)
+#undef MOE_EXPERT_KERNELS
 
 // Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
 // grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);

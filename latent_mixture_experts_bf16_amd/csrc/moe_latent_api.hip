@@ -21,8 +21,8 @@
 #include "layer_plan.h"
 
 namespace moe {
-template <int FIRST, int LAST, bool WIDE> __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre);
-template <int BITS, bool UP, bool WIDE> __global__ void moe_qexpert_kernel(LayerParams p, int lo, int hi);
+template <int FIRST, int LAST, bool WIDE, int QB>
+__global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre);
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 __global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint16_t *X, int K, int lo);
@@ -490,7 +490,7 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 // split >= 0 the first `pre` items of stage `split` on are dispatched first (see
 // moe_stage_kernel). side: 0 on the caller's stream, 1 on the handle's side stream; join: the
 // launch first waits for the side stream's work of this forward.
-enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B, K_QUP, K_QDOWN };
+enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B };
 struct Launch {
     int first, last, kernel, split, pre, side, join;
 };
@@ -511,22 +511,6 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
     auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0) {
         out[n++] = Launch{f, l, k, split, pre, side, join};
     };
-    if (p.generic) {
-        // other code widths: the routed stages in launches of their own (the width-generic
-        // expert kernels), the shared expert on the side stream (variant 2) or in line
-        const int side = variant == 2 ? 1 : 0;
-        add(ST_GATE, ST_FC1, K_GATE_SHUP);
-        if (p.SI) {
-            add(ST_SHUP, ST_SHUP, K_SHUP, -1, 0, side);
-            add(ST_SHDN_A, ST_SHDN_A, K_SHDN_A, -1, 0, side);
-            add(ST_SHDN_B, ST_SHDN_B, K_SHDN_B, -1, 0, side);
-        }
-        if (!p.single_row) add(ST_ROUTE, ST_ROUTE, K_ROUTE_UP);
-        add(ST_UP, ST_UP, K_QUP);
-        add(ST_DOWN, ST_DOWN, K_QDOWN);
-        if (p.L) add(ST_FC2, ST_FC2, K_FC2, -1, 0, 0, p.SI && side ? 1 : 0);
-        return n;
-    }
     if (variant == 2) {
         add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item last of the gate items
         if (p.SI) {
@@ -563,63 +547,48 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
 }
 
 // ev0, ev1: when set, the kernel's start and end are recorded into them by its own dispatch
-template <int KF, int KL, bool WIDE>
+template <int KF, int KL, bool WIDE, int QB = 0>
 static void launch_kernel(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const int lo = p.item_base[l.first], hi = p.item_base[l.last + 1];
     const int mid = l.split >= 0 ? p.item_base[l.split] : lo, pre = l.split >= 0 ? l.pre : 0;
     if (hi <= lo) return;
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1, 0,
-                              p, lo, hi, mid, pre);
+        hipExtLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE, QB>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1,
+                              0, p, lo, hi, mid, pre);
     else
-        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi, mid,
-                           pre);
+        hipLaunchKernelGGL((moe_stage_kernel<KF, KL, WIDE, QB>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi,
+                           mid, pre);
 }
 
-template <int BITS, bool UP, bool WIDE>
-static void launch_q(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    const int lo = p.item_base[l.first], hi = p.item_base[l.last + 1];
-    if (hi <= lo) return;
-    if (ev0 || ev1)
-        hipExtLaunchKernelGGL((moe_qexpert_kernel<BITS, UP, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, ev0, ev1,
-                              0, p, lo, hi);
-    else
-        hipLaunchKernelGGL((moe_qexpert_kernel<BITS, UP, WIDE>), dim3(hi - lo), dim3(WG_THREADS), 0, st, p, lo, hi);
-}
-
-template <bool UP, bool WIDE>
-static void launch_q_bits(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    switch (p.qbits) {
-        case 2: launch_q<2, UP, WIDE>(p, l, st, ev0, ev1); break;
-        case 3: launch_q<3, UP, WIDE>(p, l, st, ev0, ev1); break;
-        case 4: launch_q<4, UP, WIDE>(p, l, st, ev0, ev1); break;
-        case 5: launch_q<5, UP, WIDE>(p, l, st, ev0, ev1); break;
-        case 6: launch_q<6, UP, WIDE>(p, l, st, ev0, ev1); break;
-        default: launch_q<8, UP, WIDE>(p, l, st, ev0, ev1); break;   // 8: the widths are checked at create
+// A launch holding routed expert items: the instance for the input width and expert format.
+template <int KF, int KL>
+static void launch_expert(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const bool wide = p.D > 2048 || p.I > 2048;
+    const int qb = p.generic ? p.qbits : 0;
+#define MOE_CASE(QB)                                                  \
+    case QB:                                                          \
+        if (wide) launch_kernel<KF, KL, true, QB>(p, l, st, ev0, ev1); \
+        else launch_kernel<KF, KL, false, QB>(p, l, st, ev0, ev1);     \
+        break;
+    switch (qb) {
+        MOE_CASE(0)
+        MOE_CASE(2)
+        MOE_CASE(3)
+        MOE_CASE(4)
+        MOE_CASE(5)
+        MOE_CASE(6)
+        MOE_CASE(8)
+        default: break;   // widths are checked at create
     }
+#undef MOE_CASE
 }
 
 static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr) {
-    const bool wide = p.D > 2048 || p.I > 2048;
     switch (l.kernel) {
-        case K_QUP:
-            if (wide) launch_q_bits<true, true>(p, l, st, ev0, ev1);
-            else launch_q_bits<true, false>(p, l, st, ev0, ev1);
-            break;
-        case K_QDOWN:
-            if (wide) launch_q_bits<false, true>(p, l, st, ev0, ev1);
-            else launch_q_bits<false, false>(p, l, st, ev0, ev1);
-            break;
         case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st, ev0, ev1); break;
-        case K_ROUTE_UP:
-            if (wide) launch_kernel<ST_ROUTE, ST_UP, true>(p, l, st, ev0, ev1);
-            else launch_kernel<ST_ROUTE, ST_UP, false>(p, l, st, ev0, ev1);
-            break;
-        case K_UP_DOWN:
-            if (wide) launch_kernel<ST_UP, ST_DOWN, true>(p, l, st, ev0, ev1);
-            else launch_kernel<ST_UP, ST_DOWN, false>(p, l, st, ev0, ev1);
-            break;
+        case K_ROUTE_UP: launch_expert<ST_ROUTE, ST_UP>(p, l, st, ev0, ev1); break;
+        case K_UP_DOWN: launch_expert<ST_UP, ST_DOWN>(p, l, st, ev0, ev1); break;
         case K_SHUP: launch_kernel<ST_SHUP, ST_SHUP, false>(p, l, st, ev0, ev1); break;
         case K_SHDN_A: launch_kernel<ST_SHDN_A, ST_SHDN_A, false>(p, l, st, ev0, ev1); break;
         case K_SHDN_B: launch_kernel<ST_SHDN_B, ST_SHDN_B, false>(p, l, st, ev0, ev1); break;
