@@ -32,6 +32,7 @@ HBM_PEAK_GBPS = 8000.0
 # moe_latent_group_stages), and the keys of stage_bytes
 STAGE_KEYS = ["gate", "fc1", "shup", "route", "shdn_a", "up", "shdn_b", "down", "fc2"]
 KERNEL_SOURCES = ["latent_mixture_experts_bf16_amd/csrc/layer_kernels.hip",
+                  "latent_mixture_experts_bf16_amd/csrc/layer_items.h",
                   "latent_mixture_experts_bf16_amd/csrc/layer_plan.h",
                   "latent_mixture_experts_bf16_amd/csrc/moe_latent_api.hip"]
 COPY_MIB = 512   # size of the calibration copy (int32 negation: reads and writes COPY_MIB MiB)

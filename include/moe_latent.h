@@ -68,7 +68,7 @@ typedef struct {
 /* Layer configuration. Sizes the kernels take: hidden % 512 == 0; latent == 0 or
  * latent % 128 == 0; expert_inter % 64 == 0; shared_inter == 0 or % 128 == 0; expert input
  * and inter widths <= 6144; n_experts <= 1024; n_group <= 256; top_k <= 16;
- * 1 <= max_rows <= 256. latent == 0 selects the non-latent layer; shared_inter == 0 drops
+ * 1 <= max_rows <= 4096 (a decode pass takes at most 256 rows, a prefill up to max_rows). latent == 0 selects the non-latent layer; shared_inter == 0 drops
  * the shared expert. A shared expert needs a latent layer (MOE_ERR_SHAPE otherwise): its
  * output is added in the fc2 epilogue.
  * Routed expert format: quant_bits-bit affine codes in groups of group_size inputs (the
@@ -150,6 +150,23 @@ int moe_latent_create(const moe_latent_config *cfg, const moe_latent_weights *w,
  * faults surface at the caller's next synchronisation / moe_latent_status(). The handle is
  * not reentrant: forwards on one handle must not overlap in time on different streams. */
 int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out);
+
+/* The fused prefill: one pass of `rows` rows (1 .. max_rows, up to 4096) through the same
+ * layer, for prompts (TensorFold pull request 1038, «Not yet / next»: a fused prefill for the
+ * latent MoE, where prompts otherwise run through the decode kernels 16 rows at a time).
+ * The projections and the routed experts run as MFMA GEMMs over all rows at once: the picks
+ * are grouped by expert (a counting sort on the device) and each expert's weights are read
+ * once per tile of 64 of its picks. Same arithmetic as moe_latent_forward -- the same gate
+ * order, so the same logits and routing bit for bit; the same route, combine and rounding
+ * points -- with other fp32 summation orders in the projections and experts, so outputs
+ * agree with a decode pass within the parity bar, not bit for bit. Each row of a prefill
+ * equals that row passed alone through moe_latent_prefill, bit for bit. Takes bf16
+ * activations, 4-bit codes in groups of 64 and expert_inter a multiple of 128
+ * (MOE_ERR_DTYPE / MOE_ERR_SHAPE otherwise). Buffers and errors as moe_latent_forward (in
+ * place allowed); enqueued on the handle's stream as a chain of launches, no allocation;
+ * moe_latent_get_routing and moe_latent_read_stage then report this pass. moe_latent_forward
+ * itself takes at most 256 rows (MOE_ERR_ROWS above). */
+int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out);
 
 /* Release the workspace and the handle (NULL-safe; a handle already destroyed or never
  * created is ignored). Synchronises the handle's stream first, so no enqueued forward still

@@ -71,6 +71,7 @@ def _load():
                                              ctypes.POINTER(moe_latent_weights), P,
                                              ctypes.POINTER(P)]),
         "moe_latent_forward": (ctypes.c_int, [P, ctypes.c_int32, P, P]),
+        "moe_latent_prefill": (ctypes.c_int, [P, ctypes.c_int32, P, P]),
         "moe_latent_destroy": (None, [P]),
         "moe_latent_set_stream": (ctypes.c_int, [P, P]),
         "moe_latent_set_variant": (ctypes.c_int, [P, ctypes.c_int32]),
@@ -102,7 +103,7 @@ EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "mo
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
             "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
             "moe_latent_stream_read", "moe_latent_forward_static", "moe_latent_group_stages",
-            "moe_lm_head_gemv")
+            "moe_lm_head_gemv", "moe_latent_prefill")
 
 
 def lib():
@@ -155,6 +156,14 @@ def moe_latent_forward(h: int, rows: int, hidden_in: int, out: int) -> None:
 
 def moe_latent_forward_rc(h: int, rows: int, hidden_in: int, out: int) -> int:
     return _lib.moe_latent_forward(h, rows, hidden_in, out)
+
+
+def moe_latent_prefill(h: int, rows: int, hidden_in: int, out: int) -> None:
+    _check(_lib.moe_latent_prefill(h, rows, hidden_in, out))
+
+
+def moe_latent_prefill_rc(h: int, rows: int, hidden_in: int, out: int) -> int:
+    return _lib.moe_latent_prefill(h, rows, hidden_in, out)
 
 
 def moe_latent_destroy(h: int) -> None:

@@ -12,11 +12,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_latent.so")
-SOURCES = ["layer_kernels.hip", "moe_latent_api.hip"]
+SOURCES = ["layer_kernels.hip", "prefill_kernels.hip", "moe_latent_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,10 +24,22 @@ FLAGS = [
 ]
 
 
+OBJ = os.path.join(PKG, "_build")
+
+
 def build(extra=()):
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object (in parallel), then link the library."""
+    os.makedirs(OBJ, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    procs, objs = [], []
+    for s in SOURCES:
+        o = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        objs.append(o)
+        procs.append(subprocess.Popen([HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, s), "-o", o]))
+    bad = [s for s, p in zip(SOURCES, procs) if p.wait() != 0]
+    if bad:
+        raise subprocess.CalledProcessError(1, f"hipcc -c {' '.join(bad)}")
+    subprocess.run([HIPCC, *FLAGS, *extra, "-shared", *objs, "-o", LIB + ".tmp"], check=True)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -30,7 +30,8 @@ enum Stage : int {
 enum : int {
     MAX_EXPERTS = 1024,
     MAX_TOPK = 16,
-    MAX_ROWS = 256,
+    MAX_ROWS = 256,            // rows of a decode pass
+    MAX_PREFILL_ROWS = 4096,   // rows of a prefill pass (and of a handle's workspace)
     // completion counters (uint32) of the last-arriver steps; the dense projections' tile
     // counters follow (offsets in LayerParams)
     CTR_ROUTE = 1,
@@ -114,6 +115,12 @@ struct LayerParams {
     // fp32 (lm_f32) or bf16
     void *lm_out;
     int lm_n, lm_f32;
+    // the prefill's per-expert lists of picks (workspace)
+    int32_t *pf_count;     // [E] picks of each expert (zeroed before the route)
+    int32_t *pf_slot;      // [rows * K] place of each pick in its expert's list
+    int32_t *pf_off;       // [E + 1] start of each expert's list
+    int32_t *pf_tile;      // [E + 1] first row tile of each expert (tiles of 64 picks)
+    int32_t *pf_pairs;     // [rows * K] pick ids (row * K + j), grouped by expert
 };
 
 }  // namespace moe

@@ -26,6 +26,14 @@ __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 __global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint16_t *X, int K, int lo);
+// the prefill (prefill_kernels.hip)
+template <bool F32W> __global__ void pf_gate_kernel(LayerParams p);
+__global__ void pf_route_kernel(LayerParams p);
+__global__ void pf_sched_kernel(LayerParams p);
+template <int EPI>
+__global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
+template <bool UP> __global__ void pf_expert_kernel(LayerParams p);
+__global__ void pf_combine_kernel(LayerParams p);
 }  // namespace moe
 
 using namespace moe;
@@ -195,8 +203,8 @@ static int check_config(const moe_latent_config &c) {
     if (c.router_dtype != MOE_DT_BF16 && c.router_dtype != MOE_DT_F32)
         return fail(MOE_ERR_DTYPE, "config: router_dtype %s (bf16 or f32)", dt_name(c.router_dtype));
     if (c.activation != MOE_ACT_RELU2) return fail(MOE_ERR_INVALID_ARG, "config: activation %d", c.activation);
-    if (c.max_rows < 1 || c.max_rows > MAX_ROWS)
-        return fail(MOE_ERR_ROWS, "config: max_rows %d outside 1..%d", c.max_rows, (int)MAX_ROWS);
+    if (c.max_rows < 1 || c.max_rows > MAX_PREFILL_ROWS)
+        return fail(MOE_ERR_ROWS, "config: max_rows %d outside 1..%d", c.max_rows, (int)MAX_PREFILL_ROWS);
     return MOE_OK;
 }
 
@@ -326,16 +334,18 @@ static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_
     p.ctr_hand = (p.ctr_fc2 + (L ? (int)(H / DENSE_TILE) : 0) + 1) & ~1;
     *n_ctr = p.ctr_hand + 2 * (int)E;
     p.wait_ticks = 10000000u;   // 100 ms: far beyond any forward
-    // split-K partials: [tile][split][row][16] floats = N * splits * rows floats
-    const size_t part_fc1 = L * p.ks_fc1 * R * 4;
-    const size_t part_shup = SI * p.ks_shup * R * 4;
-    const size_t part_shdn = SI ? H * p.ks_shdn * R * 4 : 0;
-    const size_t part_fc2 = L ? H * p.ks_fc2 * R * 4 : 0;
-    enum { NREG = 16 };
+    // split-K partials of decode passes: [tile][split][row][16] floats = N * splits * rows
+    // floats (a decode pass takes at most MAX_ROWS rows; a prefill none of these)
+    const size_t Rd = R < (size_t)MAX_ROWS ? R : (size_t)MAX_ROWS;
+    const size_t part_fc1 = L * p.ks_fc1 * Rd * 4;
+    const size_t part_shup = SI * p.ks_shup * Rd * 4;
+    const size_t part_shdn = SI ? H * p.ks_shdn * Rd * 4 : 0;
+    const size_t part_fc2 = L ? H * p.ks_fc2 * Rd * 4 : 0;
+    enum { NREG = 21 };
     const size_t sizes[NREG] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
                                 R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
                                 R * H * 2, 256, (size_t)*n_ctr * 4, part_fc1, part_shup, part_shdn,
-                                part_fc2};
+                                part_fc2, E * 4, R * K * 4, (E + 1) * 4, (E + 1) * 4, R * K * 4};
     size_t off[NREG], total = 0;
     for (int i = 0; i < NREG; ++i) { off[i] = total; total += align256(sizes[i]); }
     if (base) {
@@ -355,6 +365,11 @@ static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_
         p.part_shup = (float *)(base + off[13]);
         p.part_shdn = (float *)(base + off[14]);
         p.part_fc2 = (float *)(base + off[15]);
+        p.pf_count = (int32_t *)(base + off[16]);
+        p.pf_slot = (int32_t *)(base + off[17]);
+        p.pf_off = (int32_t *)(base + off[18]);
+        p.pf_tile = (int32_t *)(base + off[19]);
+        p.pf_pairs = (int32_t *)(base + off[20]);
     }
     return total;
 }
@@ -681,6 +696,9 @@ static int check_io(moe_latent_t *h, int32_t rows, const void *hidden_in, void *
         return fail(MOE_ERR_LAYOUT, "hidden_in and out must be 16-byte aligned");
     if (rows < 1 || rows > h->cfg.max_rows)
         return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
+    if (rows > MAX_ROWS)
+        return fail(MOE_ERR_ROWS, "rows %d: a decode pass takes at most %d rows (moe_latent_prefill takes up "
+                    "to max_rows)", rows, (int)MAX_ROWS);
     const size_t bytes = (size_t)rows * h->cfg.hidden * 2;
     const char *a = (const char *)hidden_in, *b = (const char *)out;
     if (a != b && a < b + bytes && b < a + bytes)
@@ -697,6 +715,73 @@ extern "C" int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hid
     enqueue(h, p, -1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch: %s", hipGetErrorString(e));
+    h->last_rows = rows;
+    return MOE_OK;
+}
+
+// The layers the prefill takes: bf16 activations, 4-bit codes in groups of 64, and every
+// projection's outputs a multiple of 128 (its tiles), inputs a multiple of 64.
+static int check_prefill_layer(const moe_latent_config &c) {
+    if (c.act_dtype != MOE_DT_BF16) return fail(MOE_ERR_DTYPE, "prefill: bf16 activations only");
+    if (generic_format(c))
+        return fail(MOE_ERR_SHAPE, "prefill: 4-bit codes in groups of 64 only (%d-bit, groups of %d)",
+                    quant_bits_of(c), c.group_size);
+    if (c.expert_inter % 128)
+        return fail(MOE_ERR_SHAPE, "prefill: expert_inter %d not a multiple of 128", c.expert_inter);
+    return MOE_OK;
+}
+
+static int grid8(long n) { return (int)(8 * ((n + 7) / 8)); }
+
+extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
+    if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
+    if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
+    if (((uintptr_t)hidden_in | (uintptr_t)out) & 15)
+        return fail(MOE_ERR_LAYOUT, "hidden_in and out must be 16-byte aligned");
+    if (rows < 1 || rows > h->cfg.max_rows)
+        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, h->cfg.max_rows);
+    {
+        const size_t bytes = (size_t)rows * h->cfg.hidden * 2;
+        const char *a = (const char *)hidden_in, *b = (const char *)out;
+        if (a != b && a < b + bytes && b < a + bytes) return fail(MOE_ERR_ALIAS, "out partially overlaps hidden_in");
+    }
+    if (int rc = check_prefill_layer(h->cfg)) return rc;
+    LayerParams p = h->base;
+    p.x = (const uint16_t *)hidden_in;
+    p.out = (uint16_t *)out;
+    p.rows = rows;
+    p.single_row = 0;
+    p.inline_comb = 0;
+    const hipStream_t st = h->stream;
+    const int E = p.E, K = p.K, NP = rows * K;
+    hipLaunchKernelGGL(moe_clear_kernel, dim3((E + 255) / 256), dim3(256), 0, st, (uint32_t *)p.pf_count, E);
+    {
+        const long wb = (long)((rows + 7) / 8) * ((E + 7) / 8);
+        if (p.router_f32) hipLaunchKernelGGL(pf_gate_kernel<true>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(pf_gate_kernel<false>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
+    }
+    hipLaunchKernelGGL(pf_route_kernel, dim3(rows), dim3(WG_THREADS), 0, st, p);
+    hipLaunchKernelGGL(pf_sched_kernel, dim3((NP + 1023) / 1024), dim3(WG_THREADS), 0, st, p);
+    const int mt = (rows + 127) / 128;
+    if (p.L)
+        hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * (p.L / 128))), dim3(256), 0, st, p, p.x, p.fc1,
+                           p.L, p.H);
+    if (p.SI)
+        hipLaunchKernelGGL(pf_gemm_kernel<1>, dim3(grid8((long)mt * (p.SI / 128))), dim3(256), 0, st, p, p.x, p.su,
+                           p.SI, p.H);
+    // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
+    const long max_tiles = (NP + 63) / 64 + (E < NP ? E : NP);
+    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(max_tiles * (p.I / 128))), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * (p.D / 128))), dim3(256), 0, st, p);
+    if (p.SI)
+        hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
+                           p.H, p.SI);
+    hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)(((long)rows * (p.D / 4) + 255) / 256)), dim3(256), 0, st, p);
+    if (p.L)
+        hipLaunchKernelGGL(pf_gemm_kernel<3>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.comb, p.fc2,
+                           p.H, p.L);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     h->last_rows = rows;
     return MOE_OK;
 }
@@ -755,7 +840,7 @@ extern "C" int moe_latent_stream_read(const void *src, size_t bytes, uint32_t *s
 }
 
 extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group) {
-    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows || rows > MAX_ROWS) return -1;
     LayerParams p = h->base;
     plan_items(p, rows);
     Launch ls[MAX_LAUNCHES];
@@ -766,7 +851,7 @@ extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t gro
 
 extern "C" int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t group, int32_t *first_stage,
                                        int32_t *last_stage, int32_t *side) {
-    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows) return -1;
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows || rows > MAX_ROWS) return -1;
     LayerParams p = h->base;
     plan_items(p, rows);
     Launch ls[MAX_LAUNCHES];
@@ -884,8 +969,8 @@ extern "C" int moe_latent_forward_static(const moe_latent_config *cfg, const moe
     if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
     if (((uintptr_t)hidden_in | (uintptr_t)out) & 15)
         return fail(MOE_ERR_LAYOUT, "hidden_in and out must be 16-byte aligned");
-    if (rows < 1 || rows > cfg->max_rows)
-        return fail(MOE_ERR_ROWS, "rows %d outside 1..max_rows %d", rows, cfg->max_rows);
+    if (rows < 1 || rows > cfg->max_rows || rows > MAX_ROWS)
+        return fail(MOE_ERR_ROWS, "rows %d outside 1..%d (max_rows, at most %d)", rows, cfg->max_rows, (int)MAX_ROWS);
     const size_t bytes = (size_t)rows * cfg->hidden * 2;
     const char *a = (const char *)hidden_in, *b = (const char *)out;
     if (a != b && a < b + bytes && b < a + bytes) return fail(MOE_ERR_ALIAS, "out partially overlaps hidden_in");

@@ -1,0 +1,541 @@
+// prefill_kernels.hip -- the fused prefill of one latent mixture-of-experts layer (gfx950):
+// many rows (hundreds to thousands) through the layer in a handful of launches, with the
+// projections and the routed experts as MFMA GEMMs over all rows at once, instead of the
+// decode kernels' tiles of 16 rows (TensorFold pull request 1038, «Not yet / next»: a fused
+// prefill for the latent MoE, where prompts otherwise run through the decode kernels 16 rows
+// at a time).
+//
+// The layer's arithmetic is that of the decode path (layer_items.h): the same gate order (so
+// the logits and the routing are the same bits), the same route and combine items, and the
+// same rounding points; only the fp32 summation order of the projections and of the experts
+// differs. Launches, in order:
+//   gate     logits of every row, the decode gate's lane order (8 rows x 8 experts a wave)
+//   route    one row per workgroup (the decode route item); each pick takes a place in its
+//            expert's list with an atomic counter
+//   sched    prefix sums of the per-expert counts (list starts, row-tile starts) and the
+//            pick ids scattered into the per-expert lists
+//   gemm     fc1 (u = rnd(W1 x)) and shared up (rnd(relu^2(rnd(Su x)))): 128 x 128 tiles
+//   expert   routed up / down: tiles of 64 picks of one expert x 128 outputs, 4-bit codes
+//            decoded in registers, MFMA per group of 64 inputs, then scale and bias per group
+//   gemm     shared down (rnd(Sd a))
+//   combine  every row (the decode combine: lane order and rounding)
+//   gemm     fc2 with the final adds: out = rnd(x + rnd(rnd(W2 c) + sh))
+// Every output's sum runs over its inputs in one fixed order whatever the number of rows,
+// so each row of a pass equals that row passed alone, bit for bit.
+#include "layer_items.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ gate
+
+// Logits of rows [8 rb, +8) x experts [8 eb, +8) per wave, each the decode gate's fixed
+// order: lane t accumulates, from +0 with fused multiply-adds, the terms k = 512 j + 8 t + i
+// (j outer, i inner), and the 64 lane partials are joined by an xor butterfly 32 .. 1. Rows
+// and experts past the end are clamped (computed again, not stored). F32W: fp32 gate weights
+// (fp32 logits); else bf16 weights, logits rounded to bf16.
+template <bool F32W>
+__global__ void __launch_bounds__(256) pf_gate_kernel(LayerParams p) {
+    const int wave = threadIdx.x >> 6, t = threadIdx.x & 63;
+    const int nEB = (p.E + 7) >> 3, nRB = (p.rows + 7) >> 3;
+    const int wb = blockIdx.x * 4 + wave;
+    if (wb >= nEB * nRB) return;
+    const int eb = wb % nEB, rb = wb / nEB;
+    const int H = p.H;
+    const uint16_t *xr[8];
+    int er[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = rb * 8 + i, e = eb * 8 + i;
+        xr[i] = p.x + (size_t)(r < p.rows ? r : p.rows - 1) * H;
+        er[i] = e < p.E ? e : p.E - 1;
+    }
+    float acc[8][8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
+    for (int j = 0; j < H / 512; ++j) {
+        const int k = 512 * j + 8 * t;
+        uint4 xv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) xv[r] = *(const uint4 *)(xr[r] + k);
+        if constexpr (F32W) {
+            float4 w0[8], w1[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float *wp = p.gate_w32 + (size_t)er[e] * H + k;
+                w0[e] = *(const float4 *)wp;
+                w1[e] = *(const float4 *)(wp + 4);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float xf[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint32_t wd = i < 2 ? xv[r].x : i < 4 ? xv[r].y : i < 6 ? xv[r].z : xv[r].w;
+                    xf[r] = bf2f(i & 1 ? wd >> 16 : wd & 0xFFFFu);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float4 &q = i < 4 ? w0[e] : w1[e];
+                    const float wf = (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) acc[r][e] = __builtin_fmaf(xf[r], wf, acc[r][e]);
+                }
+            }
+        } else {
+            uint4 wv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv[e] = *(const uint4 *)(p.gate_w16 + (size_t)er[e] * H + k);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float xf[8], wf[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const uint32_t wd = i < 2 ? xv[r].x : i < 4 ? xv[r].y : i < 6 ? xv[r].z : xv[r].w;
+                    xf[r] = bf2f(i & 1 ? wd >> 16 : wd & 0xFFFFu);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t wd = i < 2 ? wv[e].x : i < 4 ? wv[e].y : i < 6 ? wv[e].z : wv[e].w;
+                    wf[e] = bf2f(i & 1 ? wd >> 16 : wd & 0xFFFFu);
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(xf[r], wf[e], acc[r][e]);
+            }
+        }
+    }
+    // the butterfly: lane t takes P[t] + P[t ^ d] (both lanes of a pair get the same sum)
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[r][e];
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
+            acc[r][e] = v;
+        }
+    if (t == 0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int row = rb * 8 + r, ex = eb * 8 + e;
+                if (row < p.rows && ex < p.E) {
+                    if constexpr (F32W) ((float *)p.logits)[(size_t)row * p.E + ex] = acc[r][e];
+                    else ((uint16_t *)p.logits)[(size_t)row * p.E + ex] = f2bf(acc[r][e]);
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ route and lists
+
+// One row per workgroup: the decode route item, then each pick counts itself in its expert's
+// list (its place there is the count before it; the order of the places inside a list does
+// not change any result, since every row of a tile is its own MFMA column).
+__global__ void __launch_bounds__(WG_THREADS) pf_route_kernel(LayerParams p) {
+    __shared__ RouteLds<WG_THREADS> lds;
+    const int r = blockIdx.x;
+    route_item<WG_THREADS>(p, r, lds);
+    __syncthreads();
+    if (threadIdx.x < p.K) {
+        const int i = r * p.K + (int)threadIdx.x;
+        int e = ld_shared32(p.idx + i);
+        e = e < 0 || e >= p.E ? 0 : e;   // never: the route writes valid ids
+        p.pf_slot[i] = atomicAdd(p.pf_count + e, 1);
+    }
+}
+
+// Exclusive prefix sums of the per-expert counts (list starts) and of their row tiles of
+// PF_BM picks (tile starts), computed by every workgroup (workgroup 0 stores them), then each
+// workgroup scatters its 1024 picks into the lists.
+constexpr int PF_BM = 64;    // picks per expert tile
+constexpr int PF_BN = 128;   // outputs per expert tile and per dense tile
+constexpr int PF_DM = 128;   // rows per dense tile
+
+__global__ void __launch_bounds__(WG_THREADS) pf_sched_kernel(LayerParams p) {
+    __shared__ int off[MAX_EXPERTS + 1], toff[MAX_EXPERTS + 1];
+    __shared__ int sa[WG_THREADS], sb[WG_THREADS];
+    const int tid = threadIdx.x, E = p.E;
+    // thread t: experts [4t, 4t + 4)
+    int c[4], tl[4], s0 = 0, s1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        c[i] = e < E ? p.pf_count[e] : 0;
+        tl[i] = (c[i] + PF_BM - 1) / PF_BM;
+        s0 += c[i];
+        s1 += tl[i];
+    }
+    sa[tid] = s0;
+    sb[tid] = s1;
+    __syncthreads();
+    for (int d = 1; d < WG_THREADS; d <<= 1) {   // inclusive scan (Hillis-Steele)
+        const int a = tid >= d ? sa[tid - d] : 0, b = tid >= d ? sb[tid - d] : 0;
+        __syncthreads();
+        sa[tid] += a;
+        sb[tid] += b;
+        __syncthreads();
+    }
+    int o0 = sa[tid] - s0, o1 = sb[tid] - s1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        if (e < E) { off[e] = o0; toff[e] = o1; }
+        o0 += c[i];
+        o1 += tl[i];
+    }
+    if (tid == WG_THREADS - 1) { off[E] = sa[tid]; toff[E] = sb[tid]; }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += WG_THREADS) {
+            p.pf_off[e] = off[e];
+            p.pf_tile[e] = toff[e];
+        }
+    const int NP = p.rows * p.K;
+    for (int i = blockIdx.x * 1024 + tid; i < NP && i < (blockIdx.x + 1) * 1024; i += WG_THREADS) {
+        int e = p.idx[i];
+        e = e < 0 || e >= E ? 0 : e;
+        p.pf_pairs[off[e] + p.pf_slot[i]] = i;
+    }
+}
+
+// ------------------------------------------------------------------ MFMA tiles
+
+// 16-byte units of a tile row of 64 bf16 (128 bytes) are stored at unit (c ^ (row & 7)), so
+// that the 16 rows a fragment read touches fall in distinct banks.
+__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+
+// vmcnt(n) with the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
+// A workgroup's place in the logical order of `total` tiles: consecutive workgroups go to
+// the 8 XCDs in turn, so logical tile i is run by XCD i / per (per = ceil(total / 8)) and
+// neighbouring tiles share an XCD's L2. Returns -1 past the end.
+__device__ __forceinline__ int xcd_tile(int total) {
+    const int b = (int)blockIdx.x, per = (total + 7) >> 3;
+    const int i = b >> 3, x = b & 7;
+    if (i >= per) return -1;
+    const int l = x * per + i;
+    return l < total ? l : -1;
+}
+
+enum PfEpi { PF_FC1 = 0, PF_SHUP = 1, PF_SHDN = 2, PF_FC2 = 3 };
+
+struct PfGemmLds {
+    uint4 a[2][PF_DM * 8];    // [buffer][row][8 units of 16 bytes]: 64 inputs of each row
+    uint4 b[2][PF_BN * 8];
+};
+
+// C[m][n] = sum_k X[m][k] W[n][k] for m < rows (X = [rows][K] bf16, W = [N][K] bf16), tiles
+// of 128 rows x 128 outputs, 64 inputs a step (double-buffered direct copies to LDS). Wave w
+// holds rows 64 (w & 1) .. +63 and outputs 64 (w >> 1) .. +63 as 4 x 4 MFMA 16x16x32 tiles
+// with the weights as the first operand, so lane l ends with outputs 4 (l >> 4) .. +3 of row
+// l & 15 of each tile; each output's sum runs over k in one fixed order. Epilogues: fc1
+// (rounded), shared up (relu^2 of the rounded sum, rounded), shared down (rounded), fc2
+// (out = rnd(x + rnd(rnd(sum) + sh))).
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_gemm_kernel(LayerParams p, const uint16_t *__restrict__ X,
+                                                         const uint16_t *__restrict__ W, int N, int K) {
+    __shared__ PfGemmLds L;
+    const int nbn = N / PF_BN, nbm = (p.rows + PF_DM - 1) / PF_DM;
+    const int tile = xcd_tile(nbn * nbm);
+    if (tile < 0) return;
+    const int m0 = (tile / nbn) * PF_DM, n0 = (tile % nbn) * PF_BN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave & 1, wn = wave >> 1;
+    // the copies: wave w moves units [256 w, 256 w + 256) of each 1024-unit tile, lane l unit
+    // 256 w + 64 i + l in instruction i: row u >> 3, stored swizzled
+    const uint16_t *xs[4], *ws[4];
+    int du[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 256 * wave + 64 * i + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
+        const int m = m0 + row < p.rows ? m0 + row : p.rows - 1;
+        xs[i] = X + (size_t)m * K + 8 * c;
+        ws[i] = W + (size_t)(n0 + row) * K + 8 * c;
+        du[i] = 256 * wave + 64 * i;   // first unit of the instruction (the copy adds 16 l bytes)
+    }
+    auto issue = [&](int ks, int buf) {
+        const int k0 = 64 * ks;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(xs[i] + k0, &L.a[buf][du[i]]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(ws[i] + k0, &L.b[buf][du[i]]);
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int nk = K / 64;
+    issue(0, 0);
+    for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nk) {
+            issue(ks + 1, buf ^ 1);
+            wait_vm<8>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint4 xf[4], wf[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                xf[mi] = lds_ld16(&L.a[buf][swz(wm * 64 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                wf[ni] = lds_ld16(&L.b[buf][swz(wn * 64 + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wf[ni]), __builtin_bit_cast(bf16x8, xf[mi]), acc[ni][mi], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    // epilogue: lane l has outputs n .. n + 3 of row m of each tile
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int m = m0 + wm * 64 + mi * 16 + (lane & 15);
+        if (m >= p.rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int n = n0 + wn * 64 + ni * 16 + 4 * (lane >> 4);
+            const f32x4 v = acc[ni][mi];
+            uint16_t o[4];
+            if constexpr (EPI == PF_FC2) {
+                const uint2 sh = *(const uint2 *)(p.shout + (size_t)m * p.H + n);
+                const uint2 xv = *(const uint2 *)(p.x + (size_t)m * p.H + n);
+                const uint32_t shw[2] = {sh.x, sh.y}, xw[2] = {xv.x, xv.y};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float s16 = bf2f(q & 1 ? shw[q >> 1] >> 16 : shw[q >> 1] & 0xFFFFu);
+                    const float x16 = bf2f(q & 1 ? xw[q >> 1] >> 16 : xw[q >> 1] & 0xFFFFu);
+                    const float mm = rnd(0, v[q]);
+                    o[q] = f2bf(x16 + rnd(0, mm + (p.SI ? s16 : 0.0f)));
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = EPI == PF_SHUP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
+            }
+            const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+            uint16_t *dst = EPI == PF_FC1 ? p.u + (size_t)m * p.L + n
+                          : EPI == PF_SHUP ? p.shact + (size_t)m * p.SI + n
+                          : EPI == PF_SHDN ? p.shout + (size_t)m * p.H + n
+                                           : p.out + (size_t)m * p.H + n;
+            *(uint2 *)dst = ov;
+        }
+    }
+}
+
+template __global__ void pf_gemm_kernel<PF_FC1>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_SHUP>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+
+// ------------------------------------------------------------------ routed experts
+
+struct PfExpertLds {
+    uint4 a[2][PF_BM * 8];        // [buffer][pick][8 units]: 64 inputs of each pick's row
+    uint32_t q[2][PF_BN * 8];     // [buffer][output][8 words]: 64 codes of each output row
+    uint16_t s[PF_BN * 96];       // scales [output][group] of the whole input range (<= 6144)
+    uint16_t b[PF_BN * 96];       // biases
+    int pair[PF_BM];
+};
+
+// Tile: picks [m0, m0 + 64) of expert e's list x outputs [n0, n0 + 128) of its up (UP) or
+// down projection, 64 inputs (one group of the 4-bit codes) a step. Per group g and output n
+// the tile forms, per pick, a = sum over the group of (128 + q) x (MFMA: the codes decoded
+// into bf16 128 + q exactly, the inputs reordered to the codes' pairing) and sx = sum of x,
+// and adds scale * a + (bias - 128 scale) * sx -- the group's share of sum(w x) with w =
+// q scale + bias. Wave w holds picks 32 (w & 1) .. +31 and outputs 64 (w >> 1) .. +63. Up:
+// eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum).
+template <bool UP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_expert_kernel(LayerParams p) {
+    __shared__ PfExpertLds L;
+    const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
+    const int nbn = N / PF_BN, G = Kin >> 6;
+    const int total_tiles = p.pf_tile[p.E];
+    const int lt = xcd_tile(total_tiles * nbn);
+    if (lt < 0) return;
+    const int t = lt / nbn, n0 = (lt % nbn) * PF_BN;
+    // the expert of row tile t: the last e with pf_tile[e] <= t
+    int lo = 0, hi = p.E;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.pf_tile[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    const int e = lo;
+    const int list0 = p.pf_off[e], cnt = p.pf_off[e + 1] - list0;
+    const int m0 = (t - p.pf_tile[e]) * PF_BM;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wm = wave & 1, wn = wave >> 1;
+    if (tid < PF_BM) {
+        const int m = m0 + tid < cnt ? m0 + tid : cnt - 1;
+        L.pair[tid] = p.pf_pairs[list0 + m];
+    }
+    // this expert's scales and biases for the tile's outputs, every group
+    const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G;
+    const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G;
+    for (int i = tid; i < PF_BN * G / 8; i += 256) {
+        ((uint4 *)L.s)[i] = *(const uint4 *)(S + 8 * i);
+        ((uint4 *)L.b)[i] = *(const uint4 *)(B + 8 * i);
+    }
+    __syncthreads();
+    // copies per step: the picks' inputs (64 x 128 bytes: two 1 KB instructions a wave) and
+    // the codes (128 x 32 bytes: one a wave)
+    const uint16_t *xsrc[2];
+    int du[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = 128 * wave + 64 * i + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
+        const int pr = L.pair[row];
+        xsrc[i] = (UP ? (p.L ? p.u : p.x) + (size_t)(pr / p.K) * Kin : p.eact + (size_t)pr * Kin) + 8 * c;
+        du[i] = 128 * wave + 64 * i;
+    }
+    const uint32_t *qsrc = (UP ? p.up_q : p.dn_q) + ((size_t)e * N + n0 + ((64 * wave + lane) >> 1)) * (Kin >> 3) +
+                           4 * (lane & 1);
+    const int qdu = 64 * wave;   // 16-byte unit of the copy (output row (64 w + l) >> 1, half l & 1)
+    auto issue = [&](int ks, int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + 64 * ks, &L.a[buf][du[i]]);
+        lds_dma16(qsrc + 8 * ks, &((uint4 *)L.q[buf])[qdu]);
+    };
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    issue(0, 0);
+    for (int g = 0; g < G; ++g) {
+        const int buf = g & 1;
+        if (g + 1 < G) {
+            issue(g + 1, buf ^ 1);
+            wait_vm<3>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();
+        // the inputs: pairs (x[8c+i], x[8c+i+4]) to match the codes' pairing, and each pick's
+        // group sum (this lane's 16 values, then the 4 lanes of the same pick, in a fixed order)
+        uint4 xf[2][2];
+        float sx[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+            sx[mi] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint4 v = lds_ld16(&L.a[buf][swz(wm * 32 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+                xf[mi][s].x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+                xf[mi][s].y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+                xf[mi][s].z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+                xf[mi][s].w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+                sx[mi] = dot2<false>(0x3F803F80u, v.x, sx[mi]);
+                sx[mi] = dot2<false>(0x3F803F80u, v.y, sx[mi]);
+                sx[mi] = dot2<false>(0x3F803F80u, v.z, sx[mi]);
+                sx[mi] = dot2<false>(0x3F803F80u, v.w, sx[mi]);
+            }
+            sx[mi] = sx[mi] + __shfl_xor(sx[mi], 16, 64);
+            sx[mi] = sx[mi] + __shfl_xor(sx[mi], 32, 64);
+        }
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int nl = wn * 64 + ni * 16 + (lane & 15);   // the code row this lane decodes
+            uint4 wf[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint32_t w = L.q[buf][nl * 8 + 4 * s + (lane >> 4)];
+                wf[s] = make_uint4(code_pair<false>(w, 0), code_pair<false>(w, 1), code_pair<false>(w, 2),
+                                   code_pair<false>(w, 3));
+            }
+            // scale and bias of the 4 outputs this lane ends with
+            const int no = wn * 64 + ni * 16 + 4 * (lane >> 4);
+            float sc[4], cb[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sc[q] = bf2f(L.s[(no + q) * G + g]);
+                cb[q] = __builtin_fmaf(-128.0f, sc[q], bf2f(L.b[(no + q) * G + g]));
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[0]),
+                                                            __builtin_bit_cast(bf16x8, xf[mi][0]), a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[1]),
+                                                            __builtin_bit_cast(bf16x8, xf[mi][1]), a, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v = __builtin_fmaf(sc[q], a[q], acc[ni][mi][q]);
+                    acc[ni][mi][q] = __builtin_fmaf(cb[q], sx[mi], v);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int ml = wm * 32 + mi * 16 + (lane & 15);
+        if (m0 + ml >= cnt) continue;
+        const int pr = L.pair[ml];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int n = n0 + wn * 64 + ni * 16 + 4 * (lane >> 4);
+            const f32x4 v = acc[ni][mi];
+            uint16_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = UP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
+            const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+            *(uint2 *)((UP ? p.eact + (size_t)pr * p.I : p.eout + (size_t)pr * p.D) + n) = ov;
+        }
+    }
+}
+
+template __global__ void pf_expert_kernel<true>(LayerParams);
+template __global__ void pf_expert_kernel<false>(LayerParams);
+
+// ------------------------------------------------------------------ combine
+
+// comb = rnd(combine) of every row (the decode combine's lane order), 4 outputs a thread; a
+// non-latent layer writes out = rnd(x + rnd(comb)) instead (no fc2, no shared expert).
+__global__ void __launch_bounds__(256) pf_combine_kernel(LayerParams p) {
+    const int per_row = p.D / 4;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= p.rows * per_row) return;
+    const int r = i / per_row, d = 4 * (i % per_row);
+    float c4[4];
+    combine4(p, r, d, c4);
+    uint16_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint16_t c = f2bf(c4[q]);
+        if (p.L) {
+            o[q] = c;
+        } else {
+            const float xv = bf2f(p.x[(size_t)r * p.H + d + q]);
+            o[q] = f2bf(xv + rnd(0, bf2f(c)));
+        }
+    }
+    const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+    *(uint2 *)((p.L ? p.comb + (size_t)r * p.D : p.out + (size_t)r * p.H) + d) = ov;
+}
+
+template __global__ void pf_gate_kernel<false>(LayerParams);
+template __global__ void pf_gate_kernel<true>(LayerParams);
+
+}  // namespace moe

@@ -75,6 +75,10 @@ class DeviceLayer:
         rows = x.shape[0] if rows is None else rows
         B.moe_latent_forward(self.handle, rows, x.data_ptr(), out.data_ptr())
 
+    def prefill(self, x: torch.Tensor, out: torch.Tensor, rows: Optional[int] = None) -> None:
+        rows = x.shape[0] if rows is None else rows
+        B.moe_latent_prefill(self.handle, rows, x.data_ptr(), out.data_ptr())
+
     def routing(self, rows: int):
         idx = torch.empty((rows, self.dims.top_k), dtype=torch.int32, device="cuda")
         w = torch.empty((rows, self.dims.top_k), dtype=torch.float32, device="cuda")

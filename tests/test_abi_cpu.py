@@ -93,7 +93,7 @@ NONLAT = synth.WORKLOADS[3].layers[0]
     ({"quant_bits": 1}, "MOE_ERR_SHAPE", "quant_bits"),
     ({"quant_bits": 3, "expert_inter": 192}, "MOE_ERR_SHAPE", "multiples of 128"),
     ({"max_rows": 0}, "MOE_ERR_ROWS", "max_rows"),
-    ({"max_rows": 257}, "MOE_ERR_ROWS", "max_rows"),
+    ({"max_rows": 4097}, "MOE_ERR_ROWS", "max_rows"),
     ({"act_dtype": B.MOE_DT_F16}, "MOE_ERR_DTYPE", "f16"),
     ({"router_dtype": B.MOE_DT_U32}, "MOE_ERR_DTYPE", "router_dtype"),
     ({"n_experts": 2048, "n_group": 8}, "MOE_ERR_SHAPE", "n_experts"),

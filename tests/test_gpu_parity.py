@@ -77,7 +77,7 @@ def act_ulp(dims, v):
     return np.spacing(v).astype(np.float64) * 65536.0
 
 
-def stage_close(dims, got, ref, what, ulps=1):
+def stage_close(dims, got, ref, what, ulps=1, eq_min=0.99):
     ref_vals, ref_pre = ref
     got = np.asarray(got, np.float64)
     rv = ref_vals.astype(np.float64)
@@ -85,7 +85,7 @@ def stage_close(dims, got, ref, what, ulps=1):
     err = np.abs(got - rv)
     tol = ulps * act_ulp(dims, ref_vals) + 1e-4 * rms
     eq = float((got == rv).mean())
-    assert eq >= 0.99 and (err <= tol).all(), (what, eq, float((err / tol).max()))
+    assert eq >= eq_min and (err <= tol).all(), (what, eq, float((err / tol).max()))
 
 
 _data = {}
