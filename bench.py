@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 # stages of the work-item table, in the library's order (include/moe_latent.h,
 # moe_latent_group_stages), and the keys of stage_bytes
 STAGE_KEYS = ["gate", "fc1", "shup", "route", "shdn_a", "up", "shdn_b", "down", "fc2"]
@@ -103,6 +104,8 @@ def parse():
     ap.add_argument("--formats", default="",
                     help="also time the Bolt-like layer with routed experts in these affine formats, "
                          "e.g. 2:64,3:64,4:64,4:128,5:64,6:64,8:64 (bits:group_size)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the fused prefill timing")
+    ap.add_argument("--only-prefill", action="store_true", help="time the fused prefill only")
     ap.add_argument("--no-lm-head", action="store_true",
                     help="skip the lm_head gemv (K 4096, N 131072, 1 and 16 rows) reported beside it")
     return ap.parse_args()
@@ -238,6 +241,9 @@ def main():
     from latent_mixture_experts_bf16_amd import layer as LY
     from latent_mixture_experts_bf16_amd import synth
 
+    if args.only_prefill:
+        print(json.dumps({"prefill": prefill_bench(B, LY, synth)}), flush=True)
+        return 0
     wl = synth.WORKLOADS[args.config]
     if len(wl.layers) != 1 and args.profile_steps:
         return profile_stack(args, B, LY, synth)
@@ -502,11 +508,68 @@ def main():
         line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
     if not args.no_lm_head and rows == 1:
         line["lm_head"] = lm_head_bench(B, LY, synth)
+    if not args.no_prefill and rows == 1:
+        line["prefill"] = prefill_bench(B, LY, synth)
     if args.formats and rows == 1:
         fmts = [tuple(int(v) for v in f.split(":")) for f in args.formats.split(",")]
         line["formats"] = formats_sweep(B, LY, synth, fmts)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def prefill_flops(d, rows):
+    """Algorithmic flops of one prefill pass: the MFMA GEMMs (fc1, shared up and down, fc2,
+    routed up and down over rows * top_k picks) and, apart, the gate (vector fp32 FMAs)."""
+    D = d.latent or d.hidden
+    gemm = 2 * rows * (d.latent * d.hidden * 2 + d.shared_inter * d.hidden * 2 +
+                       d.top_k * d.expert_inter * D * 2)
+    gate = 2 * rows * d.n_experts * d.hidden
+    return gemm, gate
+
+
+def prefill_bench(B, LY, synth, rows_list=(512, 4096), reps=10):
+    """The fused prefill of the Bolt-like layer (240 experts) at 512 and 4096 rows: one pass
+    captured in a graph and replayed; rows/s and the MFMA GEMMs' flops per second against the
+    dense bf16 peak."""
+    import numpy as np
+    import torch
+    out = {"workload": "bolt-latent-E240 prefill", "peak_tflops_bf16": MFMA_PEAK_TFLOPS}
+    for rows in rows_list:
+        d, arrays = next(synth.workload_layers(1, rows=rows))
+        lay = LY.DeviceLayer(d, arrays, max_rows=rows)
+        x = LY.to_device(arrays["x"])
+        o = torch.empty_like(x)
+        del arrays
+        s = torch.cuda.Stream()
+        B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+        with torch.cuda.stream(s):
+            lay.prefill(x, o, rows)
+        s.synchronize()
+        lay.status()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                lay.prefill(x, o, rows)
+            for _ in range(3):
+                g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            for _ in range(reps):
+                g.replay()
+            b.record(s)
+        torch.cuda.synchronize()
+        lay.status()
+        us = a.elapsed_time(b) * 1e3 / reps
+        gemm, gate = prefill_flops(d, rows)
+        tf = gemm / (us * 1e-6) / 1e12
+        out[f"rows{rows}"] = {"us": round(us, 1), "tokens_per_s": round(rows / (us * 1e-6), 1),
+                              "gemm_tflops": round(tf, 1), "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                              "gemm_flops": gemm, "gate_flops": gate}
+        print(f"[bench] prefill rows {rows}: {json.dumps(out[f'rows{rows}'])}", file=sys.stderr, flush=True)
+        lay.close()
+        del lay, x, o, g
+        torch.cuda.empty_cache()
+    return out
 
 
 def lm_head_bench(B, LY, synth, K=4096, N=131072, reps=40):

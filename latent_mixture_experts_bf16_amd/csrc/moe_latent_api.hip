@@ -771,8 +771,20 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
                            p.SI, p.H);
     // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
     const long max_tiles = (NP + 63) / 64 + (E < NP ? E : NP);
-    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(max_tiles * (p.I / 128))), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * (p.D / 128))), dim3(256), 0, st, p);
+    // dynamic LDS: the tile's scales and biases, 128 outputs x (inputs / 64) groups each (up
+    // to 48 KB beside the kernel's 37 KB; allowed once per process above the default limit)
+    static std::once_flag lds_once;
+    std::call_once(lds_once, [] {
+        (void)hipFuncSetAttribute((const void *)pf_expert_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  96 * 1024);
+        (void)hipFuncSetAttribute((const void *)pf_expert_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  96 * 1024);
+        (void)hipGetLastError();   // a refusal here only keeps the default limit
+    });
+    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(max_tiles * (p.I / 128))), dim3(256),
+                       (unsigned)(2 * 128 * (p.D / 64) * 2), st, p);
+    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * (p.D / 128))), dim3(256),
+                       (unsigned)(2 * 128 * (p.I / 64) * 2), st, p);
     if (p.SI)
         hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
                            p.H, p.SI);

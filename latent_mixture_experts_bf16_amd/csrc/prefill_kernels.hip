@@ -350,13 +350,21 @@ template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, c
 
 // ------------------------------------------------------------------ routed experts
 
+constexpr int PF_NS = 3;   // input steps (groups) in LDS at once: two copies in flight while one is used
+
 struct PfExpertLds {
-    uint4 a[2][PF_BM * 8];        // [buffer][pick][8 units]: 64 inputs of each pick's row
-    uint32_t q[2][PF_BN * 8];     // [buffer][output][8 words]: 64 codes of each output row
-    uint16_t s[PF_BN * 96];       // scales [output][group] of the whole input range (<= 6144)
-    uint16_t b[PF_BN * 96];       // biases
+    uint4 a[PF_NS][PF_BM * 8];    // [buffer][pick][8 units]: 64 inputs of each pick's row
+    uint32_t q[PF_NS][PF_BN * 8]; // [buffer][output][8 words]: 64 codes of each output row
     int pair[PF_BM];
 };
+
+// wait until at most 3 n copy instructions of this wave are outstanding (n = steps still in
+// flight behind the one about to be used)
+__device__ __forceinline__ void wait_steps(int n) {
+    if (n >= 2) wait_vm<6>();
+    else if (n == 1) wait_vm<3>();
+    else wait_vm<0>();
+}
 
 // Tile: picks [m0, m0 + 64) of expert e's list x outputs [n0, n0 + 128) of its up (UP) or
 // down projection, 64 inputs (one group of the 4-bit codes) a step. Per group g and output n
@@ -366,8 +374,11 @@ struct PfExpertLds {
 // q scale + bias. Wave w holds picks 32 (w & 1) .. +31 and outputs 64 (w >> 1) .. +63. Up:
 // eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum).
 template <bool UP>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_expert_kernel(LayerParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) pf_expert_kernel(LayerParams p) {
     __shared__ PfExpertLds L;
+    // scales and biases [output][group] of the tile's outputs over the whole input range
+    // (dynamic LDS: 2 * 128 * G halves, sized by the host)
+    extern __shared__ uint16_t dyn[];
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
     const int nbn = N / PF_BN, G = Kin >> 6;
     const int total_tiles = p.pf_tile[p.E];
@@ -393,9 +404,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     // this expert's scales and biases for the tile's outputs, every group
     const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G;
     const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G;
+    uint16_t *Ls = dyn, *Lb = dyn + PF_BN * G;
     for (int i = tid; i < PF_BN * G / 8; i += 256) {
-        ((uint4 *)L.s)[i] = *(const uint4 *)(S + 8 * i);
-        ((uint4 *)L.b)[i] = *(const uint4 *)(B + 8 * i);
+        ((uint4 *)Ls)[i] = *(const uint4 *)(S + 8 * i);
+        ((uint4 *)Lb)[i] = *(const uint4 *)(B + 8 * i);
     }
     __syncthreads();
     // copies per step: the picks' inputs (64 x 128 bytes: two 1 KB instructions a wave) and
@@ -422,15 +434,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    issue(0, 0);
+#pragma unroll
+    for (int g = 0; g < PF_NS - 1; ++g)
+        if (g < G) issue(g, g);
     for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < G) {
-            issue(g + 1, buf ^ 1);
-            wait_vm<3>();
-        } else {
-            wait_vm<0>();
-        }
+        const int buf = g % PF_NS;
+        // the buffer of step g + NS - 1 was last read in step g - 1 (closed by its barrier)
+        if (g + PF_NS - 1 < G) issue(g + PF_NS - 1, (g + PF_NS - 1) % PF_NS);
+        wait_steps(G - 1 - g < PF_NS - 1 ? G - 1 - g : PF_NS - 1);
         __syncthreads();
         // the inputs: pairs (x[8c+i], x[8c+i+4]) to match the codes' pairing, and each pick's
         // group sum (this lane's 16 values, then the 4 lanes of the same pick, in a fixed order)
@@ -469,8 +480,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
             float sc[4], cb[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sc[q] = bf2f(L.s[(no + q) * G + g]);
-                cb[q] = __builtin_fmaf(-128.0f, sc[q], bf2f(L.b[(no + q) * G + g]));
+                sc[q] = bf2f(Ls[(no + q) * G + g]);
+                cb[q] = __builtin_fmaf(-128.0f, sc[q], bf2f(Lb[(no + q) * G + g]));
             }
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi) {
