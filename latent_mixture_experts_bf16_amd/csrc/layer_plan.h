@@ -121,6 +121,7 @@ struct LayerParams {
     int32_t *pf_off;       // [E + 1] start of each expert's list
     int32_t *pf_tile;      // [E + 1] first row tile of each expert (tiles of 64 picks)
     int32_t *pf_pairs;     // [rows * K] pick ids (row * K + j), grouped by expert
+    int32_t *pf_tmap;      // [row tiles] (expert << 8) | the tile's place among the expert's
 };
 
 }  // namespace moe

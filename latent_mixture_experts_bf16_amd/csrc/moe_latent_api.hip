@@ -341,11 +341,13 @@ static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_
     const size_t part_shup = SI * p.ks_shup * Rd * 4;
     const size_t part_shdn = SI ? H * p.ks_shdn * Rd * 4 : 0;
     const size_t part_fc2 = L ? H * p.ks_fc2 * Rd * 4 : 0;
-    enum { NREG = 21 };
+    const size_t max_tiles = (R * K + 63) / 64 + (E < R * K ? E : R * K);   // prefill row tiles
+    enum { NREG = 22 };
     const size_t sizes[NREG] = {R * E * 4, R * K * 4, R * K * 4, (size_t)SCH_COUNT * 4, R * (L ? L : 1) * 2,
                                 R * (SI ? SI : 1) * 2, R * K * I * 2, R * K * D * 2, R * D * 2,
                                 R * H * 2, 256, (size_t)*n_ctr * 4, part_fc1, part_shup, part_shdn,
-                                part_fc2, E * 4, R * K * 4, (E + 1) * 4, (E + 1) * 4, R * K * 4};
+                                part_fc2, E * 4, R * K * 4, (E + 1) * 4, (E + 1) * 4, R * K * 4,
+                                max_tiles * 4};
     size_t off[NREG], total = 0;
     for (int i = 0; i < NREG; ++i) { off[i] = total; total += align256(sizes[i]); }
     if (base) {
@@ -370,6 +372,7 @@ static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_
         p.pf_off = (int32_t *)(base + off[18]);
         p.pf_tile = (int32_t *)(base + off[19]);
         p.pf_pairs = (int32_t *)(base + off[20]);
+        p.pf_tmap = (int32_t *)(base + off[21]);
     }
     return total;
 }
@@ -763,28 +766,26 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     hipLaunchKernelGGL(pf_route_kernel, dim3(rows), dim3(WG_THREADS), 0, st, p);
     hipLaunchKernelGGL(pf_sched_kernel, dim3((NP + 1023) / 1024), dim3(WG_THREADS), 0, st, p);
     const int mt = (rows + 127) / 128;
+    // fc1 with the shared up projection in the same launch (a shared expert needs a latent layer)
     if (p.L)
-        hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * (p.L / 128))), dim3(256), 0, st, p, p.x, p.fc1,
-                           p.L, p.H);
-    if (p.SI)
-        hipLaunchKernelGGL(pf_gemm_kernel<1>, dim3(grid8((long)mt * (p.SI / 128))), dim3(256), 0, st, p, p.x, p.su,
-                           p.SI, p.H);
+        hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * ((p.L + p.SI) / 128))), dim3(256), 0, st, p, p.x,
+                           p.fc1, p.L, p.H);
     // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
     const long max_tiles = (NP + 63) / 64 + (E < NP ? E : NP);
-    // dynamic LDS: the tile's scales and biases, 128 outputs x (inputs / 64) groups each (up
-    // to 48 KB beside the kernel's 37 KB; allowed once per process above the default limit)
+    // dynamic LDS: the tile's scales and biases, 256 outputs x (inputs / 64) groups each (up
+    // to 96 KB beside the kernel's LDS; allowed once per process above the default limit)
     static std::once_flag lds_once;
     std::call_once(lds_once, [] {
         (void)hipFuncSetAttribute((const void *)pf_expert_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  96 * 1024);
+                                  128 * 1024);
         (void)hipFuncSetAttribute((const void *)pf_expert_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  96 * 1024);
+                                  128 * 1024);
         (void)hipGetLastError();   // a refusal here only keeps the default limit
     });
-    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(max_tiles * (p.I / 128))), dim3(256),
-                       (unsigned)(2 * 128 * (p.D / 64) * 2), st, p);
-    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * (p.D / 128))), dim3(256),
-                       (unsigned)(2 * 128 * (p.I / 64) * 2), st, p);
+    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(max_tiles * ((p.I + 255) / 256))), dim3(256),
+                       (unsigned)(2 * 256 * (p.D / 64) * 2), st, p);
+    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * ((p.D + 255) / 256))), dim3(256),
+                       (unsigned)(2 * 256 * (p.I / 64) * 2), st, p);
     if (p.SI)
         hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
                            p.H, p.SI);

@@ -14,7 +14,8 @@
 //            expert's list with an atomic counter
 //   sched    prefix sums of the per-expert counts (list starts, row-tile starts) and the
 //            pick ids scattered into the per-expert lists
-//   gemm     fc1 (u = rnd(W1 x)) and shared up (rnd(relu^2(rnd(Su x)))): 128 x 128 tiles
+//   gemm     fc1 (u = rnd(W1 x)) and shared up (rnd(relu^2(rnd(Su x)))) in one launch: 128 x 128
+//            tiles
 //   expert   routed up / down: tiles of 64 picks of one expert x 128 outputs, 4-bit codes
 //            decoded in registers, MFMA per group of 64 inputs, then scale and bias per group
 //   gemm     shared down (rnd(Sd a))
@@ -190,11 +191,15 @@ __global__ void __launch_bounds__(WG_THREADS) pf_sched_kernel(LayerParams p) {
     }
     if (tid == WG_THREADS - 1) { off[E] = sa[tid]; toff[E] = sb[tid]; }
     __syncthreads();
-    if (blockIdx.x == 0)
+    if (blockIdx.x == 0) {
         for (int e = tid; e <= E; e += WG_THREADS) {
             p.pf_off[e] = off[e];
             p.pf_tile[e] = toff[e];
         }
+        // each row tile's expert and its place among that expert's tiles
+        for (int e = tid; e < E; e += WG_THREADS)
+            for (int mt = 0; mt < toff[e + 1] - toff[e]; ++mt) p.pf_tmap[toff[e] + mt] = (e << 8) | mt;
+    }
     const int NP = p.rows * p.K;
     for (int i = blockIdx.x * 1024 + tid; i < NP && i < (blockIdx.x + 1) * 1024; i += WG_THREADS) {
         int e = p.idx[i];
@@ -247,11 +252,21 @@ struct PfGemmLds {
 // (out = rnd(x + rnd(rnd(sum) + sh))).
 template <int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_gemm_kernel(LayerParams p, const uint16_t *__restrict__ X,
-                                                         const uint16_t *__restrict__ W, int N, int K) {
+                                                         const uint16_t *W, int N, int K) {
     __shared__ PfGemmLds L;
-    const int nbn = N / PF_BN, nbm = (p.rows + PF_DM - 1) / PF_DM;
-    const int tile = xcd_tile(nbn * nbm);
+    const int nbm = (p.rows + PF_DM - 1) / PF_DM, t1 = (N / PF_BN) * nbm;
+    // fc1 launches carry the shared up projection too (the same input): its tiles follow
+    const int total = EPI == PF_FC1 && p.SI ? t1 + (p.SI / PF_BN) * nbm : t1;
+    int tile = xcd_tile(total);
     if (tile < 0) return;
+    int epi = EPI;
+    if (EPI == PF_FC1 && tile >= t1) {
+        tile -= t1;
+        W = p.su;
+        N = p.SI;
+        epi = PF_SHUP;
+    }
+    const int nbn = N / PF_BN;
     const int m0 = (tile / nbn) * PF_DM, n0 = (tile % nbn) * PF_BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave & 1, wn = wave >> 1;
@@ -331,11 +346,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = EPI == PF_SHUP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
+                for (int q = 0; q < 4; ++q) o[q] = epi == PF_SHUP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
             }
             const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-            uint16_t *dst = EPI == PF_FC1 ? p.u + (size_t)m * p.L + n
-                          : EPI == PF_SHUP ? p.shact + (size_t)m * p.SI + n
+            uint16_t *dst = epi == PF_FC1 ? p.u + (size_t)m * p.L + n
+                          : epi == PF_SHUP ? p.shact + (size_t)m * p.SI + n
                           : EPI == PF_SHDN ? p.shout + (size_t)m * p.H + n
                                            : p.out + (size_t)m * p.H + n;
             *(uint2 *)dst = ov;
@@ -350,163 +365,172 @@ template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, c
 
 // ------------------------------------------------------------------ routed experts
 
-constexpr int PF_NS = 3;   // input steps (groups) in LDS at once: two copies in flight while one is used
+constexpr int PF_EBN = 256;   // outputs per expert tile (64 per wave)
 
+// NS input steps (groups of 64 inputs) in LDS at once: NS - 1 copies in flight while one
+// is used.
+template <int NS>
 struct PfExpertLds {
-    uint4 a[PF_NS][PF_BM * 8];    // [buffer][pick][8 units]: 64 inputs of each pick's row
-    uint32_t q[PF_NS][PF_BN * 8]; // [buffer][output][8 words]: 64 codes of each output row
-    int pair[PF_BM];
+    uint4 a[NS][PF_BM * 8];        // [buffer][pick][8 units]: 64 inputs of each pick's row, as copied
+    uint32_t q[NS][PF_EBN * 8];    // [buffer][output][8 words]: 64 codes of each output row
+    uint4 ap[PF_BM * 8];           // the step's inputs as pairs (x[i], x[i + 4]) of each 8 (unit c of
+                                   // pick r at swz(r, c))
+    float xs[PF_BM];               // the step's group sum of each pick
+    float sc[PF_EBN], cb[PF_EBN];  // the step's scale and bias - 128 scale of each output
 };
 
-// wait until at most 3 n copy instructions of this wave are outstanding (n = steps still in
-// flight behind the one about to be used)
-__device__ __forceinline__ void wait_steps(int n) {
-    if (n >= 2) wait_vm<6>();
-    else if (n == 1) wait_vm<3>();
-    else wait_vm<0>();
-}
-
-// Tile: picks [m0, m0 + 64) of expert e's list x outputs [n0, n0 + 128) of its up (UP) or
-// down projection, 64 inputs (one group of the 4-bit codes) a step. Per group g and output n
-// the tile forms, per pick, a = sum over the group of (128 + q) x (MFMA: the codes decoded
-// into bf16 128 + q exactly, the inputs reordered to the codes' pairing) and sx = sum of x,
-// and adds scale * a + (bias - 128 scale) * sx -- the group's share of sum(w x) with w =
-// q scale + bias. Wave w holds picks 32 (w & 1) .. +31 and outputs 64 (w >> 1) .. +63. Up:
-// eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum).
+// Tile: picks [m0, m0 + 64) of expert e's list x outputs [n0, n0 + 256) of its up (UP) or
+// down projection, one group of 64 inputs (of the 4-bit codes) a step. Per group g and
+// output n the tile forms, per pick, a = sum over the group of (128 + q) x (MFMA: the codes
+// decoded into bf16 128 + q exactly, the inputs reordered to the codes' pairing) and sx =
+// sum of x, and adds scale * a + (bias - 128 scale) * sx -- the group's share of sum(w x)
+// with w = q scale + bias. A step: its copies wait, then the workgroup reorders the inputs
+// and sums each pick's group once (in a fixed order), then wave w multiplies outputs
+// 64 w .. +63 for all 64 picks (4 x 4 MFMA 16x16 tiles). MFMA step s of a group takes input
+// chunk 2 (l >> 4) + s in lane l's group of 16 -- any order of k serves when both operands
+// use the same. Up: eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum).
 template <bool UP>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) pf_expert_kernel(LayerParams p) {
-    __shared__ PfExpertLds L;
-    // scales and biases [output][group] of the tile's outputs over the whole input range
-    // (dynamic LDS: 2 * 128 * G halves, sized by the host)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_expert_kernel(LayerParams p) {
+    constexpr int NS = UP ? 3 : 2;   // down: two (its scales take twice the LDS)
+    __shared__ PfExpertLds<NS> L;
+    // scales and biases of the tile's outputs, [group][output] (dynamic LDS: 2 * G * 256
+    // halves, sized by the host)
     extern __shared__ uint16_t dyn[];
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
-    const int nbn = N / PF_BN, G = Kin >> 6;
+    const int nbn = (N + PF_EBN - 1) / PF_EBN, G = Kin >> 6;
     const int total_tiles = p.pf_tile[p.E];
     const int lt = xcd_tile(total_tiles * nbn);
     if (lt < 0) return;
-    const int t = lt / nbn, n0 = (lt % nbn) * PF_BN;
-    // the expert of row tile t: the last e with pf_tile[e] <= t
-    int lo = 0, hi = p.E;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.pf_tile[mid] <= t) lo = mid;
-        else hi = mid;
-    }
-    const int e = lo;
+    const int t = lt / nbn, n0 = (lt % nbn) * PF_EBN;
+    const int tcode = p.pf_tmap[t];
+    const int e = tcode >> 8;
     const int list0 = p.pf_off[e], cnt = p.pf_off[e + 1] - list0;
-    const int m0 = (t - p.pf_tile[e]) * PF_BM;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave & 1, wn = wave >> 1;
-    if (tid < PF_BM) {
-        const int m = m0 + tid < cnt ? m0 + tid : cnt - 1;
-        L.pair[tid] = p.pf_pairs[list0 + m];
+    const int m0 = (tcode & 255) * PF_BM;
+    const int tid = threadIdx.x, wn = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
+    auto pick = [&](int m) { return p.pf_pairs[list0 + (m0 + m < cnt ? m0 + m : cnt - 1)]; };
+    auto out_row = [&](int nl) { return n0 + nl < N ? n0 + nl : N - 1; };
+    // scales and biases, transposed to [group][output]
+    const size_t eN = (size_t)e * N;
+    const uint16_t *S = UP ? p.up_s : p.dn_s, *Bs = UP ? p.up_b : p.dn_b;
+    uint16_t *Ls = dyn, *Lb = dyn + PF_EBN * G;
+    for (int i = tid; i < PF_EBN * G; i += 256) {
+        const int nl = i / G, gq = i % G;
+        const size_t off = (eN + out_row(nl)) * G + gq;
+        Ls[gq * PF_EBN + nl] = S[off];
+        Lb[gq * PF_EBN + nl] = Bs[off];
     }
-    // this expert's scales and biases for the tile's outputs, every group
-    const uint16_t *S = (UP ? p.up_s : p.dn_s) + ((size_t)e * N + n0) * G;
-    const uint16_t *B = (UP ? p.up_b : p.dn_b) + ((size_t)e * N + n0) * G;
-    uint16_t *Ls = dyn, *Lb = dyn + PF_BN * G;
-    for (int i = tid; i < PF_BN * G / 8; i += 256) {
-        ((uint4 *)Ls)[i] = *(const uint4 *)(S + 8 * i);
-        ((uint4 *)Lb)[i] = *(const uint4 *)(B + 8 * i);
-    }
-    __syncthreads();
-    // copies per step: the picks' inputs (64 x 128 bytes: two 1 KB instructions a wave) and
-    // the codes (128 x 32 bytes: one a wave)
+    // copies per step: the picks' inputs (64 x 128 bytes: two 1 KB instructions a wave, unit
+    // u = 128 w + 64 i + l is chunk u & 7 of pick row u >> 3) and the codes (256 x 32 bytes: two
+    // a wave, unit u is half u & 1 of output row u >> 1)
     const uint16_t *xsrc[2];
-    int du[2];
+    const uint32_t *qsrc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int u = 128 * wave + 64 * i + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
-        const int pr = L.pair[row];
-        xsrc[i] = (UP ? (p.L ? p.u : p.x) + (size_t)(pr / p.K) * Kin : p.eact + (size_t)pr * Kin) + 8 * c;
-        du[i] = 128 * wave + 64 * i;
+        const int u = 128 * wn + 64 * i + lane;
+        const int pr = pick(u >> 3);
+        xsrc[i] = (UP ? (p.L ? p.u : p.x) + (size_t)(pr / p.K) * Kin : p.eact + (size_t)pr * Kin) + 8 * (u & 7);
+        qsrc[i] = (UP ? p.up_q : p.dn_q) + (eN + out_row(u >> 1)) * (Kin >> 3) + 4 * (u & 1);
     }
-    const uint32_t *qsrc = (UP ? p.up_q : p.dn_q) + ((size_t)e * N + n0 + ((64 * wave + lane) >> 1)) * (Kin >> 3) +
-                           4 * (lane & 1);
-    const int qdu = 64 * wave;   // 16-byte unit of the copy (output row (64 w + l) >> 1, half l & 1)
-    auto issue = [&](int ks, int buf) {
+    auto issue = [&](int g, int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + 64 * ks, &L.a[buf][du[i]]);
-        lds_dma16(qsrc + 8 * ks, &((uint4 *)L.q[buf])[qdu]);
+        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + 64 * g, &L.a[buf][128 * wn + 64 * i]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lds_dma16(qsrc[i] + 8 * g, &((uint4 *)L.q[buf])[128 * wn + 64 * i]);
     };
-    f32x4 acc[4][2];
+    const bool active = n0 + 64 * wn < N;   // the wave has outputs in this tile
+    f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < PF_NS - 1; ++g)
-        if (g < G) issue(g, g);
+    for (int j = 0; j < NS - 1; ++j)
+        if (j < G) issue(j, j);
     for (int g = 0; g < G; ++g) {
-        const int buf = g % PF_NS;
-        // the buffer of step g + NS - 1 was last read in step g - 1 (closed by its barrier)
-        if (g + PF_NS - 1 < G) issue(g + PF_NS - 1, (g + PF_NS - 1) % PF_NS);
-        wait_steps(G - 1 - g < PF_NS - 1 ? G - 1 - g : PF_NS - 1);
-        __syncthreads();
-        // the inputs: pairs (x[8c+i], x[8c+i+4]) to match the codes' pairing, and each pick's
-        // group sum (this lane's 16 values, then the 4 lanes of the same pick, in a fixed order)
-        uint4 xf[2][2];
-        float sx[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-            sx[mi] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint4 v = lds_ld16(&L.a[buf][swz(wm * 32 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
-                xf[mi][s].x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-                xf[mi][s].y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-                xf[mi][s].z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-                xf[mi][s].w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-                sx[mi] = dot2<false>(0x3F803F80u, v.x, sx[mi]);
-                sx[mi] = dot2<false>(0x3F803F80u, v.y, sx[mi]);
-                sx[mi] = dot2<false>(0x3F803F80u, v.z, sx[mi]);
-                sx[mi] = dot2<false>(0x3F803F80u, v.w, sx[mi]);
-            }
-            sx[mi] = sx[mi] + __shfl_xor(sx[mi], 16, 64);
-            sx[mi] = sx[mi] + __shfl_xor(sx[mi], 32, 64);
+        const int buf = g % NS;
+        // the steps issued after g may stay in flight (4 copy instructions each)
+        const int behind = G - 1 - g < NS - 2 ? G - 1 - g : NS - 2;
+        if (behind >= 1) wait_vm<4>();
+        else wait_vm<0>();
+        __syncthreads();   // step g is in LDS; every wave is done with step g - 1
+        if (g + NS - 1 < G) issue(g + NS - 1, (g + NS - 1) % NS);
+        {
+            // thread t: 16 inputs (units 2 (t & 3), +1) of pick t >> 2
+            const int r = tid >> 2, part = tid & 3;
+            const uint4 v0 = lds_ld16(&L.a[buf][r * 8 + 2 * part]), v1 = lds_ld16(&L.a[buf][r * 8 + 2 * part + 1]);
+            float sx = 0.0f;
+            sx = dot2<false>(0x3F803F80u, v0.x, sx);
+            sx = dot2<false>(0x3F803F80u, v0.y, sx);
+            sx = dot2<false>(0x3F803F80u, v0.z, sx);
+            sx = dot2<false>(0x3F803F80u, v0.w, sx);
+            sx = dot2<false>(0x3F803F80u, v1.x, sx);
+            sx = dot2<false>(0x3F803F80u, v1.y, sx);
+            sx = dot2<false>(0x3F803F80u, v1.z, sx);
+            sx = dot2<false>(0x3F803F80u, v1.w, sx);
+            sx = sx + __shfl_xor(sx, 1, 64);
+            sx = sx + __shfl_xor(sx, 2, 64);
+            const uint4 p0 = {__builtin_amdgcn_perm(v0.z, v0.x, 0x05040100u), __builtin_amdgcn_perm(v0.z, v0.x, 0x07060302u),
+                              __builtin_amdgcn_perm(v0.w, v0.y, 0x05040100u), __builtin_amdgcn_perm(v0.w, v0.y, 0x07060302u)};
+            const uint4 p1 = {__builtin_amdgcn_perm(v1.z, v1.x, 0x05040100u), __builtin_amdgcn_perm(v1.z, v1.x, 0x07060302u),
+                              __builtin_amdgcn_perm(v1.w, v1.y, 0x05040100u), __builtin_amdgcn_perm(v1.w, v1.y, 0x07060302u)};
+            lds_st16(&L.ap[swz(r, 2 * part)], p0);
+            lds_st16(&L.ap[swz(r, 2 * part + 1)], p1);
+            if (part == 0) L.xs[r] = sx;
+            // thread t: output t's scale and bias for this group
+            const float sct = bf2f(Ls[g * PF_EBN + tid]);
+            L.sc[tid] = sct;
+            L.cb[tid] = __builtin_fmaf(-128.0f, sct, bf2f(Lb[g * PF_EBN + tid]));
         }
+        __syncthreads();
+        if (active) {
+            uint4 xf[4][2];
+            float sxm[4];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int nl = wn * 64 + ni * 16 + (lane & 15);   // the code row this lane decodes
-            uint4 wf[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const uint32_t w = L.q[buf][nl * 8 + 4 * s + (lane >> 4)];
-                wf[s] = make_uint4(code_pair<false>(w, 0), code_pair<false>(w, 1), code_pair<false>(w, 2),
-                                   code_pair<false>(w, 3));
-            }
-            // scale and bias of the 4 outputs this lane ends with
-            const int no = wn * 64 + ni * 16 + 4 * (lane >> 4);
-            float sc[4], cb[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sc[q] = bf2f(Ls[(no + q) * G + g]);
-                cb[q] = __builtin_fmaf(-128.0f, sc[q], bf2f(Lb[(no + q) * G + g]));
+            for (int mi = 0; mi < 4; ++mi) {
+                xf[mi][0] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg)]);
+                xf[mi][1] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg + 1)]);
+                sxm[mi] = L.xs[16 * mi + lr];
             }
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
-                f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[0]),
-                                                            __builtin_bit_cast(bf16x8, xf[mi][0]), a, 0, 0, 0);
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[1]),
-                                                            __builtin_bit_cast(bf16x8, xf[mi][1]), a, 0, 0, 0);
+            for (int ni = 0; ni < 4; ++ni) {
+                const int nl = 64 * wn + 16 * ni;
+                const uint2 w = *(const uint2 *)&L.q[buf][(nl + lr) * 8 + 2 * lg];
+                const uint4 wf0 = make_uint4(code_pair<false>(w.x, 0), code_pair<false>(w.x, 1),
+                                             code_pair<false>(w.x, 2), code_pair<false>(w.x, 3));
+                const uint4 wf1 = make_uint4(code_pair<false>(w.y, 0), code_pair<false>(w.y, 1),
+                                             code_pair<false>(w.y, 2), code_pair<false>(w.y, 3));
+                // the 4 pick tiles' products first (independent), then their scaling
+                f32x4 a[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float v = __builtin_fmaf(sc[q], a[q], acc[ni][mi][q]);
-                    acc[ni][mi][q] = __builtin_fmaf(cb[q], sx[mi], v);
+                for (int mi = 0; mi < 4; ++mi) {
+                    a[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf0),
+                                                                    __builtin_bit_cast(bf16x8, xf[mi][0]),
+                                                                    (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    a[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf1),
+                                                                    __builtin_bit_cast(bf16x8, xf[mi][1]), a[mi], 0, 0, 0);
                 }
+                // scale and bias - 128 scale of the 4 outputs this lane ends with
+                const f32x4 sc = *(const f32x4 *)&L.sc[nl + 4 * lg];
+                const f32x4 cb = *(const f32x4 *)&L.cb[nl + 4 * lg];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float v = __builtin_fmaf(sc[q], a[mi][q], acc[ni][mi][q]);
+                        acc[ni][mi][q] = __builtin_fmaf(cb[q], sxm[mi], v);
+                    }
             }
         }
-        __syncthreads();
     }
+    if (!active) return;
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-        const int ml = wm * 32 + mi * 16 + (lane & 15);
-        if (m0 + ml >= cnt) continue;
-        const int pr = L.pair[ml];
+    for (int mi = 0; mi < 4; ++mi) {
+        const int m = 16 * mi + lr;
+        if (m0 + m >= cnt) continue;
+        const int pr = pick(m);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-            const int n = n0 + wn * 64 + ni * 16 + 4 * (lane >> 4);
+            const int n = n0 + 64 * wn + 16 * ni + 4 * lg;
             const f32x4 v = acc[ni][mi];
             uint16_t o[4];
 #pragma unroll
