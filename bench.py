@@ -723,9 +723,13 @@ def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):
     """Mean duration (us) of each launch group inside full forwards: forwards enqueued eagerly,
     `sweeps` sweeps over the instances between synchronizations, each launch's kernel start and
     end recorded by its own dispatch; the first forward after each synchronization and the
-    first two rounds are left out."""
+    first two rounds are left out. Each round first queues about 1.5 ms of streaming reads, so
+    that the host has enqueued every forward before the first one starts and they run back to
+    back, as in a replayed graph, whatever the host's launch rate."""
     import numpy as np
     import torch
+    busy = torch.ones(1 << 26, dtype=torch.int32, device="cuda")   # 256 MiB
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     nf = sweeps * len(layers)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * ng)] for _ in range(nf)]
     with torch.cuda.stream(s):
@@ -737,6 +741,8 @@ def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):
     acc, n = np.zeros(ng), 0
     with torch.cuda.stream(s):
         for r in range(rounds + 2):
+            for _ in range(40):
+                B.moe_latent_stream_read(busy.data_ptr(), busy.numel() * 4, sink.data_ptr(), s.cuda_stream)
             for f in range(nf):
                 i = f % len(layers)
                 B.moe_latent_forward_timed(layers[i].handle, rows, xs[i].data_ptr(), outs[i].data_ptr(), handles[f])
@@ -747,6 +753,7 @@ def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):
                 for g in range(ng):
                     acc[g] += evs[f][2 * g].elapsed_time(evs[f][2 * g + 1]) * 1e3
                 n += 1
+    del busy, sink
     return acc / n
 
 
