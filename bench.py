@@ -65,11 +65,18 @@ def plan_groups(B, handle, dims, rows):
         if n <= 0:
             break
         stages = STAGE_KEYS[f:l + 1]
-        if rows == 1 and f == 0:
-            stages = stages + ["route"]           # the one-row route item rides in the gate launch
         name = "+".join(stages) + (" [side stream]" if side else "")
         out.append({"group": g, "name": name, "stages": stages, "side": side, "items": n,
-                    "kernel": kernel_of(f, l, wide, qb)})
+                    "kernel": kernel_of(f, l, wide, qb), "first": f, "last": l})
+    # the route items end the gate launch (the library's logit hand-off): the route stage of
+    # any later launch range holds no items
+    if out:
+        for o in out:
+            if "route" in o["stages"]:
+                o["stages"] = [st for st in o["stages"] if st != "route"]
+                o["name"] = "+".join(o["stages"]) + (" [side stream]" if o["side"] else "")
+        out[0]["stages"] = out[0]["stages"] + ["route"]
+        out[0]["name"] = out[0]["name"] + "+route"
     return out
 
 

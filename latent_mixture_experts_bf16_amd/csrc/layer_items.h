@@ -176,20 +176,21 @@ __device__ __forceinline__ bool last_arriver(uint32_t *c, uint32_t target, int *
 
 // ------------------------------------------------------------------ gate
 
-// The handoff word of expert e of a one-row pass (see LayerParams::ctr_hand).
-__device__ __forceinline__ uint64_t *hand_word(const LayerParams &p, int e) {
-    return (uint64_t *)(p.ctr + p.ctr_hand) + e;
+// The handoff word of logit (r, e) (see LayerParams::ctr_hand).
+__device__ __forceinline__ uint64_t *hand_word(const LayerParams &p, int r, int e) {
+    return (uint64_t *)(p.ctr + p.ctr_hand) + (size_t)r * p.E + e;
 }
 
-// Store logit (r, e) (raw bits: bf16, or fp32 for the fp32 router). A multi-row pass writes it
-// through for the route items of the next launch; a one-row pass hands it to the route item
-// of this launch in one 64-bit store (value and presence bit together, so the route item
-// never sees one without the other) and keeps a plain copy for the stage readback.
+// Store logit (r, e) (raw bits: bf16, or fp32 for the fp32 router). When the route items run
+// in the gate launch (p.hand), the logit is handed to them in one 64-bit store (value and
+// presence bit together, so a route item never sees one without the other) and a plain copy
+// is kept for the stage readback; otherwise it is written through for the route items of the
+// next launch.
 __device__ __forceinline__ void put_logit(const LayerParams &p, int r, int e, uint32_t bits) {
-    if (p.single_row) {
-        __hip_atomic_store(hand_word(p, e), (1ull << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.router_f32) ((uint32_t *)p.logits)[e] = bits;
-        else ((uint16_t *)p.logits)[e] = (uint16_t)bits;
+    if (p.hand) {
+        __hip_atomic_store(hand_word(p, r, e), (1ull << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.router_f32) ((uint32_t *)p.logits)[(size_t)r * p.E + e] = bits;
+        else ((uint16_t *)p.logits)[(size_t)r * p.E + e] = (uint16_t)bits;
     } else if (p.router_f32) {
         st_shared32((int32_t *)p.logits + (size_t)r * p.E + e, (int32_t)bits);
     } else {
@@ -404,23 +405,24 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
         // both loads are issued before either value is used
         const float bias = p.has_bias ? p.bias[e] : 0.0f;
         uint32_t raw;
-        if (p.single_row) {
-            // the gate items of this launch hand the logits over: poll the expert's word
-            // (read around the caches) until it is present, for at most wait_ticks (then
-            // error bit 8), and clear it for the next forward
-            uint64_t v = __hip_atomic_load(hand_word(p, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.hand) {
+            // the gate items of this launch hand the logits over: poll the word (read around
+            // the caches) until it is present, for at most wait_ticks (then error bit 8), and
+            // clear it for the next forward
+            uint64_t *hw = hand_word(p, r, e);
+            uint64_t v = __hip_atomic_load(hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (!(v >> 32)) {
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
                 do {
                     __builtin_amdgcn_s_sleep(1);
-                    v = __hip_atomic_load(hand_word(p, e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v = __hip_atomic_load(hw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (!(v >> 32) && __builtin_amdgcn_s_memrealtime() - t0 > (uint64_t)p.wait_ticks) {
                         atomicOr(p.err, 8u);
                         break;
                     }
                 } while (!(v >> 32));
             }
-            __hip_atomic_store(hand_word(p, e), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(hw, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             raw = (uint32_t)v;
         } else {
             raw = p.router_f32 ? (uint32_t)ld_shared32((const int32_t *)p.logits + (size_t)r * E + e)

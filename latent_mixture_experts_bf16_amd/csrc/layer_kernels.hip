@@ -24,7 +24,7 @@ struct StageLds {
         typename std::conditional<dense, DenseLds<NW>, NoLds>::type dense;
         typename std::conditional<has(ST_GATE) || has(ST_ROUTE), RouteLds<WG_THREADS>, NoLds>::type route;
         typename std::conditional<has(ST_GATE), GateLds, NoLds>::type gate;
-        typename std::conditional<has(ST_ROUTE), SchedLds, NoLds>::type sched;
+        typename std::conditional<has(ST_GATE) || has(ST_ROUTE), SchedLds, NoLds>::type sched;
         typename std::conditional<has(ST_UP) || has(ST_DOWN), ExpertLds<XMAX_OF(WIDE)>, NoLds>::type ex;
     };
 };
@@ -34,11 +34,18 @@ struct StageLds {
 template <int S, bool WIDE, int QB, class LdsT>
 __device__ __forceinline__ void run_stage(const LayerParams &p, int local, LdsT &lds, int *s_flag) {
     if constexpr (S == ST_GATE) {
-        // a one-row pass: the last item routes the row with the logits the gate items (all
-        // dispatched before it) hand it
-        const int ngate = p.item_base[ST_GATE + 1] - p.item_base[ST_GATE] - (p.single_row ? 1 : 0);
-        if (p.single_row && local == ngate) route_item<WG_THREADS>(p, 0, lds.route);
-        else gate_item<NW>(p, local, lds.gate);
+        // with the hand-off, the last `rows` items route the rows with the logits the gate
+        // items (all dispatched before them) hand them; the last of them builds the schedule
+        const int ngate = p.item_base[ST_GATE + 1] - p.item_base[ST_GATE] - (p.hand ? p.rows : 0);
+        if (local >= ngate) {
+            route_item<WG_THREADS>(p, local - ngate, lds.route);
+            if (!p.single_row && last_arriver(p.ctr + CTR_ROUTE, (uint32_t)p.rows, s_flag)) {
+                __syncthreads();
+                sched_item(p, lds.sched);
+            }
+        } else {
+            gate_item<NW>(p, local, lds.gate);
+        }
     } else if constexpr (S == ST_FC1) {
         const int ks = p.ks_fc1;
         dense_item<EPI_FC1, NW>(p, p.fc1, p.x, p.H, local / ks, local % ks, ks, p.part_fc1, p.ctr + p.ctr_fc1,

@@ -9,15 +9,17 @@ namespace moe {
 // it»: gate gemv -> route -> fc1_latent_proj -> routed experts -> combine -> fc2_latent_proj
 // -> + shared -> + residual). A stage only reads what earlier launches wrote, or what a
 // "last arriver" of the same launch reads after every item it depends on has counted itself
-// done. One item waits: the route item of a one-row pass, for the logits of the gate items
-// dispatched before it (bounded; see ctr_hand).
+// done. Only the route items wait: for the logits of the gate items dispatched before them
+// in the same launch (bounded; see ctr_hand).
 enum Stage : int {
-    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; a one-row pass
-                   // has one more item, last: the route item, which waits for the logits
+    ST_GATE = 0,   // gate logits, one wave per expert, fixed 64-lane order; with the logit
+                   // hand-off (LayerParams::hand) the last `rows` items are the route items,
+                   // which wait for their row's logits
     ST_FC1,        // u = rnd(W1 . x), 16 outputs per item (MFMA)
     ST_SHUP,       // shared expert up + relu^2, 16 outputs per item
-    ST_ROUTE,      // multi-row passes: one row per item; the last route item to finish builds
-                   // the schedule (distinct experts and their (row, pick) lists)
+    ST_ROUTE,      // without the hand-off: one row per item; in either place, the last route item
+                   // of a multi-row pass builds the schedule (distinct experts and their (row,
+                   // pick) lists)
     ST_SHDN_A,     // shared expert down, first half of the outputs
     ST_UP,         // routed expert up + relu^2: (slot, block of outputs) per item
     ST_SHDN_B,     // shared expert down, second half of the outputs
@@ -106,9 +108,11 @@ struct LayerParams {
     int single_row;        // rows == 1: the route item (first gate item) routes and writes the schedule
     int gate_rc;           // rows of one gate item (the whole pass unless its rows are staged)
     int inline_comb;       // one-row latent pass: fc2 items compute the combine themselves
-    // one-row pass: each gate item hands its logits to the route item (the last item of the
-    // gate stage) through 64-bit words [E] in the counter block at ctr_hand (bit 32: present),
-    // which the route item polls for at most wait_ticks ticks of the 100 MHz real-time counter
+    // hand != 0: the route items run in the gate launch, after its gate items (the last
+    // `rows` items of the gate stage); each gate item hands its logits to them through 64-bit
+    // words [rows][E] in the counter block at ctr_hand (bit 32: present), which a route item
+    // polls for at most wait_ticks ticks of the 100 MHz real-time counter
+    int hand;
     int ctr_hand;
     uint32_t wait_ticks;
     // the lm_head gemv (a separate entry point sharing the dense tiles): out [rows][lm_n],
