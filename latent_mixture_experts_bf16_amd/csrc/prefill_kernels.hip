@@ -495,10 +495,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
             for (int ni = 0; ni < 4; ++ni) {
                 const int nl = 64 * wn + 16 * ni;
                 const uint2 w = *(const uint2 *)&L.q[buf][(nl + lr) * 8 + 2 * lg];
-                const uint4 wf0 = make_uint4(code_pair<false>(w.x, 0), code_pair<false>(w.x, 1),
-                                             code_pair<false>(w.x, 2), code_pair<false>(w.x, 3));
-                const uint4 wf1 = make_uint4(code_pair<false>(w.y, 0), code_pair<false>(w.y, 1),
-                                             code_pair<false>(w.y, 2), code_pair<false>(w.y, 3));
+                uint32_t c0[4], c1[4];
+                code_pairs<false>(w.x, c0);
+                code_pairs<false>(w.y, c1);
+                const uint4 wf0 = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+                const uint4 wf1 = make_uint4(c1[0], c1[1], c1[2], c1[3]);
                 // the 4 pick tiles' products first (independent), then their scaling
                 f32x4 a[4];
 #pragma unroll
