@@ -510,7 +510,7 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 // launch first waits for the side stream's work of this forward.
 enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B };
 struct Launch {
-    int first, last, kernel, split, pre, side, join;
+    int first, last, kernel, split, pre, side, join, fork;
 };
 constexpr int MAX_LAUNCHES = 10;
 
@@ -526,18 +526,21 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
     // (the side stream's fork and join cost more than the overlap saves in so short a pass);
     // the 64-row stack 361 us per layer against 394, the 16-row pass 149 against 151.
     if (variant == 3) variant = p.single_row ? 1 : 2;
-    auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0) {
-        out[n++] = Launch{f, l, k, split, pre, side, join};
+    auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0, int fork = 0) {
+        out[n++] = Launch{f, l, k, split, pre, side, join, fork};
     };
     if (variant == 2) {
-        add(ST_GATE, ST_FC1, K_GATE_SHUP);   // one row: the route item last of the gate items
+        // the side stream forks after the gate launch, but the routed chain's expert up launch
+        // is enqueued (and so captured) before the side launches, so that it is dispatched
+        // first when both become ready
+        add(ST_GATE, ST_FC1, K_GATE_SHUP, -1, 0, 0, 0, p.SI ? 1 : 0);   // the route items end the gate stage
+        if (!p.hand) add(ST_ROUTE, ST_ROUTE, K_ROUTE_UP);
+        add(ST_UP, ST_UP, K_ROUTE_UP);
         if (p.SI) {
             add(ST_SHUP, ST_SHUP, K_SHUP, -1, 0, 1);
             add(ST_SHDN_A, ST_SHDN_A, K_SHDN_A, -1, 0, 1);
             add(ST_SHDN_B, ST_SHDN_B, K_SHDN_B, -1, 0, 1);
         }
-        if (!p.hand) add(ST_ROUTE, ST_ROUTE, K_ROUTE_UP);   // else the route items end the gate stage
-        add(ST_UP, ST_UP, K_ROUTE_UP);
         add(ST_DOWN, ST_DOWN, K_UP_DOWN);
         if (p.L) add(ST_FC2, ST_FC2, K_FC2, -1, 0, 0, p.SI ? 1 : 0);
         return n;
@@ -627,14 +630,14 @@ static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hi
 static void enqueue(const moe_latent *h, const LayerParams &p, int g, void *const *evs = nullptr) {
     Launch ls[MAX_LAUNCHES];
     const int n = plan_launches(p, h->cus, h->variant, ls);
-    bool forked = false, joined = false;
+    bool forked = false, fork_recorded = false, joined = false;
     for (int i = 0; i < n; ++i) {
         if (g != -1 && g != i) continue;
         const Launch &l = ls[i];
         hipStream_t st = h->stream;
         if (g == -1 && l.side) {
             if (!forked) {
-                (void)hipEventRecord(h->ev_fork, h->stream);
+                if (!fork_recorded) (void)hipEventRecord(h->ev_fork, h->stream);
                 (void)hipStreamWaitEvent(h->side, h->ev_fork, 0);
                 forked = true;
             }
@@ -646,6 +649,10 @@ static void enqueue(const moe_latent *h, const LayerParams &p, int g, void *cons
             joined = true;
         }
         launch_one(p, l, st, evs ? (hipEvent_t)evs[2 * i] : nullptr, evs ? (hipEvent_t)evs[2 * i + 1] : nullptr);
+        if (g == -1 && l.fork) {   // the side stream starts after this launch
+            (void)hipEventRecord(h->ev_fork, h->stream);
+            fork_recorded = true;
+        }
     }
     if (forked && !joined) {
         (void)hipEventRecord(h->ev_join, h->side);

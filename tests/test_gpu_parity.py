@@ -358,9 +358,9 @@ def test_timed_forward_equals_forward_and_records_each_launch():
     assert ng == 4      # one row, one stream: gate + fc1 + shared up, up, down, fc2
     B.moe_latent_set_variant(lay.handle, 2)
     ng2 = sum(1 for g in range(10) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
-    assert ng2 == 7     # two streams: gate + fc1, shared up, shared down x 2, expert up, down, fc2
+    assert ng2 == 7     # two streams: gate + fc1, expert up, shared up, shared down x 2, down, fc2
     sides = [B.moe_latent_group_stages(lay.handle, 1, g)[3] for g in range(ng2)]
-    assert sides == [0, 1, 1, 1, 0, 0, 0]
+    assert sides == [0, 0, 1, 1, 1, 0, 0]
     evs2 = [torch.cuda.Event(enable_timing=True) for _ in range(2 * ng2)]
     for e in evs2:
         e.record()
