@@ -228,3 +228,40 @@ def test_prefill_4096_rows_bolt():
     d, arrays = next(synth.workload_layers(1, rows=rows))
     sample = sorted(set(np.random.default_rng(11).choice(rows, 62, replace=False).tolist()) | {0, rows - 1})
     _check_layer(d, arrays, "bolt 4096", sample=sample, alone=(0, 4095))
+
+
+@pytest.mark.parametrize("rows", [70, 300])
+def test_prefill_graph_replays_match_eager(rows):
+    """A prefill captured in a HIP graph gives the eager bits on every replay, with eager work
+    (a prefill of other rows and a decode pass) between the replays; the per-expert counts
+    are cleared by a kernel, not a memset node."""
+    B, LY = _B(), _LY()
+    arrays = synth.make_layer(TINY, rows, weight_seed=9700, input_seed=9701 + rows)
+    lay = LY.DeviceLayer(TINY, arrays, rows)
+    xd = LY.to_device(arrays["x"])
+    eager = torch.empty_like(xd)
+    lay.prefill(xd, eager, rows)
+    torch.cuda.synchronize()
+    ref = eager.cpu().numpy()
+    s = torch.cuda.Stream()
+    B.moe_latent_set_stream(lay.handle, s.cuda_stream)
+    out = torch.empty_like(xd)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        lay.prefill(xd, out, rows)      # warm-up on the capture stream
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            lay.prefill(xd, out, rows)
+    x_other = xd[5:40].contiguous()
+    other = torch.empty_like(x_other)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), i
+        with torch.cuda.stream(s):
+            lay.prefill(x_other, other, 35)
+            lay.forward(x_other[:3], other[:3], 3)
+        torch.cuda.synchronize()
+    lay.status()
+    lay.close()
