@@ -39,26 +39,9 @@ KERNEL_SOURCES = ["latent_mixture_experts_bf16_amd/csrc/layer_kernels.hip",
 COPY_MIB = 512   # size of the calibration copy (int32 negation: reads and writes COPY_MIB MiB)
 
 
-def kernel_of(first, last, wide, qb=0):
-    """The kernel instance (as rocprofv3 names it: first and last stage of its template, wide
-    expert variant, expert code width or 0 for the fused 4-bit items) that runs a launch of
-    stages [first, last] (moe_latent_api.hip, launch_one)."""
-    w = "true" if wide else "false"
-    if last <= 2 and first == 0:
-        return "moe_stage_kernel<0, 2, false, 0>"
-    if first == last and first in (2, 4, 6, 8):
-        return f"moe_stage_kernel<{first}, {last}, false, 0>"
-    if 3 <= first and last <= 5:
-        return f"moe_stage_kernel<3, 5, {w}, {qb}>"
-    return f"moe_stage_kernel<5, 7, {w}, {qb}>"
-
-
 def plan_groups(B, handle, dims, rows):
     """The launch groups of a pass, from the library's plan: index, name, stages (stage_bytes
     keys), side stream, workgroups, kernel name."""
-    D = dims.latent or dims.hidden
-    wide = D > 2048 or dims.expert_inter > 2048
-    qb = 0 if (dims.quant_bits, dims.group_size) == (4, 64) else dims.quant_bits
     out = []
     for g in range(16):
         n, f, l, side = B.moe_latent_group_stages(handle, rows, g)
@@ -67,7 +50,7 @@ def plan_groups(B, handle, dims, rows):
         stages = STAGE_KEYS[f:l + 1]
         name = "+".join(stages) + (" [side stream]" if side else "")
         out.append({"group": g, "name": name, "stages": stages, "side": side, "items": n,
-                    "kernel": kernel_of(f, l, wide, qb), "first": f, "last": l})
+                    "kernel": B.moe_latent_group_kernel(handle, rows, g), "first": f, "last": l})
     # the route items end the gate launch (the library's logit hand-off): the route stage of
     # any later launch range holds no items
     if out:
@@ -141,9 +124,17 @@ def _csv_rows(folder, name):
     return rows
 
 
-def _short(kernel_name):
+def _layer_kernel(kernel_name):
+    """A layer kernel's name as the library reports it (moe_latent_group_kernel), or None."""
     if "moe_stage_kernel<" in kernel_name:
         return "moe_stage_kernel<" + kernel_name.split("moe_stage_kernel<")[1].split(">")[0] + ">"
+    return "moe_front_kernel" if "moe_front_kernel" in kernel_name else None
+
+
+def _short(kernel_name):
+    k = _layer_kernel(kernel_name)
+    if k is not None:
+        return k
     return "copy" if "elementwise" in kernel_name else None
 
 
@@ -191,11 +182,11 @@ def summarize_stats(args):
     split = {}
     for i in range(1, len(disp)):
         st, en, name = disp[i]
-        if "moe_stage_kernel" not in name:
+        if _layer_kernel(name) is None:
             continue
         key = (name, "inside forwards" if disp[i - 1][2] != name else "after itself")
         split.setdefault(key, []).append((en - st) / 1e3)
-    lines += ["", "by the dispatch before (moe_stage_kernel only)", f"{'kernel':70s} {'context':>16s} {'calls':>7s} {'avg_us':>9s}"]
+    lines += ["", "by the dispatch before (layer kernels only)", f"{'kernel':70s} {'context':>16s} {'calls':>7s} {'avg_us':>9s}"]
     for (name, ctx), v in sorted(split.items()):
         lines.append(f"{name[:70]:70s} {ctx:>16s} {len(v):7d} {sum(v) / len(v):9.3f}")
     txt = "\n".join(lines) + "\n"
@@ -649,10 +640,9 @@ def summarize_mfma(args):
     rows = _csv_rows(args.summarize_mfma, "counter_collection.csv")
     per = {}
     for r in rows:
-        name = r.get("Kernel_Name", "")
-        if "moe_stage_kernel" not in name:
+        k = _layer_kernel(r.get("Kernel_Name", ""))
+        if k is None:
             continue
-        k = "moe_stage_kernel<" + name.split("moe_stage_kernel<")[1].split(">")[0] + ">"
         per.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     out = {}
     for (k, c), v in sorted(per.items()):

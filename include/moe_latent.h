@@ -212,6 +212,13 @@ int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t group);
 int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t group, int32_t *first_stage,
                             int32_t *last_stage, int32_t *side);
 
+/* The name of the kernel launch group `group` runs for a pass of `rows` rows, as a profiler
+ * lists it without namespace and arguments (e.g. "moe_front_kernel", "moe_stage_kernel<3, 5,
+ * false, 0>"), written NUL-terminated into name (at most cap bytes, cut to fit); for matching
+ * per-launch measurements with profiler records. Returns its length, 0 (empty name) when
+ * there is no such group, or -1 for an invalid handle, rows, name or cap. */
+int moe_latent_group_kernel(moe_latent_t *h, int32_t rows, int32_t group, char *name, int32_t cap);
+
 /* A forward like moe_latent_forward, whose launch i (launch group i) also records the start
  * and the end of its own kernel into events[2 i] and events[2 i + 1] (hipEvent_t handles the
  * caller created with timing enabled; the timestamps come from the kernel's dispatch itself,
@@ -230,7 +237,10 @@ int moe_latent_set_stream(moe_latent_t *h, void *hip_stream);
  * and the shared expert on the handle's side stream, in parallel; 1: one chain of launches on
  * the handle's stream, the shared expert's workgroups filling its launches; 3 (the default):
  * variant 1 for a one-row pass and variant 2 for more rows (the side stream's fork and join
- * cost more than they save in a one-row pass). All give the same bits. 0 (one fused launch per forward, a dependency-ordered work queue)
+ * cost more than they save in a one-row pass); 4: variant 1, but the first launch of a one-row
+ * pass as work items of the stage kernel (gate, route, fc1 and shared up items) instead of the
+ * front kernel (fc1 and shared up in slices spread evenly over the compute units, the gate
+ * rows and the route beside them). All give the same bits. 0 (one fused launch per forward, a dependency-ordered work queue)
  * is reserved and refused with MOE_ERR_INVALID_ARG: its first GPU run did not complete, and
  * it is not built. Synchronises the handle's stream first. */
 int moe_latent_set_variant(moe_latent_t *h, int32_t variant);

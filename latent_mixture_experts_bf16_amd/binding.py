@@ -83,6 +83,8 @@ def _load():
         "moe_latent_launch_group": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.c_int32]),
         "moe_latent_group_items": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32]),
         "moe_latent_group_stages": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P, P]),
+        "moe_latent_group_kernel": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_char_p,
+                                                   ctypes.c_int32]),
         "moe_latent_forward_timed": (ctypes.c_int, [P, ctypes.c_int32, P, P, ctypes.POINTER(P), ctypes.c_int32]),
         "moe_latent_stream_read": (ctypes.c_int, [P, ctypes.c_size_t, P, P]),
         "moe_lm_head_gemv": (ctypes.c_int, [ctypes.POINTER(moe_tensor), ctypes.c_int32, P, P, ctypes.c_int32, P]),
@@ -103,7 +105,7 @@ EXPORTED = ("moe_latent_create", "moe_latent_forward", "moe_latent_destroy", "mo
             "moe_latent_status", "moe_latent_last_error", "moe_latent_live_allocations",
             "moe_latent_launch_group", "moe_latent_group_items", "moe_latent_forward_timed",
             "moe_latent_stream_read", "moe_latent_forward_static", "moe_latent_group_stages",
-            "moe_lm_head_gemv", "moe_latent_prefill")
+            "moe_lm_head_gemv", "moe_latent_prefill", "moe_latent_group_kernel")
 
 
 def lib():
@@ -208,6 +210,16 @@ def moe_latent_group_stages(h: int, rows: int, group: int):
     f, l, sd = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     n = _lib.moe_latent_group_stages(h, rows, group, ctypes.byref(f), ctypes.byref(l), ctypes.byref(sd))
     return n, f.value, l.value, sd.value
+
+
+def moe_latent_group_kernel(h: int, rows: int, group: int) -> str:
+    """The kernel launch group `group` runs (its name as a profiler lists it); "" when there
+    is no such group."""
+    buf = ctypes.create_string_buffer(128)
+    n = _lib.moe_latent_group_kernel(h, rows, group, buf, len(buf))
+    if n < 0:
+        raise MoeError(-1, "moe_latent_group_kernel: invalid handle or rows")
+    return buf.value.decode()
 
 
 def moe_latent_forward_timed(h: int, rows: int, hidden_in: int, out: int, events) -> None:

@@ -204,58 +204,10 @@ struct GateLds {
     uint4 x[GATE_LDS_ELEMS / 8];
 };
 
-// Item: NW experts (one per wave) for the rows [r0, r1) of chunk item / groups (all rows when
-// gate_rc >= rows). Fixed summation order described above. bf16 gate rows of up to 4096
-// inputs stay in registers across the rows; a one-row pass loads its input row into registers
-// with them, a multi-row item first copies its chunk of input rows into LDS (all rows' loads
-// in flight at once) and reads each row from there.
-template <int NW>
-__device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLds &L) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int groups = (p.E + NW - 1) / NW;
-    const int e = (item % groups) * NW + wave;
-    const int r0 = (item / groups) * p.gate_rc;
-    const int r1 = r0 + p.gate_rc < p.rows ? r0 + p.gate_rc : p.rows;
+// Expert e's logits for the rows [r0, r1): one wave, the order above, the gate row held in
+// registers (bf16 rows of up to 4096 inputs) and each input row read from global memory.
+__device__ __forceinline__ void gate_expert(const LayerParams &p, int e, int r0, int r1, int lane) {
     const int nj = p.H / 512;
-    if (!p.router_f32 && nj <= 8 && p.rows > 1) {
-        // the chunk's rows: direct global -> LDS copies, 1 KB per wave instruction
-        const int units = (r1 - r0) * (p.H >> 3);
-        const uint4 *src = (const uint4 *)(p.x + (size_t)r0 * p.H);
-        for (int u0 = wave * 64; u0 < units; u0 += NW * 64) {
-            if (u0 + lane < units)
-                __builtin_amdgcn_global_load_lds((const void *)(src + u0 + lane),
-                                                 (__attribute__((address_space(3))) void *)(L.x + u0), 16, 0, 0);
-        }
-        uint4 wv[8];
-        if (e < p.E) {
-            const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j < nj) wv[j] = ld_weight16(wr + 512 * j);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (e >= p.E) return;
-        for (int r = r0; r < r1; ++r) {
-            const uint4 *xr = L.x + (size_t)(r - r0) * (p.H >> 3) + lane;
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j < nj) {
-                    float xf[8], wf[8];
-                    unpack8(p.act_f16, xr[64 * j], xf);
-                    unpack8(0, wv[j], wf);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
-                }
-            }
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
-            if (lane == 0) put_logit(p, r, e, f2bf(acc));
-        }
-        return;
-    }
-    if (e >= p.E) return;
     if (!p.router_f32 && nj <= 8) {
         const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
         uint4 wv[8];
@@ -325,6 +277,61 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLd
         for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
         if (lane == 0) put_logit(p, r, e, p.router_f32 ? __float_as_uint(acc) : (uint32_t)f2bf(acc));
     }
+}
+
+// Item: NW experts (one per wave) for the rows [r0, r1) of chunk item / groups (all rows when
+// gate_rc >= rows). Fixed summation order described above. bf16 gate rows of up to 4096
+// inputs stay in registers across the rows; a one-row pass loads its input row into registers
+// with them, a multi-row item first copies its chunk of input rows into LDS (all rows' loads
+// in flight at once) and reads each row from there.
+template <int NW>
+__device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLds &L) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int groups = (p.E + NW - 1) / NW;
+    const int e = (item % groups) * NW + wave;
+    const int r0 = (item / groups) * p.gate_rc;
+    const int r1 = r0 + p.gate_rc < p.rows ? r0 + p.gate_rc : p.rows;
+    const int nj = p.H / 512;
+    if (!p.router_f32 && nj <= 8 && p.rows > 1) {
+        // the chunk's rows: direct global -> LDS copies, 1 KB per wave instruction
+        const int units = (r1 - r0) * (p.H >> 3);
+        const uint4 *src = (const uint4 *)(p.x + (size_t)r0 * p.H);
+        for (int u0 = wave * 64; u0 < units; u0 += NW * 64) {
+            if (u0 + lane < units)
+                __builtin_amdgcn_global_load_lds((const void *)(src + u0 + lane),
+                                                 (__attribute__((address_space(3))) void *)(L.x + u0), 16, 0, 0);
+        }
+        uint4 wv[8];
+        if (e < p.E) {
+            const uint16_t *wr = p.gate_w16 + (size_t)e * p.H + 8 * lane;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < nj) wv[j] = ld_weight16(wr + 512 * j);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (e >= p.E) return;
+        for (int r = r0; r < r1; ++r) {
+            const uint4 *xr = L.x + (size_t)(r - r0) * (p.H >> 3) + lane;
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < nj) {
+                    float xf[8], wf[8];
+                    unpack8(p.act_f16, xr[64 * j], xf);
+                    unpack8(0, wv[j], wf);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], wf[i], acc);
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
+            if (lane == 0) put_logit(p, r, e, f2bf(acc));
+        }
+        return;
+    }
+    if (e >= p.E) return;
+    gate_expert(p, e, r0, r1, lane);
 }
 
 // ------------------------------------------------------------------ route
@@ -805,8 +812,7 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
     const int nr = lane & 15, grp = lane >> 4;
     const int n0 = tile * DENSE_TILE;
     const int kpart = K / ks, kbase = split * kpart;
-    int nsplit = NW;
-    while (nsplit > 1 && kpart % (128 * nsplit)) nsplit >>= 1;
+    const int nsplit = dense_nsplit(kpart, NW);
     const int kw = kpart / nsplit, nit = kw / 128;
     const int nrt = (p.rows + 15) >> 4;
     float *mypart = part + ((size_t)(tile * ks + split) * p.rows) * DENSE_TILE;
@@ -950,6 +956,134 @@ __device__ __forceinline__ void dense_item(const LayerParams &p, const uint16_t 
             dense_epilogue(p, EPI, row, n0 + nn, v);
         }
     }
+}
+
+// ------------------------------------------------------------------ first launch of a one-row pass
+
+// Weight steps of 128 inputs a slice wave keeps in flight (a build-time knob).
+#ifndef MOE_FRONT_DEP
+#define MOE_FRONT_DEP 1
+#endif
+
+// The fc1 and shared up projections of a one-row pass, as blocks of whole output rows (of the
+// rows of W1 followed by those of the shared up projection) spread evenly over the compute
+// units, each block in one workgroup over all of K: no sums cross workgroups. Wave s of a
+// block takes K slice s: the K range that wave s % nsplit of K part s / nsplit takes in a
+// dense item, with the same MFMA chain from zero over the same inputs in the same order (an
+// MFMA computes each output row alike, whatever rows share its tile); the block then adds
+// each row's slices as the dense items do (the waves' sums in wave order within a part, then
+// the parts in order). So every output equals the dense items', and so those of every
+// multi-row pass, bit for bit.
+struct FrontLds {
+    union {
+        struct {
+            uint4 wt[FRONT_SW][16 * 17];                // per slice wave: one step's weights (as in DenseLds)
+            uint4 xs[FRONT_SW][64];                     // per slice wave: the inputs of its slice
+            float part[FRONT_U_MAX][32];                // [slice][row of the block's two row tiles]
+        } s;
+        RouteLds<FRONT_THREADS> route;
+    };
+};
+
+// Row r of the concatenated projections: its weight row and its epilogue.
+__device__ __forceinline__ const uint16_t *front_row(const LayerParams &p, int r) {
+    return r < p.L ? p.fc1 + (size_t)r * p.H : p.su + (size_t)(r - p.L) * p.H;
+}
+
+// Slice wave `wave`: its K slices (wave, wave + FRONT_SW, ...) for the rows [r0, r1). A step
+// is 128 inputs of every row of the block (instruction i loads rows 4 i .. 4 i + 3, 16 lanes
+// per row, 256-byte runs; rows past r1 are not loaded), DEP steps in flight; the rows are
+// multiplied as MFMA row tiles of 16 (the last one partial: its missing rows are not kept),
+// one accumulator each, and each tile's sums go to part[slice][row].
+template <int DEP>
+__device__ __forceinline__ void front_rows(const LayerParams &p, int r0, int r1, int wave, int lane, FrontLds &L) {
+    const int nr = lane & 15, grp = lane >> 4, rr = lane >> 4, kk = lane & 15;
+    const int K = p.H, ks = p.ks_fc1, kpart = K / ks, nsplit = dense_nsplit(kpart, WG_THREADS / 64);
+    const int kw = kpart / nsplit, nit = kw >> 7, U = ks * nsplit, nrow = r1 - r0;
+    constexpr int NI = (FRONT_ROWS_MAX + 3) / 4;   // load instructions of a step at most
+    uint4 *wt = L.s.wt[wave], *xs = L.s.xs[wave];
+    for (int s = wave; s < U; s += FRONT_SW) {
+        const int kb = (s / nsplit) * kpart + (s % nsplit) * kw;
+        // the slice's inputs first: loads complete in order, so the first weights wait on
+        // nothing else
+        uint4 xv = make_uint4(0, 0, 0, 0);
+        if (8 * lane < kw) xv = glb_ld16(p.x + kb + 8 * lane);
+        // loads of step g's row tile tt (instructions 4 tt .. 4 tt + 3)
+        auto load = [&](int g, int tt, uint4 *dst) {
+#pragma unroll
+            for (int i = 4 * tt; i < 4 * tt + 4; ++i) {
+                if (i < NI) {
+                    dst[i] = make_uint4(0, 0, 0, 0);
+                    if (4 * i + rr < nrow) dst[i] = ld_weight16(front_row(p, r0 + 4 * i + rr) + kb + 128 * g + 8 * kk);
+                }
+            }
+        };
+        uint4 a[DEP][NI];
+#pragma unroll
+        for (int q = 0; q < DEP; ++q)
+            if (q < nit) {
+                load(q, 0, a[q]);
+                load(q, 1, a[q]);
+            }
+        lds_st16(&xs[lane], xv);
+        f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int g0 = 0; g0 < nit; g0 += DEP) {
+#pragma unroll
+            for (int q = 0; q < DEP; ++q) {
+                const int g = g0 + q;
+                if (g < nit) {
+                    // the step's input fragments, for both row tiles
+                    uint4 b[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) b[j] = lds_ld16(xs + 16 * g + 4 * j + grp);
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        if (16 * tt < nrow) {
+                            // the tile's rows through the wave's buffer into fragments (LDS
+                            // accesses of a wave are carried out in order); the same rows of
+                            // the step DEP ahead into the registers at once
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (4 * tt + i < NI && 16 * tt + 4 * i < nrow)
+                                    lds_st16(&wt[(4 * i + rr) * 17 + kk], a[q][4 * tt + i]);
+                            if (g + DEP < nit) load(g + DEP, tt, a[q]);
+                            uint4 f[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) f[j] = lds_ld16(&wt[nr * 17 + 4 * j + grp]);
+                            // every column of the MFMA gets the input row; column 0 is kept
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, f[j]), __builtin_bit_cast(bf16x8, b[j]), acc[tt], 0, 0, 0);
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (nr == 0) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) L.s.part[s][16 * tt + 4 * grp + i] = acc[tt][i];
+        }
+    }
+}
+
+// After the block's barrier: row r0 + t's slices added up in the dense items' order, then its
+// epilogue (fc1: rounding; shared up: relu^2).
+__device__ __forceinline__ void front_join(const LayerParams &p, int r0, int r1, const FrontLds &L) {
+    const int t = threadIdx.x;
+    if (t >= r1 - r0) return;
+    const int ks = p.ks_fc1, nsplit = dense_nsplit(p.H / ks, WG_THREADS / 64);
+    float v = 0.0f;
+    for (int q = 0; q < ks; ++q) {
+        float w = L.s.part[q * nsplit][t];
+        for (int s = 1; s < nsplit; ++s) w = w + L.s.part[q * nsplit + s][t];
+        v = q ? v + w : w;
+    }
+    const int r = r0 + t;
+    dense_epilogue(p, r < p.L ? EPI_FC1 : EPI_SHUP, 0, r < p.L ? r : r - p.L, v);
 }
 
 // ------------------------------------------------------------------ routed experts (4-bit)

@@ -141,6 +141,33 @@ MOE_EXPERT_KERNELS(6)
 MOE_EXPERT_KERNELS(8)
 #undef MOE_EXPERT_KERNELS
 
+// The first launch of a one-row pass. Workgroup 0 does nothing: the route workgroup,
+// dispatched last, goes to the compute unit it leaves, where no weights stream (a compute
+// unit holds one workgroup of this kernel's size at 4 waves per SIMD, so that unit is the
+// only one with room). Workgroups 1 .. n take the row blocks of fc1 and the shared up
+// projection (rows [(b-1) R / n, b R / n) of the R rows), their last wave the gate rows b - 1,
+// b - 1 + n, ...; workgroup n + 1 routes the row with the logits the gate waves hand it (its
+// wait is bounded, see route_item; every workgroup it waits for was dispatched before it).
+__global__ void __launch_bounds__(FRONT_THREADS) __attribute__((amdgpu_waves_per_eu(4, 8)))
+moe_front_kernel(LayerParams p, int n) {
+    __shared__ FrontLds lds;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, b = (int)blockIdx.x;
+    if (b > n) {
+        route_item<FRONT_THREADS>(p, 0, lds.route);
+        return;
+    }
+    if (b == 0) return;
+    const int w = b - 1, R = p.L + p.SI;
+    const int r0 = (int)((long)w * R / n), r1 = (int)((long)(w + 1) * R / n);
+    if (wave == FRONT_SW) {
+        for (int e = w; e < p.E; e += n) gate_expert(p, e, 0, 1, lane);
+    } else {
+        front_rows<MOE_FRONT_DEP>(p, r0, r1, wave, lane, lds);
+    }
+    __syncthreads();
+    front_join(p, r0, r1, lds);
+}
+
 // Read-only stream: n 16-byte units, 8 nontemporal loads in flight per thread per round,
 // grid-stride (one workgroup per compute unit: the fastest shape measured on this machine);
 // the data is folded into one XOR per workgroup so that the loads are kept.

@@ -62,6 +62,24 @@ constexpr int EXPERT_MAX_BLOCK = 64;      // output rows of one expert item at m
 constexpr int DENSE_TILE = 16;    // outputs per dense item
 constexpr int DENSE_XLDS = 8192;  // input elements a dense item stages in LDS at most
 
+// Waves a dense item splits its part of K over, in contiguous slices that are each a multiple
+// of 128 inputs: nw, halved while the part does not divide evenly.
+__host__ __device__ inline int dense_nsplit(int kpart, int nw) {
+    int n = nw;
+    while (n > 1 && kpart % (128 * n)) n >>= 1;
+    return n;
+}
+
+// The first launch of a one-row pass (the front kernel): blocks of whole output rows of fc1
+// and the shared up projection, one workgroup each, FRONT_SW waves taking one K slice each (a
+// slice: the K range one wave of a dense item takes), and a gate wave; after them one
+// workgroup routes the row.
+constexpr int FRONT_SW = 8;
+constexpr int FRONT_THREADS = (FRONT_SW + 1) * 64;
+constexpr int FRONT_ROWS_MAX = 24;   // rows of a block at most (two MFMA row tiles, the second partial)
+constexpr int FRONT_U_MAX = 16;      // K slices at most (each wave takes at most two)
+constexpr int FRONT_KW_MAX = 512;   // inputs of a slice at most (one 16-byte load per lane)
+
 struct LayerParams {
     // sizes
     int H, L, D, E, G, TG, K, I, SI, rows;
@@ -115,6 +133,10 @@ struct LayerParams {
     int hand;
     int ctr_hand;
     uint32_t wait_ticks;
+    // front_wgs > 0: a one-row pass may run its first launch as the front kernel: an empty
+    // workgroup, front_wgs row blocks, then the route workgroup
+    int front_wgs;
+    int cus;               // compute units of the device
     // the lm_head gemv (a separate entry point sharing the dense tiles): out [rows][lm_n],
     // fp32 (lm_f32) or bf16
     void *lm_out;

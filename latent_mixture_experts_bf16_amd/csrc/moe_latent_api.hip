@@ -26,6 +26,7 @@ __global__ void moe_stage_kernel(LayerParams p, int lo, int hi, int mid, int pre
 __global__ void moe_clear_kernel(uint32_t *ctr, int n);
 __global__ void moe_stream_read_kernel(const uint4 *src, size_t n, uint32_t *sink);
 __global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint16_t *X, int K, int lo);
+__global__ void moe_front_kernel(LayerParams p, int nwg);
 // the prefill (prefill_kernels.hip)
 template <bool F32W> __global__ void pf_gate_kernel(LayerParams p);
 __global__ void pf_route_kernel(LayerParams p);
@@ -335,10 +336,12 @@ static size_t layout_workspace(const moe_latent_config &c, LayerParams &p, size_
     *n_ctr = p.ctr_hand + 2 * (int)E * (int)(R < (size_t)MAX_ROWS ? R : (size_t)MAX_ROWS);
     p.wait_ticks = 10000000u;   // 100 ms: far beyond any forward
     // split-K partials of decode passes: [tile][split][row][16] floats = N * splits * rows
-    // floats (a decode pass takes at most MAX_ROWS rows; a prefill none of these)
+    // floats (a decode pass takes at most MAX_ROWS rows; a prefill none of these); fc1 and
+    // shared up hold at least [tile][split][wave slice][16], the front kernel's slices
     const size_t Rd = R < (size_t)MAX_ROWS ? R : (size_t)MAX_ROWS;
-    const size_t part_fc1 = L * p.ks_fc1 * Rd * 4;
-    const size_t part_shup = SI * p.ks_shup * Rd * 4;
+    const size_t Rf = Rd > (size_t)(WG_THREADS / 64) ? Rd : (size_t)(WG_THREADS / 64);
+    const size_t part_fc1 = L * p.ks_fc1 * Rf * 4;
+    const size_t part_shup = SI * p.ks_shup * Rf * 4;
     const size_t part_shdn = SI ? H * p.ks_shdn * Rd * 4 : 0;
     const size_t part_fc2 = L ? H * p.ks_fc2 * Rd * 4 : 0;
     const size_t max_tiles = (R * K + 63) / 64 + (E < R * K ? E : R * K);   // prefill row tiles
@@ -474,6 +477,7 @@ extern "C" int moe_latent_create(const moe_latent_config *cfg, const moe_latent_
     h->magic = kMagic;
     h->last_rows = 0;
     h->cus = cus;
+    h->base.cus = cus;
     fill_params(*cfg, *w, h->base);
 
     if ((rc = setup_workspace(h))) {
@@ -508,7 +512,7 @@ extern "C" int moe_latent_set_stream(moe_latent_t *h, void *hip_stream) {
 // split >= 0 the first `pre` items of stage `split` on are dispatched first (see
 // moe_stage_kernel). side: 0 on the caller's stream, 1 on the handle's side stream; join: the
 // launch first waits for the side stream's work of this forward.
-enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B };
+enum Kernel { K_GATE_SHUP, K_ROUTE_UP, K_UP_DOWN, K_FC2, K_SHUP, K_SHDN_A, K_SHDN_B, K_FRONT };
 struct Launch {
     int first, last, kernel, split, pre, side, join, fork;
 };
@@ -526,6 +530,9 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
     // (the side stream's fork and join cost more than the overlap saves in so short a pass);
     // the 64-row stack 361 us per layer against 394, the 16-row pass 149 against 151.
     if (variant == 3) variant = p.single_row ? 1 : 2;
+    // variant 4: variant 1 with the first launch of a one-row pass as stage-kernel items
+    const bool front = p.single_row && p.front_wgs > 0 && variant != 4;
+    if (variant == 4) variant = 1;
     auto add = [&](int f, int l, int k, int split = -1, int pre = 0, int side = 0, int join = 0, int fork = 0) {
         out[n++] = Launch{f, l, k, split, pre, side, join, fork};
     };
@@ -554,7 +561,7 @@ static int plan_launches(const LayerParams &p, int cus, int variant, Launch *out
             const int a = cus - sd;
             return a <= 0 ? 0 : (a < e ? a : e);
         };
-        add(ST_GATE, ST_SHUP, K_GATE_SHUP);
+        add(ST_GATE, ST_SHUP, front ? K_FRONT : K_GATE_SHUP);
         add(ST_ROUTE, ST_UP, K_ROUTE_UP, ST_UP, pre(ST_SHDN_A, ST_UP));
         add(ST_SHDN_B, ST_DOWN, K_UP_DOWN, ST_DOWN, pre(ST_SHDN_B, ST_DOWN));
     } else if (p.hand) {
@@ -609,9 +616,26 @@ static void launch_expert(const LayerParams &p, const Launch &l, hipStream_t st,
 #undef MOE_CASE
 }
 
+// The first launch of a one-row pass as the front kernel: an empty workgroup, the row blocks,
+// then the route workgroup.
+static void launch_front(const LayerParams &p, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const int n = p.front_wgs;
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(moe_front_kernel, dim3(n + 2), dim3(FRONT_THREADS), 0, st, ev0, ev1, 0, p, n);
+    else
+        hipLaunchKernelGGL(moe_front_kernel, dim3(n + 2), dim3(FRONT_THREADS), 0, st, p, n);
+}
+
+// Workgroups of a launch.
+static int launch_items(const LayerParams &p, const Launch &l) {
+    if (l.kernel == K_FRONT) return p.front_wgs + 2;
+    return p.item_base[l.last + 1] - p.item_base[l.first];
+}
+
 static void launch_one(const LayerParams &p, const Launch &l, hipStream_t st, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr) {
     switch (l.kernel) {
+        case K_FRONT: launch_front(p, st, ev0, ev1); break;
         case K_GATE_SHUP: launch_kernel<ST_GATE, ST_SHUP, false>(p, l, st, ev0, ev1); break;
         case K_ROUTE_UP: launch_expert<ST_ROUTE, ST_UP>(p, l, st, ev0, ev1); break;
         case K_UP_DOWN: launch_expert<ST_UP, ST_DOWN>(p, l, st, ev0, ev1); break;
@@ -665,8 +689,9 @@ extern "C" int moe_latent_set_variant(moe_latent_t *h, int32_t variant) {
     if (variant == 0)
         return fail(MOE_ERR_INVALID_ARG, "variant 0 (one fused launch per forward) is disabled: its first "
                     "GPU run did not complete (see the description of moe_latent_set_variant)");
-    if (variant < 1 || variant > 3)
-        return fail(MOE_ERR_INVALID_ARG, "variant %d (1: one stream, 2: two streams, 3: by row count)", variant);
+    if (variant < 1 || variant > 4)
+        return fail(MOE_ERR_INVALID_ARG, "variant %d (1: one stream, 2: two streams, 3: by row count, 4: one "
+                    "stream, a one-row pass without the front kernel)", variant);
     (void)hipStreamSynchronize(h->stream);
     h->variant = variant;
     return MOE_OK;
@@ -686,6 +711,18 @@ static void plan_items(LayerParams &p, int rows) {
     p.dn_nb = expert_block(p.D, p.I, p.qbits, 1 << p.gs_log2);
     p.up_blocks = p.I / p.up_nb;
     p.dn_blocks = p.D / p.dn_nb;
+    // a one-row latent pass of bf16 activations: fc1 and shared up in the front kernel's row
+    // blocks (one per compute unit but one, at most FRONT_ROWS_MAX rows each; K slices of at
+    // most FRONT_KW_MAX inputs, at most FRONT_U_MAX of them)
+    p.front_wgs = 0;
+    if (rows == 1 && p.L && !p.act_f16 && p.ks_fc1 == p.ks_shup) {
+        const int kpart = p.H / p.ks_fc1, ns = dense_nsplit(kpart, WG_THREADS / 64);
+        const int R = p.L + p.SI;
+        if (kpart / ns <= FRONT_KW_MAX && p.ks_fc1 * ns <= FRONT_U_MAX) {
+            const int nb = p.cus > 1 ? p.cus - 1 : 1;
+            p.front_wgs = nb > (R + FRONT_ROWS_MAX - 1) / FRONT_ROWS_MAX ? nb : (R + FRONT_ROWS_MAX - 1) / FRONT_ROWS_MAX;
+        }
+    }
     // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's
     // tiles are cut in two halves for two launches
     const int shdn = p.SI ? p.H / DENSE_TILE : 0, ks_sd = p.ks_shdn;
@@ -876,7 +913,7 @@ extern "C" int moe_latent_group_items(moe_latent_t *h, int32_t rows, int32_t gro
     Launch ls[MAX_LAUNCHES];
     const int n = plan_launches(p, h->cus, h->variant, ls);
     if (group < 0 || group >= n) return 0;
-    return p.item_base[ls[group].last + 1] - p.item_base[ls[group].first];
+    return launch_items(p, ls[group]);
 }
 
 extern "C" int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t group, int32_t *first_stage,
@@ -890,7 +927,37 @@ extern "C" int moe_latent_group_stages(moe_latent_t *h, int32_t rows, int32_t gr
     if (first_stage) *first_stage = ls[group].first;
     if (last_stage) *last_stage = ls[group].last;
     if (side) *side = ls[group].side;
-    return p.item_base[ls[group].last + 1] - p.item_base[ls[group].first];
+    return launch_items(p, ls[group]);
+}
+
+// The kernel a launch runs, as a profiler names it (without namespace and arguments).
+static void kernel_name(const LayerParams &p, const Launch &l, char *buf, size_t cap) {
+    const char *wide = p.D > 2048 || p.I > 2048 ? "true" : "false";
+    const int qb = p.generic ? p.qbits : 0;
+    switch (l.kernel) {
+        case K_FRONT: snprintf(buf, cap, "moe_front_kernel"); break;
+        case K_GATE_SHUP: snprintf(buf, cap, "moe_stage_kernel<%d, %d, false, 0>", ST_GATE, ST_SHUP); break;
+        case K_ROUTE_UP: snprintf(buf, cap, "moe_stage_kernel<%d, %d, %s, %d>", ST_ROUTE, ST_UP, wide, qb); break;
+        case K_UP_DOWN: snprintf(buf, cap, "moe_stage_kernel<%d, %d, %s, %d>", ST_UP, ST_DOWN, wide, qb); break;
+        case K_SHUP: snprintf(buf, cap, "moe_stage_kernel<%d, %d, false, 0>", ST_SHUP, ST_SHUP); break;
+        case K_SHDN_A: snprintf(buf, cap, "moe_stage_kernel<%d, %d, false, 0>", ST_SHDN_A, ST_SHDN_A); break;
+        case K_SHDN_B: snprintf(buf, cap, "moe_stage_kernel<%d, %d, false, 0>", ST_SHDN_B, ST_SHDN_B); break;
+        default: snprintf(buf, cap, "moe_stage_kernel<%d, %d, false, 0>", ST_FC2, ST_FC2); break;
+    }
+}
+
+extern "C" int moe_latent_group_kernel(moe_latent_t *h, int32_t rows, int32_t group, char *name, int32_t cap) {
+    if (!valid(h) || rows < 1 || rows > h->cfg.max_rows || rows > MAX_ROWS || !name || cap < 1) return -1;
+    LayerParams p = h->base;
+    plan_items(p, rows);
+    Launch ls[MAX_LAUNCHES];
+    const int n = plan_launches(p, h->cus, h->variant, ls);
+    name[0] = 0;
+    if (group < 0 || group >= n) return 0;
+    char buf[96];
+    kernel_name(p, ls[group], buf, sizeof buf);
+    snprintf(name, (size_t)cap, "%s", buf);
+    return (int)strlen(name);
 }
 
 extern "C" int moe_latent_get_routing(moe_latent_t *h, int32_t *idx_dev, float *w_dev) {
@@ -1017,6 +1084,7 @@ extern "C" int moe_latent_forward_static(const moe_latent_config *cfg, const moe
     void *base = nullptr;
     if ((rc = scratch_of_current_device(&base, &cus))) return rc;
     layout_workspace(*cfg, p, (size_t)rows, (char *)base, &n_ctr);
+    p.cus = cus;
     p.x = (const uint16_t *)hidden_in;
     p.out = (uint16_t *)out;
     plan_items(p, rows);

@@ -356,6 +356,14 @@ def test_timed_forward_equals_forward_and_records_each_launch():
     torch.cuda.synchronize()
     ng = sum(1 for g in range(10) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
     assert ng == 4      # one row, one stream: gate + fc1 + shared up, up, down, fc2
+    # the first launch: the front kernel (256 slice workgroups and the route workgroup), or
+    # stage-kernel items under variant 4
+    assert B.moe_latent_group_kernel(lay.handle, 1, 0) == "moe_front_kernel"
+    assert B.moe_latent_group_items(lay.handle, 1, 0) == 257
+    assert B.moe_latent_group_kernel(lay.handle, 1, 3) == "moe_stage_kernel<8, 8, false, 0>"
+    assert B.moe_latent_group_kernel(lay.handle, 1, 4) == ""
+    B.moe_latent_set_variant(lay.handle, 4)
+    assert B.moe_latent_group_kernel(lay.handle, 1, 0) == "moe_stage_kernel<0, 2, false, 0>"
     B.moe_latent_set_variant(lay.handle, 2)
     ng2 = sum(1 for g in range(10) if B.moe_latent_group_items(lay.handle, 1, g) > 0)
     assert ng2 == 7     # two streams: gate + fc1, expert up, shared up, shared down x 2, down, fc2
@@ -644,8 +652,8 @@ def test_variant_zero_is_refused():
     with pytest.raises(B.MoeError):
         B.moe_latent_set_variant(lay.handle, 0)
     with pytest.raises(B.MoeError):
-        B.moe_latent_set_variant(lay.handle, 4)
-    for v in (1, 2, 3):
+        B.moe_latent_set_variant(lay.handle, 5)
+    for v in (1, 2, 3, 4):
         B.moe_latent_set_variant(lay.handle, v)
     lay.close()
 
@@ -653,13 +661,16 @@ def test_variant_zero_is_refused():
 @pytest.mark.parametrize("cid", [0, 1, 2, 3])
 def test_one_stream_and_two_stream_variants_agree_bitwise(cid):
     """The shared expert on the side stream (variant 2) and inside the chain's launches
-    (variant 1) give the same bits: outputs, routing, and every stage."""
+    (variant 1), and a one-row pass's first launch as the front kernel (variant 1) or as
+    stage-kernel items (variant 4), give the same bits: outputs, routing, and every stage."""
     dims, arrays = workload(cid)
     rows = arrays["x"].shape[0]
     res = []
-    for variant in (1, 2, 3):
+    for variant in (1, 2, 3, 4):
         lay, xd, out = run_gpu(dims, arrays, variant=variant)
         st = [lay.stage(n, rows) for n in ("logits", "expert_act", "expert_out", "combine")]
+        if dims.latent:
+            st.append(lay.stage("latent", rows))
         if dims.shared_inter:
             st += [lay.stage("shared_act", rows), lay.stage("shared_out", rows)]
         res.append((out.cpu().numpy(), *lay.routing(rows), *st))
