@@ -204,11 +204,12 @@ def stage_bytes(dims, rows, n_distinct):
     a = 2  # activation bytes
     expert = D * I * dims.quant_bits // 8 + (D * I // dims.group_size) * 4   # codes + bf16 scale, bias per group
     half = (H // 16 // 2) * 16
+    lg = 4 if dims.router_dtype == 3 else 2   # logit bytes (fp32 router: fp32 logits)
     return {
-        "gate": E * H * (4 if dims.router_dtype == 3 else 2) + rows * H * a + rows * E * 2,
+        "gate": E * H * lg + rows * H * a + rows * E * lg,
         "fc1": L * H * 2 + rows * L * a,
         "shup": SI * H * 2 + rows * SI * a,
-        "route": (E * 4 if dims.has_bias else 0) + rows * E * 2 + rows * K * 8,
+        "route": (E * 4 if dims.has_bias else 0) + rows * E * lg + rows * K * 8,
         "shdn_a": half * SI * 2 + rows * SI * a + rows * half * a if SI else 0,
         "up": n_distinct * expert + rows * D * a + rows * K * I * a,
         "shdn_b": (H - half) * SI * 2 + rows * SI * a + rows * (H - half) * a if SI else 0,
@@ -503,7 +504,8 @@ def main():
     del layers, xs, outs
     torch.cuda.empty_cache()
     if not args.no_rows_sweep and rows == 1:
-        line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(4, 1, B, LY, synth)]
+        line["rows_sweep"] = [rows_sweep(2, 2, B, LY, synth), rows_sweep(3, 4, B, LY, synth),
+                              rows_sweep(4, 1, B, LY, synth)]
     if not args.no_lm_head and rows == 1:
         line["lm_head"] = lm_head_bench(B, LY, synth)
     if not args.no_prefill and rows == 1:
@@ -755,9 +757,10 @@ def in_forward_launches(B, layers, xs, outs, rows, s, ng, sweeps=4, rounds=30):
 
 
 def rows_sweep(cfg, instances, B, LY, synth, sweeps=200, warmup=20):
-    """Multi-row passes: the 16-row pass (distinct weight instances rotated through HBM) or the
-    8-layer 64-row stack (each layer with its own input), timed as graph replays of one sweep
-    over all layers and instances; algorithmic bytes as for the one-row line."""
+    """Multi-row passes: the 16-row pass, the 4-row pass of the non-latent fp16 layer with the
+    fp32 router (distinct weight instances rotated through HBM), or the 8-layer 64-row stack
+    (each layer with its own input), timed as graph replays of one sweep over all layers and
+    instances; algorithmic bytes as for the one-row line."""
     wl = synth.WORKLOADS[cfg]
     t0 = time.time()
     sets = [(d, arrays) for i in range(instances) for d, arrays in synth.workload_layers(cfg, instance=i)]
