@@ -280,10 +280,11 @@ __device__ __forceinline__ void gate_expert(const LayerParams &p, int e, int r0,
 }
 
 // Item: NW experts (one per wave) for the rows [r0, r1) of chunk item / groups (all rows when
-// gate_rc >= rows). Fixed summation order described above. bf16 gate rows of up to 4096
-// inputs stay in registers across the rows; a one-row pass loads its input row into registers
-// with them, a multi-row item first copies its chunk of input rows into LDS (all rows' loads
-// in flight at once) and reads each row from there.
+// gate_rc >= rows). Fixed summation order described above. Gate rows of up to 4096 bf16 or
+// 5120 fp32 inputs stay in registers across the rows; a one-row pass loads its input row into
+// registers with them, a multi-row item first copies its chunk of input rows into LDS (all
+// rows' loads in flight at once) and reads each row from there.
+constexpr int GATE_NJ_F32 = 10;   // 512-input chunks of an fp32 gate row held in registers
 template <int NW>
 __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLds &L) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -292,6 +293,48 @@ __device__ __forceinline__ void gate_item(const LayerParams &p, int item, GateLd
     const int r0 = (item / groups) * p.gate_rc;
     const int r1 = r0 + p.gate_rc < p.rows ? r0 + p.gate_rc : p.rows;
     const int nj = p.H / 512;
+    if (p.router_f32 && nj <= GATE_NJ_F32 && p.rows > 1) {
+        // the fp32 router: the same, with each chunk of the gate row in two registers
+        const int units = (r1 - r0) * (p.H >> 3);
+        const uint4 *src = (const uint4 *)(p.x + (size_t)r0 * p.H);
+        for (int u0 = wave * 64; u0 < units; u0 += NW * 64) {
+            if (u0 + lane < units)
+                __builtin_amdgcn_global_load_lds((const void *)(src + u0 + lane),
+                                                 (__attribute__((address_space(3))) void *)(L.x + u0), 16, 0, 0);
+        }
+        uint4 wv[GATE_NJ_F32][2];
+        if (e < p.E) {
+            const float *wr = p.gate_w32 + (size_t)e * p.H + 8 * lane;
+#pragma unroll
+            for (int j = 0; j < GATE_NJ_F32; ++j)
+                if (j < nj) {
+                    wv[j][0] = ld_weight16(wr + 512 * j);
+                    wv[j][1] = ld_weight16(wr + 512 * j + 4);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (e >= p.E) return;
+        for (int r = r0; r < r1; ++r) {
+            const uint4 *xr = L.x + (size_t)(r - r0) * (p.H >> 3) + lane;
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < GATE_NJ_F32; ++j) {
+                if (j < nj) {
+                    float xf[8];
+                    unpack8(p.act_f16, xr[64 * j], xf);
+                    const uint32_t w8[8] = {wv[j][0].x, wv[j][0].y, wv[j][0].z, wv[j][0].w,
+                                            wv[j][1].x, wv[j][1].y, wv[j][1].z, wv[j][1].w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(xf[i], __uint_as_float(w8[i]), acc);
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d, 64);
+            if (lane == 0) put_logit(p, r, e, __float_as_uint(acc));
+        }
+        return;
+    }
     if (!p.router_f32 && nj <= 8 && p.rows > 1) {
         // the chunk's rows: direct global -> LDS copies, 1 KB per wave instruction
         const int units = (r1 - r0) * (p.H >> 3);
@@ -445,23 +488,30 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
     if (tid < MAX_TOPK) L.picks[tid] = -1;
     for (int c = tid; c < E; c += NT) L.rank[c] = 0;
     __syncthreads();
-    // every expert's rank inside its group (without group selection: among all experts, which
-    // picks the top_k directly)
-    const bool grouped = p.TG < G;
-    const int gsz = grouped ? per : E;
+    // every expert's rank inside its group. Without group selection: among all experts, which
+    // picks the top_k directly, or for more than 64 experts inside blocks of 64, whose top_k
+    // are the candidates (a pick is among the top_k of its block)
+    const bool grouped = p.TG < G, blocked = !grouped && E > 64;
+    const int gsz = grouped ? per : blocked ? 64 : E;
+    const int nblk = (E + 63) >> 6;
+    if (blocked)   // a block of fewer than top_k experts leaves candidate slots that rank last
+        for (int c = tid; c < nblk * p.K; c += NT) L.ckey[c] = 0;
     for (int e = tid; e < E; e += NT) {
-        const int g = e / gsz;
-        const int rank = count_greater_any(L.key + g * gsz, gsz, L.key[e]);
+        const int g = e / gsz, n = E - g * gsz < gsz ? E - g * gsz : gsz;
+        const int rank = count_greater_any(L.key + g * gsz, n, L.key[e]);
         L.inr[e] = rank;
         if (grouped && rank < 2) L.top[g][rank] = e;
-        if (!grouped && rank < p.K) L.picks[rank] = e;
+        if (!grouped && !blocked && rank < p.K) L.picks[rank] = e;
     }
     __syncthreads();
-    if (grouped) {
+    if (grouped || blocked) {
         // candidates: a pick is among the top_k of its own group, so only those members of the
         // kept groups enter; candidate slot = (kept groups before g) * KK + rank in the group
-        const int KK = p.K < per ? p.K : per;
-        if (G <= 64) {
+        const int KK = blocked ? p.K : p.K < per ? p.K : per;
+        if (blocked) {
+            for (int e = tid; e < E; e += NT)
+                if (L.inr[e] < KK) L.ckey[(e >> 6) * KK + L.inr[e]] = L.key[e];
+        } else if (G <= 64) {
             // up to 64 groups: every wave scores the groups itself, lane g taking group g, and
             // ranks them with lane reads, so the kept groups are a mask in every wave and no
             // barrier is needed before the candidates
@@ -504,7 +554,7 @@ __device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds
         __syncthreads();
         // the top_k of the candidates: rank among them, counted by T threads per candidate
         // (each over a contiguous part of the list) and summed in LDS
-        const int nc = p.TG * KK;
+        const int nc = blocked ? nblk * KK : p.TG * KK;
         int T = 1;
         while (T < 16 && 2 * T * nc <= NT) T *= 2;
         for (int i = tid; i < nc * T; i += NT) {
@@ -572,12 +622,23 @@ struct SchedLds {
 };
 
 // Item: the whole pass. Slots are the distinct picked experts in increasing id; each slot
-// lists its (row * top_k + pick) pairs in increasing row.
+// lists its (row * top_k + pick) pairs in increasing row. The picks are read once (one round
+// trip) and everything is built in LDS; the schedule is written after the last barrier, since
+// a barrier waits for the stores before it.
 __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
     const int tid = threadIdx.x, E = p.E, NP = p.rows * p.K;
+    constexpr int PPT = MAX_ROWS * MAX_TOPK / WG_THREADS;   // picks per thread at most
+    int pick[PPT];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int i = tid + k * WG_THREADS;
+        pick[k] = i < NP ? ld_shared32(p.idx + i) : 0;
+    }
     for (int e = tid; e < E; e += WG_THREADS) { L.cnt[e] = 0; L.cur[e] = 0; }
     __syncthreads();
-    for (int i = tid; i < NP; i += WG_THREADS) atomicAdd(&L.cnt[ld_shared32(p.idx + i)], 1);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k)
+        if (tid + k * WG_THREADS < NP) atomicAdd(&L.cnt[pick[k]], 1);
     __syncthreads();
     // exclusive scans of cnt (pair offsets) and of (cnt > 0) (slot ids), 4 experts per thread
     const int per_t = (E + WG_THREADS - 1) / WG_THREADS;
@@ -605,14 +666,12 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             run_pairs += L.cnt[e];
         }
     }
-    if (tid == WG_THREADS - 1) p.sched[SCH_U] = run_slots;
-    // slots past U (up to the slots the item grid enumerates) are marked empty
     const int U = L.scan[WG_THREADS - 1] >> 16, umax = E < NP ? E : NP;
-    for (int u = U + tid; u < umax; u += WG_THREADS) *(int4 *)(p.sched + SCH_REC + SCH_RECW * u) = make_int4(-1, 0, 0, 0);
     __syncthreads();
-    for (int i = tid; i < NP; i += WG_THREADS) {
-        const int e = ld_shared32(p.idx + i);
-        L.pairs[L.off[e] + atomicAdd(&L.cur[e], 1)] = i;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int i = tid + k * WG_THREADS;
+        if (i < NP) L.pairs[L.off[pick[k]] + atomicAdd(&L.cur[pick[k]], 1)] = i;
     }
     __syncthreads();
     // order each expert's list by row (insertion sort: lists are short)
@@ -624,12 +683,19 @@ __device__ __forceinline__ void sched_item(const LayerParams &p, SchedLds &L) {
             while (b >= 0 && L.pairs[o + b] > v) { L.pairs[o + b + 1] = L.pairs[o + b]; --b; }
             L.pairs[o + b + 1] = v;
         }
+    }
+    __syncthreads();
+    // the schedule: U, each slot's record (slots past U, up to the slots the item grid
+    // enumerates, marked empty), the pair lists
+    if (tid == 0) p.sched[SCH_U] = U;
+    for (int e = tid; e < E; e += WG_THREADS) {
+        const int o = L.off[e], n = L.cnt[e];
         if (n > 0) {
             *(int4 *)(p.sched + SCH_REC + SCH_RECW * L.slot[e]) = make_int4(e, o, n, L.pairs[o]);
             *(int4 *)(p.sched + SCH_REC + SCH_RECW * L.slot[e] + 4) = make_int4(n > 1 ? L.pairs[o + 1] : -1, 0, 0, 0);
         }
     }
-    __syncthreads();
+    for (int u = U + tid; u < umax; u += WG_THREADS) *(int4 *)(p.sched + SCH_REC + SCH_RECW * u) = make_int4(-1, 0, 0, 0);
     for (int i = tid; i < NP; i += WG_THREADS) p.sched[SCH_PAIRS + i] = L.pairs[i];
 }
 

@@ -726,9 +726,9 @@ static void plan_items(LayerParams &p, int rows) {
     // dense projections: (tile of 16 outputs, K split) per item; the shared down projection's
     // tiles are cut in two halves for two launches
     const int shdn = p.SI ? p.H / DENSE_TILE : 0, ks_sd = p.ks_shdn;
-    // gate: groups of 4 experts; a multi-row pass of bf16 rows up to 4096 wide splits its rows
-    // in chunks that fit the item's 32 KB of LDS
-    p.gate_rc = rows > 1 && !p.router_f32 && p.H <= 4096 ? 16384 / p.H : rows;
+    // gate: groups of 4 experts; a multi-row pass of gate rows up to 4096 (bf16) or 5120 (fp32)
+    // wide splits its rows in chunks that fit the item's 32 KB of LDS
+    p.gate_rc = rows > 1 && p.H <= (p.router_f32 ? 5120 : 4096) ? 16384 / p.H : rows;
     if (p.gate_rc > 16) p.gate_rc = 16;
     n[ST_GATE] = (p.E + WG_THREADS / 64 - 1) / (WG_THREADS / 64) * ((rows + p.gate_rc - 1) / p.gate_rc) +
                  (p.hand ? rows : 0);
