@@ -187,8 +187,14 @@ def test_wide_projections_split_over_items():
 def _routing_layer(case):
     """Small layers whose routing takes the less common paths: more than 64 groups, more
     than 64 candidates (both ranked by the multi-step LDS path), planted ties of scores and
-    of group scores, and NaN logits."""
-    if case == "groups_over_64":
+    of group scores, NaN logits, and more than 64 experts without group selection in a number
+    that is not a multiple of 64 (ranked inside blocks of 64, the last block holding fewer
+    experts than top_k), with ties across the blocks."""
+    if case == "ungrouped_ragged":
+        dims = synth.LayerDims(hidden=512, latent=128, n_experts=70, n_group=1, topk_group=1, top_k=8,
+                               expert_inter=256, shared_inter=512, group_size=64, act_dtype=1,
+                               router_dtype=1, has_bias=True, norm_topk=True, routed_scaling=2.5)
+    elif case == "groups_over_64":
         dims = synth.LayerDims(hidden=512, latent=128, n_experts=256, n_group=128, topk_group=6, top_k=9,
                                expert_inter=256, shared_inter=0, group_size=64, act_dtype=1,
                                router_dtype=1, has_bias=True, norm_topk=True, routed_scaling=2.5)
@@ -216,22 +222,43 @@ def _routing_layer(case):
         wg[7, 100] = 0x7FC0          # a NaN weight: expert 7's logit is NaN
         wg[56:64, 0] = 0x7FC0        # all of group 7
         cb[7] = np.float32(1.0)      # would rank first otherwise
+    elif case == "ungrouped_ragged":
+        # experts 66 and 68 (the last block, of 6) tie with 2 and 40 (the first), all raised
+        # so that they are picked: the tie goes to the lower id across the blocks
+        for a, b in ((66, 2), (68, 40)):
+            wg[a] = wg[b]
+            cb[a] = cb[b]
+        cb[[2, 40, 66, 68]] += np.float32(0.5)
     return dims, arrays
 
 
-@pytest.mark.parametrize("case", ["groups_over_64", "candidates_over_64", "ties", "nan"])
+@pytest.mark.parametrize("case", ["groups_over_64", "candidates_over_64", "ties", "nan", "ungrouped_ragged"])
 def test_routing_edge_cases(case):
+    """Routing bit for bit in a 3-row pass (the stage kernel's route items) and in each row's
+    one-row pass (the front kernel's route workgroup), and each row's output equal in both."""
     dims, arrays = _routing_layer(case)
     ref = O.forward(dims, arrays)
     lay, xd, out = run_gpu(dims, arrays)
     idx, w = lay.routing(3)
     assert np.array_equal(idx, ref["idx"]), (case, idx, ref["idx"])
     assert np.array_equal(w.view(np.uint32), ref["w"].view(np.uint32)), case
-    assert_out_close(dims, out.cpu().numpy().view(np.uint16), ref["out_f32"], case)
+    got = out.cpu().numpy().view(np.uint16)
+    assert_out_close(dims, got, ref["out_f32"], case)
     if case == "ties":
         assert {3, 5}.issubset(set(ref["idx"][0].tolist()))
     if case == "nan":
         assert 7 not in ref["idx"][0].tolist()
+    if case == "ungrouped_ragged":
+        assert {2, 40, 66, 68}.issubset(set(ref["idx"][0].tolist()))
+    for r in range(3):
+        o1 = torch.empty_like(xd[r:r + 1])
+        lay.forward(xd[r:r + 1], o1, 1)
+        torch.cuda.synchronize()
+        lay.status()
+        i1, w1 = lay.routing(1)
+        assert np.array_equal(i1[0], ref["idx"][r]), (case, r)
+        assert np.array_equal(w1[0].view(np.uint32), ref["w"][r].view(np.uint32)), (case, r)
+        assert np.array_equal(o1.cpu().numpy().view(np.uint16)[0], got[r]), (case, r)
     lay.close()
 
 
