@@ -19,7 +19,9 @@ except ImportError:  # pragma: no cover
     pass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_latent.so")
+# MOE_LATENT_LIB names another build of the same sources to load instead (the CPU sanitizer
+# tests point it at a host-only build instrumented with AddressSanitizer and UBSan).
+LIB_PATH = os.environ.get("MOE_LATENT_LIB") or os.path.join(_PKG, "libmoe_latent.so")
 
 # enum values of include/moe_latent.h
 MOE_DT_BF16, MOE_DT_F16, MOE_DT_F32, MOE_DT_U32, MOE_DT_I32 = 1, 2, 3, 4, 5

@@ -27,21 +27,25 @@ FLAGS = [
 OBJ = os.path.join(PKG, "_build")
 
 
-def build(extra=()):
-    """Compile every source to an object (in parallel), then link the library."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(extra=(), lib=LIB, obj=OBJ):
+    """Compile every source to an object (in parallel), then link the library.
+
+    `extra` flags go to every compile and to the link; `lib` and `obj` place another build
+    of the same sources (the CPU sanitizer tests build one with instrumented host code).
+    """
+    os.makedirs(obj, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     procs, objs = [], []
     for s in SOURCES:
-        o = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        o = os.path.join(obj, os.path.splitext(s)[0] + ".o")
         objs.append(o)
         procs.append(subprocess.Popen([HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, s), "-o", o]))
     bad = [s for s, p in zip(SOURCES, procs) if p.wait() != 0]
     if bad:
         raise subprocess.CalledProcessError(1, f"hipcc -c {' '.join(bad)}")
-    subprocess.run([HIPCC, *FLAGS, *extra, "-shared", *objs, "-o", LIB + ".tmp"], check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    subprocess.run([HIPCC, *FLAGS, *extra, "-shared", *objs, "-o", lib + ".tmp"], check=True)
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
