@@ -34,6 +34,8 @@ __global__ void pf_sched_kernel(LayerParams p);
 template <int EPI>
 __global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 template <bool UP> __global__ void pf_expert_kernel(LayerParams p);
+template <int EPI>
+__global__ void pf_gemm_big_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 __global__ void pf_combine_kernel(LayerParams p);
 }  // namespace moe
 
@@ -820,10 +822,23 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     hipLaunchKernelGGL(pf_route_kernel, dim3(rows), dim3(WG_THREADS), 0, st, p);
     hipLaunchKernelGGL(pf_sched_kernel, dim3((NP + 1023) / 1024), dim3(WG_THREADS), 0, st, p);
     const int mt = (rows + 127) / 128;
-    // fc1 with the shared up projection in the same launch (a shared expert needs a latent layer)
-    if (p.L)
-        hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * ((p.L + p.SI) / 128))), dim3(256), 0, st, p, p.x,
-                           p.fc1, p.L, p.H);
+    // 256 x 256 tiles for a projection of N outputs once they alone fill about the machine
+    const auto big = [&](int N) { return N % 256 == 0 && (long)((rows + 255) / 256) * (N / 256) * 4 >= 3L * h->cus; };
+    const auto big_tiles = [&](int N) { return grid8((long)((rows + 255) / 256) * (N / 256)); };
+    // fc1 with the shared up projection in the same launch (a shared expert needs a latent
+    // layer), or the shared up projection in big tiles and fc1 alone
+    if (p.L) {
+        if (p.SI && big(p.SI)) {
+            hipLaunchKernelGGL(pf_gemm_big_kernel<1>, dim3(big_tiles(p.SI)), dim3(512), 0, st, p, p.x, p.su, p.SI, p.H);
+            LayerParams q = p;
+            q.SI = 0;   // the fc1 launch's tiles only
+            hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * (p.L / 128))), dim3(256), 0, st, q, p.x,
+                               p.fc1, p.L, p.H);
+        } else {
+            hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * ((p.L + p.SI) / 128))), dim3(256), 0, st, p,
+                               p.x, p.fc1, p.L, p.H);
+        }
+    }
     // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
     const long max_tiles = (NP + 63) / 64 + (E < NP ? E : NP);
     // dynamic LDS: the tile's scales and biases, 256 outputs x (inputs / 64) groups each (up
@@ -840,11 +855,15 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
                        (unsigned)(2 * 256 * (p.D / 64) * 2), st, p);
     hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(max_tiles * ((p.D + 255) / 256))), dim3(256),
                        (unsigned)(2 * 256 * (p.I / 64) * 2), st, p);
-    if (p.SI)
+    if (p.SI && big(p.H))
+        hipLaunchKernelGGL(pf_gemm_big_kernel<2>, dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.shact, p.sd, p.H, p.SI);
+    else if (p.SI)
         hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
                            p.H, p.SI);
     hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)(((long)rows * (p.D / 4) + 255) / 256)), dim3(256), 0, st, p);
-    if (p.L)
+    if (p.L && big(p.H))
+        hipLaunchKernelGGL(pf_gemm_big_kernel<3>, dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.comb, p.fc2, p.H, p.L);
+    else if (p.L)
         hipLaunchKernelGGL(pf_gemm_kernel<3>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.comb, p.fc2,
                            p.H, p.L);
     const hipError_t e = hipGetLastError();

@@ -243,13 +243,41 @@ struct PfGemmLds {
     uint4 b[2][PF_BN * 8];
 };
 
+// Outputs n .. n + 3 of row m from their fp32 sums v, through the launch's epilogue (epi is
+// EPI, or PF_SHUP for the shared up tiles of an fc1 launch): fc1 (rounded), shared up (relu^2
+// of the rounded sum, rounded), shared down (rounded), fc2 (out = rnd(x + rnd(rnd(sum) + sh))).
+template <int EPI>
+__device__ __forceinline__ void pf_store4(const LayerParams &p, int epi, int m, int n, f32x4 v) {
+    uint16_t o[4];
+    if constexpr (EPI == PF_FC2) {
+        const uint2 sh = *(const uint2 *)(p.shout + (size_t)m * p.H + n);
+        const uint2 xv = *(const uint2 *)(p.x + (size_t)m * p.H + n);
+        const uint32_t shw[2] = {sh.x, sh.y}, xw[2] = {xv.x, xv.y};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float s16 = bf2f(q & 1 ? shw[q >> 1] >> 16 : shw[q >> 1] & 0xFFFFu);
+            const float x16 = bf2f(q & 1 ? xw[q >> 1] >> 16 : xw[q >> 1] & 0xFFFFu);
+            const float mm = rnd(0, v[q]);
+            o[q] = f2bf(x16 + rnd(0, mm + (p.SI ? s16 : 0.0f)));
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = epi == PF_SHUP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
+    }
+    const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
+    uint16_t *dst = epi == PF_FC1 ? p.u + (size_t)m * p.L + n
+                  : epi == PF_SHUP ? p.shact + (size_t)m * p.SI + n
+                  : EPI == PF_SHDN ? p.shout + (size_t)m * p.H + n
+                                   : p.out + (size_t)m * p.H + n;
+    *(uint2 *)dst = ov;
+}
+
 // C[m][n] = sum_k X[m][k] W[n][k] for m < rows (X = [rows][K] bf16, W = [N][K] bf16), tiles
 // of 128 rows x 128 outputs, 64 inputs a step (double-buffered direct copies to LDS). Wave w
 // holds rows 64 (w & 1) .. +63 and outputs 64 (w >> 1) .. +63 as 4 x 4 MFMA 16x16x32 tiles
 // with the weights as the first operand, so lane l ends with outputs 4 (l >> 4) .. +3 of row
-// l & 15 of each tile; each output's sum runs over k in one fixed order. Epilogues: fc1
-// (rounded), shared up (relu^2 of the rounded sum, rounded), shared down (rounded), fc2
-// (out = rnd(x + rnd(rnd(sum) + sh))).
+// l & 15 of each tile; each output's sum runs over k in one fixed order (the epilogue is
+// pf_store4's). An fc1 launch also runs the shared up tiles when p.SI is set.
 template <int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_gemm_kernel(LayerParams p, const uint16_t *__restrict__ X,
                                                          const uint16_t *W, int N, int K) {
@@ -298,13 +326,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     issue(0, 0);
     for (int ks = 0; ks < nk; ++ks) {
         const int buf = ks & 1;
-        if (ks + 1 < nk) {
-            issue(ks + 1, buf ^ 1);
-            wait_vm<8>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();
+        wait_vm<0>();
+        __syncthreads();   // step ks is in LDS; every wave is done with step ks - 1
+        if (ks + 1 < nk) issue(ks + 1, buf ^ 1);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             uint4 xf[4], wf[4];
@@ -321,7 +345,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
                     acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, wf[ni]), __builtin_bit_cast(bf16x8, xf[mi]), acc[ni][mi], 0, 0, 0);
         }
-        __syncthreads();
     }
     // epilogue: lane l has outputs n .. n + 3 of row m of each tile
 #pragma unroll
@@ -329,32 +352,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
         const int m = m0 + wm * 64 + mi * 16 + (lane & 15);
         if (m >= p.rows) continue;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int n = n0 + wn * 64 + ni * 16 + 4 * (lane >> 4);
-            const f32x4 v = acc[ni][mi];
-            uint16_t o[4];
-            if constexpr (EPI == PF_FC2) {
-                const uint2 sh = *(const uint2 *)(p.shout + (size_t)m * p.H + n);
-                const uint2 xv = *(const uint2 *)(p.x + (size_t)m * p.H + n);
-                const uint32_t shw[2] = {sh.x, sh.y}, xw[2] = {xv.x, xv.y};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float s16 = bf2f(q & 1 ? shw[q >> 1] >> 16 : shw[q >> 1] & 0xFFFFu);
-                    const float x16 = bf2f(q & 1 ? xw[q >> 1] >> 16 : xw[q >> 1] & 0xFFFFu);
-                    const float mm = rnd(0, v[q]);
-                    o[q] = f2bf(x16 + rnd(0, mm + (p.SI ? s16 : 0.0f)));
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = epi == PF_SHUP ? f2bf(relu_sq(0, rnd(0, v[q]))) : f2bf(v[q]);
-            }
-            const uint2 ov = {pack2(o[0], o[1]), pack2(o[2], o[3])};
-            uint16_t *dst = epi == PF_FC1 ? p.u + (size_t)m * p.L + n
-                          : epi == PF_SHUP ? p.shact + (size_t)m * p.SI + n
-                          : EPI == PF_SHDN ? p.shout + (size_t)m * p.H + n
-                                           : p.out + (size_t)m * p.H + n;
-            *(uint2 *)dst = ov;
-        }
+        for (int ni = 0; ni < 4; ++ni) pf_store4<EPI>(p, epi, m, n0 + wn * 64 + ni * 16 + 4 * (lane >> 4), acc[ni][mi]);
     }
 }
 
@@ -362,6 +360,92 @@ template __global__ void pf_gemm_kernel<PF_FC1>(LayerParams, const uint16_t *, c
 template __global__ void pf_gemm_kernel<PF_SHUP>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 template __global__ void pf_gemm_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+
+// The same products in tiles of 256 rows x 256 outputs (8 waves; wave w holds rows 128 (w & 1)
+// .. +127 and outputs 64 (w >> 1) .. +63 as 4 x 8 MFMA 16x16x32 tiles), for passes with enough
+// rows to fill the machine with them: per product they copy half the bytes of the 128 x 128
+// tiles, which at this rate is what a compute unit's load path can deliver. Every output's
+// sum is formed as in pf_gemm_kernel (the same MFMA, operand order and input chunks, in the
+// same order), so both give the same bits. N is a multiple of 256; EPI is not PF_FC1 with
+// a shared up part (the launch carries one projection).
+constexpr int PF_GM = 256, PF_GN = 256;
+
+struct PfBigLds {
+    uint4 a[2][PF_GM * 8];   // [buffer][row][8 units of 16 bytes]: 64 inputs of each row
+    uint4 b[2][PF_GN * 8];
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(512) pf_gemm_big_kernel(LayerParams p, const uint16_t *__restrict__ X,
+                                                          const uint16_t *__restrict__ W, int N, int K) {
+    __shared__ PfBigLds L;
+    const int nbn = N / PF_GN, total = ((p.rows + PF_GM - 1) / PF_GM) * nbn;
+    const int tile = xcd_tile(total);
+    if (tile < 0) return;
+    const int m0 = (tile / nbn) * PF_GM, n0 = (tile % nbn) * PF_GN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave & 1, wn = wave >> 1;
+    // the copies: instruction i of wave w moves units 64 (8 i + w) .. +63 of each 2048-unit
+    // tile, lane l the unit u = 64 (8 i + w) + l: row u >> 3, stored swizzled
+    const uint16_t *xs[4], *ws[4];
+    int du[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int u = 64 * (8 * i + wave) + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
+        const int m = m0 + row < p.rows ? m0 + row : p.rows - 1;
+        xs[i] = X + (size_t)m * K + 8 * c;
+        ws[i] = W + (size_t)(n0 + row) * K + 8 * c;
+        du[i] = 64 * (8 * i + wave);
+    }
+    auto issue = [&](int ks, int buf) {
+        const int k0 = 64 * ks;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(xs[i] + k0, &L.a[buf][du[i]]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16(ws[i] + k0, &L.b[buf][du[i]]);
+    };
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int nk = K / 64;
+    issue(0, 0);
+    for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        wait_vm<0>();
+        __syncthreads();   // step ks is in LDS; every wave is done with step ks - 1
+        if (ks + 1 < nk) issue(ks + 1, buf ^ 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint4 xf[8], wf[4];
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+                xf[mi] = lds_ld16(&L.a[buf][swz(wm * 128 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                wf[ni] = lds_ld16(&L.b[buf][swz(wn * 64 + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 8; ++mi)
+                    acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wf[ni]), __builtin_bit_cast(bf16x8, xf[mi]), acc[ni][mi], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+        const int m = m0 + wm * 128 + mi * 16 + (lane & 15);
+        if (m >= p.rows) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) pf_store4<EPI>(p, EPI, m, n0 + wn * 64 + ni * 16 + 4 * (lane >> 4), acc[ni][mi]);
+    }
+}
+
+template __global__ void pf_gemm_big_kernel<PF_FC1>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_SHUP>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 
 // ------------------------------------------------------------------ routed experts
 

@@ -230,6 +230,26 @@ def test_prefill_4096_rows_bolt():
     _check_layer(d, arrays, "bolt 4096", sample=sample, alone=(0, 4095))
 
 
+def test_prefill_big_tiles_match_small_tiles():
+    """At 4096 rows the shared up and down projections and fc2 run in tiles of 256 rows x 256
+    outputs; passes of 512 rows run them in 128 x 128 tiles. Both sum each output in the same
+    order, so every row's shared expert stages and output are the same bits either way."""
+    rows, chunk = 4096, 512
+    d, arrays = next(synth.workload_layers(1, rows=rows))
+    lay, xd, out = _prefill(d, arrays)
+    got = out.cpu().numpy().view(np.uint16)
+    stages = {n: lay.stage(n, rows).copy() for n in ("latent", "shared_act", "shared_out")}
+    for c in range(0, rows, chunk):
+        o = torch.empty_like(xd[c:c + chunk])
+        lay.prefill(xd[c:c + chunk], o, chunk)
+        torch.cuda.synchronize()
+        lay.status()
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), got[c:c + chunk]), c
+        for n, full in stages.items():
+            assert np.array_equal(lay.stage(n, chunk), full[c:c + chunk]), (n, c)
+    lay.close()
+
+
 @pytest.mark.parametrize("rows", [70, 300])
 def test_prefill_graph_replays_match_eager(rows):
     """A prefill captured in a HIP graph gives the eager bits on every replay, with eager work
