@@ -451,16 +451,15 @@ template __global__ void pf_gemm_big_kernel<PF_FC2>(LayerParams, const uint16_t 
 
 constexpr int PF_EBN = 256;   // outputs per expert tile (64 per wave)
 
-// NS input steps (groups of 64 inputs) in LDS at once: NS - 1 copies in flight while one
-// is used.
-template <int NS>
+// Two input steps (groups of 64 inputs) in LDS: one copy in flight while the other is used.
 struct PfExpertLds {
-    uint4 a[NS][PF_BM * 8];        // [buffer][pick][8 units]: 64 inputs of each pick's row, as copied
-    uint32_t q[NS][PF_EBN * 8];    // [buffer][output][8 words]: 64 codes of each output row
+    uint4 a[2][PF_BM * 8];         // [buffer][pick][8 units]: 64 inputs of each pick's row, as copied
+    uint32_t q[2][PF_EBN * 8];     // [buffer][output][8 words]: 64 codes of each output row
     uint4 ap[PF_BM * 8];           // the step's inputs as pairs (x[i], x[i + 4]) of each 8 (unit c of
                                    // pick r at swz(r, c))
     float xs[PF_BM];               // the step's group sum of each pick
     float sc[PF_EBN], cb[PF_EBN];  // the step's scale and bias - 128 scale of each output
+    uint32_t scp[2][PF_EBN], bcp[2][PF_EBN];   // scales and biases of two groups of each output
 };
 
 // Tile: picks [m0, m0 + 64) of expert e's list x outputs [n0, n0 + 256) of its up (UP) or
@@ -472,14 +471,12 @@ struct PfExpertLds {
 // and sums each pick's group once (in a fixed order), then wave w multiplies outputs
 // 64 w .. +63 for all 64 picks (4 x 4 MFMA 16x16 tiles). MFMA step s of a group takes input
 // chunk 2 (l >> 4) + s in lane l's group of 16 -- any order of k serves when both operands
-// use the same. Up: eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum).
-template <bool UP>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_expert_kernel(LayerParams p) {
-    constexpr int NS = UP ? 3 : 2;   // down: two (its scales take twice the LDS)
-    __shared__ PfExpertLds<NS> L;
-    // scales and biases of the tile's outputs, [group][output] (dynamic LDS: 2 * G * 256
-    // halves, sized by the host)
-    extern __shared__ uint16_t dyn[];
+// use the same. Up: eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum). OCC workgroups
+// share a compute unit (3 hides more latency, at the price of a few spilled registers; 2
+// when the launch has too few tiles for three to a compute unit to pay).
+template <bool UP, int OCC>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8))) pf_expert_kernel(LayerParams p) {
+    __shared__ PfExpertLds L;
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
     const int nbn = (N + PF_EBN - 1) / PF_EBN, G = Kin >> 6;
     const int total_tiles = p.pf_tile[p.E];
@@ -493,16 +490,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int tid = threadIdx.x, wn = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
     auto pick = [&](int m) { return p.pf_pairs[list0 + (m0 + m < cnt ? m0 + m : cnt - 1)]; };
     auto out_row = [&](int nl) { return n0 + nl < N ? n0 + nl : N - 1; };
-    // scales and biases, transposed to [group][output]
     const size_t eN = (size_t)e * N;
     const uint16_t *S = UP ? p.up_s : p.dn_s, *Bs = UP ? p.up_b : p.dn_b;
-    uint16_t *Ls = dyn, *Lb = dyn + PF_EBN * G;
-    for (int i = tid; i < PF_EBN * G; i += 256) {
-        const int nl = i / G, gq = i % G;
-        const size_t off = (eN + out_row(nl)) * G + gq;
-        Ls[gq * PF_EBN + nl] = S[off];
-        Lb[gq * PF_EBN + nl] = Bs[off];
-    }
+    const uint16_t *sp = S + (eN + out_row(tid)) * G, *bp = Bs + (eN + out_row(tid)) * G;
+    // the scales and biases of groups 2 j and 2 j + 1 of every output, copied into pair buffer
+    // j & 1 (G is even): lane l of wave w copies those of output 64 w + l
+    auto issue_sc = [&](int j) {
+        __builtin_amdgcn_global_load_lds((const void *)(sp + 2 * j),
+                                         (__attribute__((address_space(3))) void *)&L.scp[j & 1][64 * wn], 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(bp + 2 * j),
+                                         (__attribute__((address_space(3))) void *)&L.bcp[j & 1][64 * wn], 4, 0, 0);
+    };
+    issue_sc(0);
     // copies per step: the picks' inputs (64 x 128 bytes: two 1 KB instructions a wave, unit
     // u = 128 w + 64 i + l is chunk u & 7 of pick row u >> 3) and the codes (256 x 32 bytes: two
     // a wave, unit u is half u & 1 of output row u >> 1)
@@ -527,17 +526,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NS - 1; ++j)
-        if (j < G) issue(j, j);
+    issue(0, 0);
     for (int g = 0; g < G; ++g) {
-        const int buf = g % NS;
-        // the steps issued after g may stay in flight (4 copy instructions each)
-        const int behind = G - 1 - g < NS - 2 ? G - 1 - g : NS - 2;
-        if (behind >= 1) wait_vm<4>();
-        else wait_vm<0>();
-        __syncthreads();   // step g is in LDS; every wave is done with step g - 1
-        if (g + NS - 1 < G) issue(g + NS - 1, (g + NS - 1) % NS);
+        const int buf = g & 1;
+        wait_vm<0>();
+        __syncthreads();   // step g and its scales are in LDS; every wave is done with step g - 1
+        if (g + 1 < G) issue(g + 1, buf ^ 1);
+        if ((g & 1) && g + 1 < G) issue_sc((g + 1) >> 1);
         {
             // thread t: 16 inputs (units 2 (t & 3), +1) of pick t >> 2
             const int r = tid >> 2, part = tid & 3;
@@ -561,9 +556,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
             lds_st16(&L.ap[swz(r, 2 * part + 1)], p1);
             if (part == 0) L.xs[r] = sx;
             // thread t: output t's scale and bias for this group
-            const float sct = bf2f(Ls[g * PF_EBN + tid]);
+            const uint32_t sw = L.scp[(g >> 1) & 1][tid], bw = L.bcp[(g >> 1) & 1][tid];
+            const float sct = bf2f(g & 1 ? sw >> 16 : sw & 0xFFFFu);
             L.sc[tid] = sct;
-            L.cb[tid] = __builtin_fmaf(-128.0f, sct, bf2f(Lb[g * PF_EBN + tid]));
+            L.cb[tid] = __builtin_fmaf(-128.0f, sct, bf2f(g & 1 ? bw >> 16 : bw & 0xFFFFu));
         }
         __syncthreads();
         if (active) {
@@ -626,8 +622,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
 }
 
-template __global__ void pf_expert_kernel<true>(LayerParams);
-template __global__ void pf_expert_kernel<false>(LayerParams);
+template __global__ void pf_expert_kernel<true, 2>(LayerParams);
+template __global__ void pf_expert_kernel<false, 2>(LayerParams);
+template __global__ void pf_expert_kernel<true, 3>(LayerParams);
+template __global__ void pf_expert_kernel<false, 3>(LayerParams);
 
 // ------------------------------------------------------------------ combine
 
