@@ -33,7 +33,7 @@ __global__ void pf_route_kernel(LayerParams p);
 __global__ void pf_sched_kernel(LayerParams p);
 template <int EPI>
 __global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
-template <bool UP, int OCC> __global__ void pf_expert_kernel(LayerParams p);
+template <bool UP> __global__ void pf_expert_kernel(LayerParams p);
 template <int EPI>
 __global__ void pf_gemm_big_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 __global__ void pf_combine_kernel(LayerParams p);
@@ -841,14 +841,13 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     }
     // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
     const long max_tiles = (NP + 63) / 64 + (E < NP ? E : NP);
-    // three expert workgroups to a compute unit once the launch spans several rounds of them
-    // (fewer rounds lose more to the last one's idle slots than the third workgroup gains)
+    // three expert workgroups (50 KB of LDS each) to a compute unit once the launch spans
+    // several rounds of them; otherwise 24 KB of unused dynamic LDS holds it to two (with few
+    // rounds the last one's idle slots cost more than the third workgroup gains)
     const long up_wgs = max_tiles * ((p.I + 255) / 256), dn_wgs = max_tiles * ((p.D + 255) / 256);
-    const auto occ3 = [&](long wgs) { return wgs >= 12L * h->cus; };
-    if (occ3(up_wgs)) hipLaunchKernelGGL((pf_expert_kernel<true, 3>), dim3(grid8(up_wgs)), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((pf_expert_kernel<true, 2>), dim3(grid8(up_wgs)), dim3(256), 0, st, p);
-    if (occ3(dn_wgs)) hipLaunchKernelGGL((pf_expert_kernel<false, 3>), dim3(grid8(dn_wgs)), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((pf_expert_kernel<false, 2>), dim3(grid8(dn_wgs)), dim3(256), 0, st, p);
+    const auto pad = [&](long wgs) { return wgs >= 12L * h->cus ? 0u : 24u * 1024u; };
+    hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(up_wgs)), dim3(256), pad(up_wgs), st, p);
+    hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(dn_wgs)), dim3(256), pad(dn_wgs), st, p);
     if (p.SI && big(p.H))
         hipLaunchKernelGGL(pf_gemm_big_kernel<2>, dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.shact, p.sd, p.H, p.SI);
     else if (p.SI)

@@ -457,8 +457,9 @@ struct PfExpertLds {
     uint32_t q[2][PF_EBN * 8];     // [buffer][output][8 words]: 64 codes of each output row
     uint4 ap[PF_BM * 8];           // the step's inputs as pairs (x[i], x[i + 4]) of each 8 (unit c of
                                    // pick r at swz(r, c))
-    float xs[PF_BM];               // the step's group sum of each pick
-    float sc[PF_EBN], cb[PF_EBN];  // the step's scale and bias - 128 scale of each output
+    float sc[PF_EBN];              // the step's scale of each output
+    float xs4[4][PF_BM];           // group sums of each pick, for groups g with g % 4 = slot
+    float cb4[4][PF_EBN];          // bias - 128 scale of each output, for the same groups
     uint32_t scp[2][PF_EBN], bcp[2][PF_EBN];   // scales and biases of two groups of each output
 };
 
@@ -466,16 +467,17 @@ struct PfExpertLds {
 // down projection, one group of 64 inputs (of the 4-bit codes) a step. Per group g and
 // output n the tile forms, per pick, a = sum over the group of (128 + q) x (MFMA: the codes
 // decoded into bf16 128 + q exactly, the inputs reordered to the codes' pairing) and sx =
-// sum of x, and adds scale * a + (bias - 128 scale) * sx -- the group's share of sum(w x)
-// with w = q scale + bias. A step: its copies wait, then the workgroup reorders the inputs
-// and sums each pick's group once (in a fixed order), then wave w multiplies outputs
+// sum of x; sum(w x) with w = q scale + bias is the sum over groups of scale * a (added
+// group by group) and of (bias - 128 scale) * sx (added four groups at a time as one fp32
+// MFMA 16x16x4 of those factors). A step: its copies wait, then the workgroup reorders the
+// inputs and sums each pick's group once (in a fixed order), then wave w multiplies outputs
 // 64 w .. +63 for all 64 picks (4 x 4 MFMA 16x16 tiles). MFMA step s of a group takes input
 // chunk 2 (l >> 4) + s in lane l's group of 16 -- any order of k serves when both operands
-// use the same. Up: eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum). OCC workgroups
-// share a compute unit (3 hides more latency, at the price of a few spilled registers; 2
-// when the launch has too few tiles for three to a compute unit to pay).
-template <bool UP, int OCC>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8))) pf_expert_kernel(LayerParams p) {
+// use the same. Up: eact = rnd(relu^2(rnd(sum))); down: eout = rnd(sum). Three workgroups
+// fit a compute unit; the host holds a launch to two with unused dynamic LDS when it has too
+// few tiles for a third to pay.
+template <bool UP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) pf_expert_kernel(LayerParams p) {
     __shared__ PfExpertLds L;
     const int Kin = UP ? p.D : p.I, N = UP ? p.I : p.D;
     const int nbn = (N + PF_EBN - 1) / PF_EBN, G = Kin >> 6;
@@ -554,22 +556,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8
                               __builtin_amdgcn_perm(v1.w, v1.y, 0x05040100u), __builtin_amdgcn_perm(v1.w, v1.y, 0x07060302u)};
             lds_st16(&L.ap[swz(r, 2 * part)], p0);
             lds_st16(&L.ap[swz(r, 2 * part + 1)], p1);
-            if (part == 0) L.xs[r] = sx;
+            const int slot = g & 3;
+            if (part == 0) L.xs4[slot][r] = sx;
             // thread t: output t's scale and bias for this group
             const uint32_t sw = L.scp[(g >> 1) & 1][tid], bw = L.bcp[(g >> 1) & 1][tid];
             const float sct = bf2f(g & 1 ? sw >> 16 : sw & 0xFFFFu);
             L.sc[tid] = sct;
-            L.cb[tid] = __builtin_fmaf(-128.0f, sct, bf2f(g & 1 ? bw >> 16 : bw & 0xFFFFu));
+            L.cb4[slot][tid] = __builtin_fmaf(-128.0f, sct, bf2f(g & 1 ? bw >> 16 : bw & 0xFFFFu));
+            // the last group: the slots after it add nothing
+            if (g == G - 1)
+                for (int z = slot + 1; z < 4; ++z) {
+                    L.cb4[z][tid] = 0.0f;
+                    if (tid < PF_BM) L.xs4[z][tid] = 0.0f;
+                }
         }
         __syncthreads();
         if (active) {
             uint4 xf[4][2];
-            float sxm[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
                 xf[mi][0] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg)]);
                 xf[mi][1] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg + 1)]);
-                sxm[mi] = L.xs[16 * mi + lr];
             }
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
@@ -590,16 +597,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8
                     a[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf1),
                                                                     __builtin_bit_cast(bf16x8, xf[mi][1]), a[mi], 0, 0, 0);
                 }
-                // scale and bias - 128 scale of the 4 outputs this lane ends with
+                // the scale of the 4 outputs this lane ends with
                 const f32x4 sc = *(const f32x4 *)&L.sc[nl + 4 * lg];
-                const f32x4 cb = *(const f32x4 *)&L.cb[nl + 4 * lg];
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float v = __builtin_fmaf(sc[q], a[mi][q], acc[ni][mi][q]);
-                        acc[ni][mi][q] = __builtin_fmaf(cb[q], sxm[mi], v);
-                    }
+                    for (int q = 0; q < 4; ++q) acc[ni][mi][q] = __builtin_fmaf(sc[q], a[mi][q], acc[ni][mi][q]);
+            }
+            if ((g & 3) == 3 || g == G - 1) {
+                // the bias terms of the last four groups: lane l supplies (bias - 128 scale) of
+                // output l & 15 of the tile and the group sum of pick l & 15, group slot l >> 4
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const float cbl = L.cb4[lg][64 * wn + 16 * ni + lr];
+#pragma unroll
+                    for (int mi = 0; mi < 4; ++mi)
+                        acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(cbl, L.xs4[lg][16 * mi + lr], acc[ni][mi], 0, 0, 0);
+                }
             }
         }
     }
@@ -622,10 +636,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, 8
     }
 }
 
-template __global__ void pf_expert_kernel<true, 2>(LayerParams);
-template __global__ void pf_expert_kernel<false, 2>(LayerParams);
-template __global__ void pf_expert_kernel<true, 3>(LayerParams);
-template __global__ void pf_expert_kernel<false, 3>(LayerParams);
+template __global__ void pf_expert_kernel<true>(LayerParams);
+template __global__ void pf_expert_kernel<false>(LayerParams);
 
 // ------------------------------------------------------------------ combine
 
