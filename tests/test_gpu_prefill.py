@@ -230,23 +230,26 @@ def test_prefill_4096_rows_bolt():
     _check_layer(d, arrays, "bolt 4096", sample=sample, alone=(0, 4095))
 
 
-def test_prefill_big_tiles_match_small_tiles():
-    """At 4096 rows the shared up and down projections and fc2 run in tiles of 256 rows x 256
-    outputs; passes of 512 rows run them in 128 x 128 tiles. Both sum each output in the same
-    order, so every row's shared expert stages and output are the same bits either way."""
-    rows, chunk = 4096, 512
+@pytest.mark.parametrize("rows", [4096, 3500])
+def test_prefill_big_tiles_match_small_tiles(rows):
+    """At 4096 rows (and at 3500, whose last tile of 256 rows holds 172) the shared up and
+    down projections and fc2 run in tiles of 256 rows x 256 outputs; passes of at most 512
+    rows run them in 128 x 128 tiles. Both sum each output in the same order, so every row's
+    shared expert stages and output are the same bits either way."""
+    chunk = 512
     d, arrays = next(synth.workload_layers(1, rows=rows))
     lay, xd, out = _prefill(d, arrays)
     got = out.cpu().numpy().view(np.uint16)
     stages = {n: lay.stage(n, rows).copy() for n in ("latent", "shared_act", "shared_out")}
     for c in range(0, rows, chunk):
-        o = torch.empty_like(xd[c:c + chunk])
-        lay.prefill(xd[c:c + chunk], o, chunk)
+        n_rows = min(chunk, rows - c)
+        o = torch.empty_like(xd[c:c + n_rows])
+        lay.prefill(xd[c:c + n_rows], o, n_rows)
         torch.cuda.synchronize()
         lay.status()
-        assert np.array_equal(o.cpu().numpy().view(np.uint16), got[c:c + chunk]), c
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), got[c:c + n_rows]), c
         for n, full in stages.items():
-            assert np.array_equal(lay.stage(n, chunk), full[c:c + chunk]), (n, c)
+            assert np.array_equal(lay.stage(n, n_rows), full[c:c + n_rows]), (n, c)
     lay.close()
 
 
