@@ -34,7 +34,7 @@ __global__ void pf_sched_kernel(LayerParams p);
 template <int EPI>
 __global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 template <bool UP> __global__ void pf_expert_kernel(LayerParams p);
-template <int EPI>
+template <int EPI, int TN>
 __global__ void pf_gemm_big_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 __global__ void pf_combine_kernel(LayerParams p);
 }  // namespace moe
@@ -826,10 +826,17 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     const auto big = [&](int N) { return N % 256 == 0 && (long)((rows + 255) / 256) * (N / 256) * 4 >= 3L * h->cus; };
     const auto big_tiles = [&](int N) { return grid8((long)((rows + 255) / 256) * (N / 256)); };
     // fc1 with the shared up projection in the same launch (a shared expert needs a latent
-    // layer), or the shared up projection in big tiles and fc1 alone
-    if (p.L) {
+    // layer): as one matrix in big tiles of 320 outputs when those fill about the machine,
+    // else the shared up projection in big tiles and fc1 alone, else 128 x 128 tiles
+    const int NC = p.L + p.SI;
+    const long cat_tiles = (long)((rows + 255) / 256) * (NC / 320);
+    if (p.L && p.SI && NC % 320 == 0 && cat_tiles * 4 >= 3L * h->cus) {
+        hipLaunchKernelGGL((pf_gemm_big_kernel<0, 320>), dim3(grid8(cat_tiles)), dim3(512), 0, st, p, p.x, p.fc1, NC,
+                           p.H);
+    } else if (p.L) {
         if (p.SI && big(p.SI)) {
-            hipLaunchKernelGGL(pf_gemm_big_kernel<1>, dim3(big_tiles(p.SI)), dim3(512), 0, st, p, p.x, p.su, p.SI, p.H);
+            hipLaunchKernelGGL((pf_gemm_big_kernel<1, 256>), dim3(big_tiles(p.SI)), dim3(512), 0, st, p, p.x, p.su,
+                               p.SI, p.H);
             LayerParams q = p;
             q.SI = 0;   // the fc1 launch's tiles only
             hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * (p.L / 128))), dim3(256), 0, st, q, p.x,
@@ -849,13 +856,15 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     hipLaunchKernelGGL(pf_expert_kernel<true>, dim3(grid8(up_wgs)), dim3(256), pad(up_wgs), st, p);
     hipLaunchKernelGGL(pf_expert_kernel<false>, dim3(grid8(dn_wgs)), dim3(256), pad(dn_wgs), st, p);
     if (p.SI && big(p.H))
-        hipLaunchKernelGGL(pf_gemm_big_kernel<2>, dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.shact, p.sd, p.H, p.SI);
+        hipLaunchKernelGGL((pf_gemm_big_kernel<2, 256>), dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.shact, p.sd, p.H,
+                           p.SI);
     else if (p.SI)
         hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
                            p.H, p.SI);
     hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)(((long)rows * (p.D / 4) + 255) / 256)), dim3(256), 0, st, p);
     if (p.L && big(p.H))
-        hipLaunchKernelGGL(pf_gemm_big_kernel<3>, dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.comb, p.fc2, p.H, p.L);
+        hipLaunchKernelGGL((pf_gemm_big_kernel<3, 256>), dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.comb, p.fc2, p.H,
+                           p.L);
     else if (p.L)
         hipLaunchKernelGGL(pf_gemm_kernel<3>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.comb, p.fc2,
                            p.H, p.L);

@@ -361,52 +361,59 @@ template __global__ void pf_gemm_kernel<PF_SHUP>(LayerParams, const uint16_t *, 
 template __global__ void pf_gemm_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 
-// The same products in tiles of 256 rows x 256 outputs (8 waves; wave w holds rows 128 (w & 1)
-// .. +127 and outputs 64 (w >> 1) .. +63 as 4 x 8 MFMA 16x16x32 tiles), for passes with enough
-// rows to fill the machine with them: per product they copy half the bytes of the 128 x 128
-// tiles, which at this rate is what a compute unit's load path can deliver. Every output's
-// sum is formed as in pf_gemm_kernel (the same MFMA, operand order and input chunks, in the
-// same order), so both give the same bits. N is a multiple of 256; EPI is not PF_FC1 with
-// a shared up part (the launch carries one projection).
-constexpr int PF_GM = 256, PF_GN = 256;
+// The same products in tiles of 256 rows x TN outputs (8 waves; wave w holds rows 128 (w & 1)
+// .. +127 and outputs TN / 4 (w >> 1) .. + TN / 4 - 1 as MFMA 16x16x32 tiles), for passes with
+// enough rows to fill the machine with them: per product they copy about half the bytes of
+// the 128 x 128 tiles. Every output's sum is formed as in pf_gemm_kernel (the same MFMA,
+// operand order and input chunks, in the same order), so both give the same bits. N is a
+// multiple of TN. An fc1 launch with p.SI set carries fc1 and the shared up projection as one
+// matrix of L + SI rows (fc1's rows first), in tiles of 320 outputs: 256 tiles at 4096 rows
+// of the Bolt-like layer, one per compute unit.
+constexpr int PF_GM = 256;
 
+template <int TN>
 struct PfBigLds {
     uint4 a[2][PF_GM * 8];   // [buffer][row][8 units of 16 bytes]: 64 inputs of each row
-    uint4 b[2][PF_GN * 8];
+    uint4 b[2][TN * 8];
 };
 
-template <int EPI>
+template <int EPI, int TN>
 __global__ void __launch_bounds__(512) pf_gemm_big_kernel(LayerParams p, const uint16_t *__restrict__ X,
                                                           const uint16_t *__restrict__ W, int N, int K) {
-    __shared__ PfBigLds L;
-    const int nbn = N / PF_GN, total = ((p.rows + PF_GM - 1) / PF_GM) * nbn;
+    constexpr int NW = TN / 4, NIT = NW / 16, WI = TN / 64;   // outputs, MFMA tiles, copies a wave
+    constexpr bool CAT = EPI == PF_FC1;   // fc1 rows, then the shared up rows
+    __shared__ PfBigLds<TN> L;
+    const int nbn = N / TN, total = ((p.rows + PF_GM - 1) / PF_GM) * nbn;
     const int tile = xcd_tile(total);
     if (tile < 0) return;
-    const int m0 = (tile / nbn) * PF_GM, n0 = (tile % nbn) * PF_GN;
+    const int m0 = (tile / nbn) * PF_GM, n0 = (tile % nbn) * TN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave & 1, wn = wave >> 1;
-    // the copies: instruction i of wave w moves units 64 (8 i + w) .. +63 of each 2048-unit
-    // tile, lane l the unit u = 64 (8 i + w) + l: row u >> 3, stored swizzled
-    const uint16_t *xs[4], *ws[4];
-    int du[4];
+    // the copies: instruction i of wave w moves units 64 (8 i + w) .. +63 of each tile, lane l
+    // the unit u = 64 (8 i + w) + l: row u >> 3, stored swizzled
+    const uint16_t *xs[4], *ws[WI];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int u = 64 * (8 * i + wave) + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
+        const int u = 64 * (8 * i + wave) + lane, row = u >> 3, c = (u & 7) ^ (row & 7);
         const int m = m0 + row < p.rows ? m0 + row : p.rows - 1;
         xs[i] = X + (size_t)m * K + 8 * c;
-        ws[i] = W + (size_t)(n0 + row) * K + 8 * c;
-        du[i] = 64 * (8 * i + wave);
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+        const int u = 64 * (8 * i + wave) + lane, row = u >> 3, c = (u & 7) ^ (row & 7);
+        const int n = n0 + row;
+        ws[i] = (CAT && n >= p.L ? p.su + (size_t)(n - p.L) * K : W + (size_t)n * K) + 8 * c;
     }
     auto issue = [&](int ks, int buf) {
         const int k0 = 64 * ks;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(xs[i] + k0, &L.a[buf][du[i]]);
+        for (int i = 0; i < 4; ++i) lds_dma16(xs[i] + k0, &L.a[buf][64 * (8 * i + wave)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(ws[i] + k0, &L.b[buf][du[i]]);
+        for (int i = 0; i < WI; ++i) lds_dma16(ws[i] + k0, &L.b[buf][64 * (8 * i + wave)]);
     };
-    f32x4 acc[4][8];
+    f32x4 acc[NIT][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NIT; ++a)
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const int nk = K / 64;
@@ -418,15 +425,15 @@ __global__ void __launch_bounds__(512) pf_gemm_big_kernel(LayerParams p, const u
         if (ks + 1 < nk) issue(ks + 1, buf ^ 1);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            uint4 xf[8], wf[4];
+            uint4 xf[8], wf[NIT];
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi)
                 xf[mi] = lds_ld16(&L.a[buf][swz(wm * 128 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                wf[ni] = lds_ld16(&L.b[buf][swz(wn * 64 + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+            for (int ni = 0; ni < NIT; ++ni)
+                wf[ni] = lds_ld16(&L.b[buf][swz(wn * NW + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
+            for (int ni = 0; ni < NIT; ++ni)
 #pragma unroll
                 for (int mi = 0; mi < 8; ++mi)
                     acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -438,14 +445,18 @@ __global__ void __launch_bounds__(512) pf_gemm_big_kernel(LayerParams p, const u
         const int m = m0 + wm * 128 + mi * 16 + (lane & 15);
         if (m >= p.rows) continue;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) pf_store4<EPI>(p, EPI, m, n0 + wn * 64 + ni * 16 + 4 * (lane >> 4), acc[ni][mi]);
+        for (int ni = 0; ni < NIT; ++ni) {
+            const int n = n0 + wn * NW + ni * 16 + 4 * (lane >> 4);   // L is a multiple of 4
+            if (CAT && n >= p.L) pf_store4<EPI>(p, PF_SHUP, m, n - p.L, acc[ni][mi]);
+            else pf_store4<EPI>(p, EPI, m, n, acc[ni][mi]);
+        }
     }
 }
 
-template __global__ void pf_gemm_big_kernel<PF_FC1>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_big_kernel<PF_SHUP>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_big_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_big_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_FC1, 320>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_SHUP, 256>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_SHDN, 256>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_big_kernel<PF_FC2, 256>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 
 // ------------------------------------------------------------------ routed experts
 
