@@ -427,15 +427,17 @@ __device__ __forceinline__ int count_greater_any(const uint64_t *v, int n, uint6
     return c;
 }
 
-template <int NT>
+// ME: the most experts the item serves (the candidates never outnumber the experts: at most
+// top_k per kept group, or top_k per block of 64 when blocked, with top_k <= 16)
+template <int NT, int ME = MAX_EXPERTS>
 struct RouteLds {
-    float s[MAX_EXPERTS];
-    float b[MAX_EXPERTS];
-    alignas(16) uint64_t key[MAX_EXPERTS];    // rank keys of the biased scores
-    alignas(16) uint64_t ckey[MAX_EXPERTS];   // the candidates' keys
-    alignas(16) uint64_t gkey[256];           // rank keys of the group scores
-    int rank[MAX_EXPERTS];                    // candidate ranks, summed over counting threads
-    int inr[MAX_EXPERTS];                     // each expert's rank inside its group
+    float s[ME];
+    float b[ME];
+    alignas(16) uint64_t key[ME];    // rank keys of the biased scores
+    alignas(16) uint64_t ckey[ME];   // the candidates' keys
+    alignas(16) uint64_t gkey[256];  // rank keys of the group scores
+    int rank[ME];                    // candidate ranks, summed over counting threads
+    int inr[ME];                     // each expert's rank inside its group
     int top[256][2];              // the two best members of each group
     int keep[256];                // 1: the group is kept
     int picks[MAX_TOPK];
@@ -447,8 +449,8 @@ struct RouteLds {
 // elements whose 64-bit key is larger, counted by the element's own thread from LDS (group
 // keys, up to 64 groups: by the group's lane of every wave, from the other lanes) -- keys
 // are unique, so ranks are a permutation and no thread waits on another's choice.
-template <int NT>
-__device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds<NT> &L) {
+template <int NT, int ME = MAX_EXPERTS>
+__device__ __forceinline__ void route_item(const LayerParams &p, int r, RouteLds<NT, ME> &L) {
     const int tid = threadIdx.x;
     const int E = p.E, G = p.G, per = p.E / p.G;
     for (int e = tid; e < E; e += NT) {

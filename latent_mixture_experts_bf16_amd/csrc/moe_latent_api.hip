@@ -29,7 +29,7 @@ __global__ void moe_lm_head_kernel(LayerParams p, const uint16_t *W, const uint1
 __global__ void moe_front_kernel(LayerParams p, int nwg);
 // the prefill (prefill_kernels.hip)
 template <bool F32W> __global__ void pf_gate_kernel(LayerParams p);
-__global__ void pf_route_kernel(LayerParams p);
+template <int ME> __global__ void pf_route_kernel(LayerParams p);
 __global__ void pf_sched_kernel(LayerParams p);
 template <int EPI>
 __global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
@@ -819,7 +819,8 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
         if (p.router_f32) hipLaunchKernelGGL(pf_gate_kernel<true>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
         else hipLaunchKernelGGL(pf_gate_kernel<false>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
     }
-    hipLaunchKernelGGL(pf_route_kernel, dim3(rows), dim3(WG_THREADS), 0, st, p);
+    if (E <= 256) hipLaunchKernelGGL(pf_route_kernel<256>, dim3(rows), dim3(WG_THREADS), 0, st, p);
+    else hipLaunchKernelGGL(pf_route_kernel<MAX_EXPERTS>, dim3(rows), dim3(WG_THREADS), 0, st, p);
     hipLaunchKernelGGL(pf_sched_kernel, dim3((NP + 1023) / 1024), dim3(WG_THREADS), 0, st, p);
     const int mt = (rows + 127) / 128;
     // 256 x 256 tiles for a projection of N outputs once they alone fill about the machine

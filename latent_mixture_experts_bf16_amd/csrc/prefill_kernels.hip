@@ -16,7 +16,7 @@
 //            pick ids scattered into the per-expert lists
 //   gemm     fc1 (u = rnd(W1 x)) and shared up (rnd(relu^2(rnd(Su x)))) in one launch: 128 x 128
 //            tiles
-//   expert   routed up / down: tiles of 64 picks of one expert x 128 outputs, 4-bit codes
+//   expert   routed up / down: tiles of 64 picks of one expert x 256 outputs, 4-bit codes
 //            decoded in registers, MFMA per group of 64 inputs, then scale and bias per group
 //   gemm     shared down (rnd(Sd a))
 //   combine  every row (the decode combine: lane order and rounding)
@@ -137,10 +137,11 @@ __global__ void __launch_bounds__(256) pf_gate_kernel(LayerParams p) {
 // One row per workgroup: the decode route item, then each pick counts itself in its expert's
 // list (its place there is the count before it; the order of the places inside a list does
 // not change any result, since every row of a tile is its own MFMA column).
+template <int ME>
 __global__ void __launch_bounds__(WG_THREADS) pf_route_kernel(LayerParams p) {
-    __shared__ RouteLds<WG_THREADS> lds;
+    __shared__ RouteLds<WG_THREADS, ME> lds;   // E <= ME (a small table lets more rows run at once)
     const int r = blockIdx.x;
-    route_item<WG_THREADS>(p, r, lds);
+    route_item<WG_THREADS, ME>(p, r, lds);
     __syncthreads();
     if (threadIdx.x < p.K) {
         const int i = r * p.K + (int)threadIdx.x;
@@ -676,6 +677,8 @@ __global__ void __launch_bounds__(256) pf_combine_kernel(LayerParams p) {
     *(uint2 *)((p.L ? p.comb + (size_t)r * p.D : p.out + (size_t)r * p.H) + d) = ov;
 }
 
+template __global__ void pf_route_kernel<256>(LayerParams);
+template __global__ void pf_route_kernel<MAX_EXPERTS>(LayerParams);
 template __global__ void pf_gate_kernel<false>(LayerParams);
 template __global__ void pf_gate_kernel<true>(LayerParams);
 

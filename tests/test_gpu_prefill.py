@@ -162,6 +162,13 @@ def test_prefill_matches_decode_within_bar():
     lay.close()
 
 
+def test_prefill_496_experts():
+    """More than 256 experts (the route's large table): the Bolt-like layer with 496 experts
+    at 40 rows, routing bit for bit and outputs within the bar on every row."""
+    d, arrays = next(synth.workload_layers(2, rows=40))
+    _check_layer(d, arrays, "bolt E496", stage_rows=(0, 39), alone=(17,))
+
+
 def test_prefill_non_latent_bf16_layer():
     dims = synth.LayerDims(hidden=1024, latent=0, n_experts=32, n_group=1, topk_group=1, top_k=4,
                            expert_inter=512, shared_inter=0)
