@@ -501,6 +501,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int e = tcode >> 8;
     const int list0 = p.pf_off[e], cnt = p.pf_off[e + 1] - list0;
     const int m0 = (tcode & 255) * PF_BM;
+    // 16-pick MFMA tiles that hold picks: a tile short of 64 picks (the last of its expert)
+    // skips the products, copies and reordering of the empty ones
+    const int mlim = cnt - m0 >= PF_BM ? 4 : (cnt - m0 + 15) >> 4;
     const int tid = threadIdx.x, wn = tid >> 6, lane = tid & 63, lg = lane >> 4, lr = lane & 15;
     auto pick = [&](int m) { return p.pf_pairs[list0 + (m0 + m < cnt ? m0 + m : cnt - 1)]; };
     auto out_row = [&](int nl) { return n0 + nl < N ? n0 + nl : N - 1; };
@@ -529,8 +532,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
         qsrc[i] = (UP ? p.up_q : p.dn_q) + (eN + out_row(u >> 1)) * (Kin >> 3) + 4 * (u & 1);
     }
     auto issue = [&](int g, int buf) {
+        if (wn < mlim)   // wave w copies the inputs of picks 16 w .. +15
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + 64 * g, &L.a[buf][128 * wn + 64 * i]);
+            for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + 64 * g, &L.a[buf][128 * wn + 64 * i]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_dma16(qsrc[i] + 8 * g, &((uint4 *)L.q[buf])[128 * wn + 64 * i]);
     };
@@ -548,8 +552,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
         if (g + 1 < G) issue(g + 1, buf ^ 1);
         if ((g & 1) && g + 1 < G) issue_sc((g + 1) >> 1);
         {
-            // thread t: 16 inputs (units 2 (t & 3), +1) of pick t >> 2
-            const int r = tid >> 2, part = tid & 3;
+            // thread t: 16 inputs (units 2 (t & 3), +1) of pick t >> 2 (wave w: picks 16 w .. +15)
+            const int r = tid >> 2, part = tid & 3, slot = g & 3;
+            if (wn < mlim) {
             const uint4 v0 = lds_ld16(&L.a[buf][r * 8 + 2 * part]), v1 = lds_ld16(&L.a[buf][r * 8 + 2 * part + 1]);
             float sx = 0.0f;
             sx = dot2<false>(0x3F803F80u, v0.x, sx);
@@ -568,8 +573,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                               __builtin_amdgcn_perm(v1.w, v1.y, 0x05040100u), __builtin_amdgcn_perm(v1.w, v1.y, 0x07060302u)};
             lds_st16(&L.ap[swz(r, 2 * part)], p0);
             lds_st16(&L.ap[swz(r, 2 * part + 1)], p1);
-            const int slot = g & 3;
             if (part == 0) L.xs4[slot][r] = sx;
+            }
             // thread t: output t's scale and bias for this group
             const uint32_t sw = L.scp[(g >> 1) & 1][tid], bw = L.bcp[(g >> 1) & 1][tid];
             const float sct = bf2f(g & 1 ? sw >> 16 : sw & 0xFFFFu);
@@ -583,10 +588,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                 }
         }
         __syncthreads();
-        if (active) {
-            uint4 xf[4][2];
+        // the products of the first MT pick tiles (MT = 4, or 2 when the tile holds at most 32
+        // picks): the same operations in the same order either way
+        auto products = [&](auto mt) {
+            constexpr int MT = decltype(mt)::value;
+            uint4 xf[MT][2];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+            for (int mi = 0; mi < MT; ++mi) {
                 xf[mi][0] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg)]);
                 xf[mi][1] = lds_ld16(&L.ap[swz(16 * mi + lr, 2 * lg + 1)]);
             }
@@ -599,10 +607,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                 code_pairs<false>(w.y, c1);
                 const uint4 wf0 = make_uint4(c0[0], c0[1], c0[2], c0[3]);
                 const uint4 wf1 = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-                // the 4 pick tiles' products first (independent), then their scaling
-                f32x4 a[4];
+                // the pick tiles' products first (independent), then their scaling
+                f32x4 a[MT];
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi) {
+                for (int mi = 0; mi < MT; ++mi) {
                     a[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf0),
                                                                     __builtin_bit_cast(bf16x8, xf[mi][0]),
                                                                     (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -612,7 +620,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                 // the scale of the 4 outputs this lane ends with
                 const f32x4 sc = *(const f32x4 *)&L.sc[nl + 4 * lg];
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[ni][mi][q] = __builtin_fmaf(sc[q], a[mi][q], acc[ni][mi][q]);
             }
@@ -623,10 +631,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                 for (int ni = 0; ni < 4; ++ni) {
                     const float cbl = L.cb4[lg][64 * wn + 16 * ni + lr];
 #pragma unroll
-                    for (int mi = 0; mi < 4; ++mi)
+                    for (int mi = 0; mi < MT; ++mi)
                         acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(cbl, L.xs4[lg][16 * mi + lr], acc[ni][mi], 0, 0, 0);
                 }
             }
+        };
+        if (active) {
+            if (mlim > 2) products(std::integral_constant<int, 4>{});
+            else products(std::integral_constant<int, 2>{});
         }
     }
     if (!active) return;
