@@ -31,7 +31,7 @@ __global__ void moe_front_kernel(LayerParams p, int nwg);
 template <bool F32W> __global__ void pf_gate_kernel(LayerParams p);
 template <int ME> __global__ void pf_route_kernel(LayerParams p);
 __global__ void pf_sched_kernel(LayerParams p);
-template <int EPI>
+template <int EPI, int KS>
 __global__ void pf_gemm_kernel(LayerParams p, const uint16_t *X, const uint16_t *W, int N, int K);
 template <bool UP> __global__ void pf_expert_kernel(LayerParams p);
 template <int EPI, int TN>
@@ -791,6 +791,17 @@ static int check_prefill_layer(const moe_latent_config &c) {
 
 static int grid8(long n) { return (int)(8 * ((n + 7) / 8)); }
 
+// A launch of 128 x 128 GEMM tiles: 128 inputs a step when it has at most one tile per compute
+// unit (their 128 KB of LDS then cost no occupancy) and K allows, else 64 (same bits).
+template <int EPI>
+static void small_gemm(const LayerParams &p, int cus, long tiles, hipStream_t st, const uint16_t *X,
+                       const uint16_t *W, int N, int K) {
+    if (tiles <= cus && K % 128 == 0)
+        hipLaunchKernelGGL((pf_gemm_kernel<EPI, 128>), dim3(grid8(tiles)), dim3(256), 0, st, p, X, W, N, K);
+    else
+        hipLaunchKernelGGL((pf_gemm_kernel<EPI, 64>), dim3(grid8(tiles)), dim3(256), 0, st, p, X, W, N, K);
+}
+
 extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hidden_in, void *out) {
     if (!valid(h)) return fail(MOE_ERR_INVALID_ARG, "invalid handle");
     if (!hidden_in || !out) return fail(MOE_ERR_INVALID_ARG, "hidden_in or out is NULL");
@@ -840,11 +851,9 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
                                p.SI, p.H);
             LayerParams q = p;
             q.SI = 0;   // the fc1 launch's tiles only
-            hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * (p.L / 128))), dim3(256), 0, st, q, p.x,
-                               p.fc1, p.L, p.H);
+            small_gemm<0>(q, h->cus, (long)mt * (p.L / 128), st, p.x, p.fc1, p.L, p.H);
         } else {
-            hipLaunchKernelGGL(pf_gemm_kernel<0>, dim3(grid8((long)mt * ((p.L + p.SI) / 128))), dim3(256), 0, st, p,
-                               p.x, p.fc1, p.L, p.H);
+            small_gemm<0>(p, h->cus, (long)mt * ((p.L + p.SI) / 128), st, p.x, p.fc1, p.L, p.H);
         }
     }
     // expert tiles: at most one partial tile of 64 picks per expert beyond the full ones
@@ -860,15 +869,13 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
         hipLaunchKernelGGL((pf_gemm_big_kernel<2, 256>), dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.shact, p.sd, p.H,
                            p.SI);
     else if (p.SI)
-        hipLaunchKernelGGL(pf_gemm_kernel<2>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.shact, p.sd,
-                           p.H, p.SI);
+        small_gemm<2>(p, h->cus, (long)mt * (p.H / 128), st, p.shact, p.sd, p.H, p.SI);
     hipLaunchKernelGGL(pf_combine_kernel, dim3((unsigned)(((long)rows * (p.D / 4) + 255) / 256)), dim3(256), 0, st, p);
     if (p.L && big(p.H))
         hipLaunchKernelGGL((pf_gemm_big_kernel<3, 256>), dim3(big_tiles(p.H)), dim3(512), 0, st, p, p.comb, p.fc2, p.H,
                            p.L);
     else if (p.L)
-        hipLaunchKernelGGL(pf_gemm_kernel<3>, dim3(grid8((long)mt * (p.H / 128))), dim3(256), 0, st, p, p.comb, p.fc2,
-                           p.H, p.L);
+        small_gemm<3>(p, h->cus, (long)mt * (p.H / 128), st, p.comb, p.fc2, p.H, p.L);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     h->last_rows = rows;

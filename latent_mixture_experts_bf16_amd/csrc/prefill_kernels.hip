@@ -239,10 +239,15 @@ __device__ __forceinline__ int xcd_tile(int total) {
 
 enum PfEpi { PF_FC1 = 0, PF_SHUP = 1, PF_SHDN = 2, PF_FC2 = 3 };
 
+template <int KS>
 struct PfGemmLds {
-    uint4 a[2][PF_DM * 8];    // [buffer][row][8 units of 16 bytes]: 64 inputs of each row
-    uint4 b[2][PF_BN * 8];
+    uint4 a[2][PF_DM * KS / 8];    // [buffer][row][KS / 8 units of 16 bytes]: KS inputs of each row
+    uint4 b[2][PF_BN * KS / 8];
 };
+
+// unit c of a row of U units: the 16 rows of a fragment read fall in distinct banks
+template <int U>
+__device__ __forceinline__ int swz_u(int row, int c) { return row * U + (c ^ (row & (U - 1))); }
 
 // Outputs n .. n + 3 of row m from their fp32 sums v, through the launch's epilogue (epi is
 // EPI, or PF_SHUP for the shared up tiles of an fc1 launch): fc1 (rounded), shared up (relu^2
@@ -274,15 +279,18 @@ __device__ __forceinline__ void pf_store4(const LayerParams &p, int epi, int m, 
 }
 
 // C[m][n] = sum_k X[m][k] W[n][k] for m < rows (X = [rows][K] bf16, W = [N][K] bf16), tiles
-// of 128 rows x 128 outputs, 64 inputs a step (double-buffered direct copies to LDS). Wave w
+// of 128 rows x 128 outputs, KS inputs a step (double-buffered direct copies to LDS; 128 for
+// launches of at most one tile per compute unit, whose 128 KB then cost no occupancy, and
+// half the barriers per input). Wave w
 // holds rows 64 (w & 1) .. +63 and outputs 64 (w >> 1) .. +63 as 4 x 4 MFMA 16x16x32 tiles
 // with the weights as the first operand, so lane l ends with outputs 4 (l >> 4) .. +3 of row
 // l & 15 of each tile; each output's sum runs over k in one fixed order (the epilogue is
 // pf_store4's). An fc1 launch also runs the shared up tiles when p.SI is set.
-template <int EPI>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) pf_gemm_kernel(LayerParams p, const uint16_t *__restrict__ X,
+template <int EPI, int KS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KS == 128 ? 1 : 2, 8))) pf_gemm_kernel(LayerParams p, const uint16_t *__restrict__ X,
                                                          const uint16_t *W, int N, int K) {
-    __shared__ PfGemmLds L;
+    constexpr int UPR = KS / 8, NI = UPR / 2;   // units of a row a step; copies a thread and operand
+    __shared__ PfGemmLds<KS> L;
     const int nbm = (p.rows + PF_DM - 1) / PF_DM, t1 = (N / PF_BN) * nbm;
     // fc1 launches carry the shared up projection too (the same input): its tiles follow
     const int total = EPI == PF_FC1 && p.SI ? t1 + (p.SI / PF_BN) * nbm : t1;
@@ -299,31 +307,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int m0 = (tile / nbn) * PF_DM, n0 = (tile % nbn) * PF_BN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave & 1, wn = wave >> 1;
-    // the copies: wave w moves units [256 w, 256 w + 256) of each 1024-unit tile, lane l unit
-    // 256 w + 64 i + l in instruction i: row u >> 3, stored swizzled
-    const uint16_t *xs[4], *ws[4];
-    int du[4];
+    // the copies: instruction i of wave w moves units 64 (4 i + w) .. +63 of each tile of
+    // 128 UPR units, lane l the unit u = 64 (4 i + w) + l: row u / UPR, stored swizzled
+    const uint16_t *xs[NI], *ws[NI];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int u = 256 * wave + 64 * i + lane, row = u >> 3, cs = u & 7, c = cs ^ (row & 7);
+    for (int i = 0; i < NI; ++i) {
+        const int u = 64 * (4 * i + wave) + lane, row = u / UPR, cs = u % UPR;
+        const int c = swz_u<UPR>(row, cs) - row * UPR;   // the swizzle is its own inverse
         const int m = m0 + row < p.rows ? m0 + row : p.rows - 1;
         xs[i] = X + (size_t)m * K + 8 * c;
         ws[i] = W + (size_t)(n0 + row) * K + 8 * c;
-        du[i] = 256 * wave + 64 * i;   // first unit of the instruction (the copy adds 16 l bytes)
     }
     auto issue = [&](int ks, int buf) {
-        const int k0 = 64 * ks;
+        const int k0 = KS * ks;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(xs[i] + k0, &L.a[buf][du[i]]);
+        for (int i = 0; i < NI; ++i) lds_dma16(xs[i] + k0, &L.a[buf][64 * (4 * i + wave)]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(ws[i] + k0, &L.b[buf][du[i]]);
+        for (int i = 0; i < NI; ++i) lds_dma16(ws[i] + k0, &L.b[buf][64 * (4 * i + wave)]);
     };
     f32x4 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int nk = K / 64;
+    const int nk = K / KS;
     issue(0, 0);
     for (int ks = 0; ks < nk; ++ks) {
         const int buf = ks & 1;
@@ -331,14 +338,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
         __syncthreads();   // step ks is in LDS; every wave is done with step ks - 1
         if (ks + 1 < nk) issue(ks + 1, buf ^ 1);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < KS / 32; ++s) {
             uint4 xf[4], wf[4];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
-                xf[mi] = lds_ld16(&L.a[buf][swz(wm * 64 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+                xf[mi] = lds_ld16(&L.a[buf][swz_u<UPR>(wm * 64 + mi * 16 + (lane & 15), 4 * s + (lane >> 4))]);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-                wf[ni] = lds_ld16(&L.b[buf][swz(wn * 64 + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
+                wf[ni] = lds_ld16(&L.b[buf][swz_u<UPR>(wn * 64 + ni * 16 + (lane & 15), 4 * s + (lane >> 4))]);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
@@ -357,10 +364,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))
     }
 }
 
-template __global__ void pf_gemm_kernel<PF_FC1>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_kernel<PF_SHUP>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_kernel<PF_SHDN>(LayerParams, const uint16_t *, const uint16_t *, int, int);
-template __global__ void pf_gemm_kernel<PF_FC2>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_FC1, 64>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_SHDN, 64>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_FC2, 64>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_FC1, 128>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_SHDN, 128>(LayerParams, const uint16_t *, const uint16_t *, int, int);
+template __global__ void pf_gemm_kernel<PF_FC2, 128>(LayerParams, const uint16_t *, const uint16_t *, int, int);
 
 // The same products in tiles of 256 rows x TN outputs (8 waves; wave w holds rows 128 (w & 1)
 // .. +127 and outputs TN / 4 (w >> 1) .. + TN / 4 - 1 as MFMA 16x16x32 tiles), for passes with
