@@ -786,6 +786,9 @@ static int check_prefill_layer(const moe_latent_config &c) {
                     quant_bits_of(c), c.group_size);
     if (c.expert_inter % 128)
         return fail(MOE_ERR_SHAPE, "prefill: expert_inter %d not a multiple of 128", c.expert_inter);
+    if ((long long)c.n_experts * c.hidden >= (1LL << 31))   // the gate's 32-bit row offsets
+        return fail(MOE_ERR_SHAPE, "prefill: n_experts %d x hidden %d gate elements exceed 2^31 - 1",
+                    c.n_experts, c.hidden);
     return MOE_OK;
 }
 
@@ -826,6 +829,7 @@ extern "C" int moe_latent_prefill(moe_latent_t *h, int32_t rows, const void *hid
     const int E = p.E, K = p.K, NP = rows * K;
     hipLaunchKernelGGL(moe_clear_kernel, dim3((E + 255) / 256), dim3(256), 0, st, (uint32_t *)p.pf_count, E);
     {
+        // waves of 8 rows x 8 experts, 4 a workgroup
         const long wb = (long)((rows + 7) / 8) * ((E + 7) / 8);
         if (p.router_f32) hipLaunchKernelGGL(pf_gate_kernel<true>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
         else hipLaunchKernelGGL(pf_gate_kernel<false>, dim3((unsigned)((wb + 3) / 4)), dim3(256), 0, st, p);
