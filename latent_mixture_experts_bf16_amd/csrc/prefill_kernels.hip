@@ -15,14 +15,15 @@
 //   sched    prefix sums of the per-expert counts (list starts, row-tile starts) and the
 //            pick ids scattered into the per-expert lists
 //   gemm     fc1 (u = rnd(W1 x)) and shared up (rnd(relu^2(rnd(Su x)))) in one launch: 128 x 128
-//            tiles
+//            tiles, or one matrix of L + SI rows in 256 x 320 tiles when those fill the machine
 //   expert   routed up / down: tiles of 64 picks of one expert x 256 outputs, 4-bit codes
-//            decoded in registers, MFMA per group of 64 inputs, then scale and bias per group
-//   gemm     shared down (rnd(Sd a))
+//            decoded in registers, MFMA per group of 64 inputs, then the scale per group (the
+//            bias terms by an fp32 MFMA every four groups)
+//   gemm     shared down (rnd(Sd a)): 128 x 128 or 256 x 256 tiles
 //   combine  every row (the decode combine: lane order and rounding)
-//   gemm     fc2 with the final adds: out = rnd(x + rnd(rnd(W2 c) + sh))
-// Every output's sum runs over its inputs in one fixed order whatever the number of rows,
-// so each row of a pass equals that row passed alone, bit for bit.
+//   gemm     fc2 with the final adds: out = rnd(x + rnd(rnd(W2 c) + sh)): as shared down
+// Every output's sum runs over its inputs in one fixed order whatever the number of rows and
+// the tile shape, so each row of a pass equals that row passed alone, bit for bit.
 #include "layer_items.h"
 
 namespace moe {
