@@ -186,9 +186,22 @@ def summarize_stats(args):
             continue
         key = (name, "inside forwards" if disp[i - 1][2] != name else "after itself")
         split.setdefault(key, []).append((en - st) / 1e3)
-    lines += ["", "by the dispatch before (layer kernels only)", f"{'kernel':70s} {'context':>16s} {'calls':>7s} {'avg_us':>9s}"]
+    if split:
+        lines += ["", "by the dispatch before (layer kernels only)",
+                  f"{'kernel':70s} {'context':>16s} {'calls':>7s} {'avg_us':>9s}"]
     for (name, ctx), v in sorted(split.items()):
         lines.append(f"{name[:70]:70s} {ctx:>16s} {len(v):7d} {sum(v) / len(v):9.3f}")
+    # prefill kernels by grid size (each row count of a prefill pass launches its own grids)
+    grids = {}
+    for r in trace:
+        if "pf_" in r["Kernel_Name"]:
+            key = (r["Kernel_Name"].split("(")[0].replace("void ", ""), int(r["Grid_Size_X"]))
+            grids.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if grids:
+        lines += ["", "prefill kernels by grid size (threads)", f"{'kernel':60s} {'grid':>9s} {'calls':>7s} {'median_us':>10s}"]
+        for (name, grid), v in sorted(grids.items()):
+            v = sorted(v)
+            lines.append(f"{name[:60]:60s} {grid:9d} {len(v):7d} {v[len(v) // 2]:10.1f}")
     txt = "\n".join(lines) + "\n"
     with open(args.stats_out, "w") as fh:
         fh.write(txt)
