@@ -237,13 +237,13 @@ def test_prefill_4096_rows_bolt():
     _check_layer(d, arrays, "bolt 4096", sample=sample, alone=(0, 4095))
 
 
-@pytest.mark.parametrize("rows", [4096, 3500])
-def test_prefill_big_tiles_match_small_tiles(rows):
-    """At 4096 rows (and at 3500, whose last tile of 256 rows holds 172) the shared up and
-    down projections and fc2 run in tiles of 256 rows x 256 outputs; passes of at most 512
-    rows run them in 128 x 128 tiles. Both sum each output in the same order, so every row's
-    shared expert stages and output are the same bits either way."""
-    chunk = 512
+@pytest.mark.parametrize("rows,chunk", [(4096, 512), (3500, 512), (1500, 500)])
+def test_prefill_big_tiles_match_small_tiles(rows, chunk):
+    """At 4096 rows (and at 3500, whose last tile of 256 rows holds 172) the dense projections
+    run in tiles of 256 rows x 320 or 256 outputs; passes of at most 512 rows run them in
+    128 x 128 tiles of 128 inputs a step. At 1500 rows (a last tile of 92 rows) they run in
+    128 x 128 tiles of 64 inputs a step. Every shape sums each output in the same order, so
+    every row's latent, shared expert stages and output are the same bits either way."""
     d, arrays = next(synth.workload_layers(1, rows=rows))
     lay, xd, out = _prefill(d, arrays)
     got = out.cpu().numpy().view(np.uint16)
