@@ -242,8 +242,8 @@ def main():
         return summarize_mfma(args)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer's sharding "
-              "is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         return 2
 
     import numpy as np

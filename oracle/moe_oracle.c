@@ -167,7 +167,7 @@ static float rnd(const orc_cfg *cfg, float v) { return act_load(cfg, act_store(c
 
 /* C64, the gate's fixed summation order (the pages pin routing to one reference
  * kernel's bits, TensorFold pull request 1038, «Per operator and row invariance»; the
- * order itself is this build's reading): 64 lane partials, lane t accumulating, in
+ * order itself is the reading taken here): 64 lane partials, lane t accumulating, in
  * order, the terms at k = 512 j + 8 t + i for j = 0, 1, ... and i = 0..7, starting from
  * +0; then for d = 32, 16, 8, 4, 2, 1 every lane t replaces P[t] by P[t] + P[t ^ d];
  * the result is P[0]. Each term is fmaf(x_k, w_k, P): for bf16 x bf16 the product is

@@ -300,7 +300,7 @@ def test_sigmoid_of_every_finite_bf16_logit():
 
 
 @pytest.mark.skip(reason="the one-launch fused variant is disabled: its first GPU run did not "
-                         "complete and the cause is not yet found; see DESIGN.md")
+                         "complete, and the library refuses it (variant 0) until a cause is shown")
 def test_fused_and_staged_launches_agree_bitwise():
     for cid in (0, 1):
         dims, arrays = workload(cid)

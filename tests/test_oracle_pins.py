@@ -95,8 +95,8 @@ def test_dequant_closed_form_every_code_and_scale():
 
 
 def test_nibble_layout_low_nibble_first():
-    """Code k of a row sits in word k // 8 at bits 4 * (k % 8) (the layout this build
-    fixes): a one-hot input at k returns exactly the dequantised weight at k."""
+    """Code k of a row sits in word k // 8 at bits 4 * (k % 8) (the layout the library
+    takes): a one-hot input at k returns exactly the dequantised weight at k."""
     rng = np.random.default_rng(7)
     K = 256
     codes = rng.integers(0, 16, size=(3, K))
