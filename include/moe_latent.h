@@ -161,8 +161,9 @@ int moe_latent_forward(moe_latent_t *h, int32_t rows, const void *hidden_in, voi
  * points -- with other fp32 summation orders in the projections and experts, so outputs
  * agree with a decode pass within the parity bar, not bit for bit. Each row of a prefill
  * equals that row passed alone through moe_latent_prefill, bit for bit. Takes bf16
- * activations, 4-bit codes in groups of 64 and expert_inter a multiple of 128
- * (MOE_ERR_DTYPE / MOE_ERR_SHAPE otherwise). Buffers and errors as moe_latent_forward (in
+ * activations, 4-bit codes in groups of 64, expert_inter a multiple of 128 and
+ * n_experts * hidden below 2^31 (MOE_ERR_DTYPE / MOE_ERR_SHAPE otherwise). Buffers and
+ * errors as moe_latent_forward (in
  * place allowed); enqueued on the handle's stream as a chain of launches, no allocation;
  * moe_latent_get_routing and moe_latent_read_stage then report this pass. moe_latent_forward
  * itself takes at most 256 rows (MOE_ERR_ROWS above). */
